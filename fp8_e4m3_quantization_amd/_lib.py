@@ -1,0 +1,300 @@
+"""ctypes binding of libfp8q.so (the C ABI declared in include/fp8q.h).
+
+Argument marshalling only: tensors are checked (dtype, device, contiguity, shape) and
+their device pointers handed to the library together with the current HIP stream.  Every
+step of the computation runs in the library's HIP kernels; there is no fallback path:
+a missing or unloadable library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8q.so")
+
+FP8Q_OK = 0
+FP8Q_CALIB_STAGE, FP8Q_CALIB_DECLINE, FP8Q_CALIB_FREEZE, FP8Q_CALIB_FROZEN = 0, 1, 2, 3
+
+# Every symbol include/fp8q.h declares.
+EXPORTS = (
+    "fp8q_strerror", "fp8q_version", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
+    "w8a8_block_gemm", "fp8_kv_write", "fp8_kv_amax", "fp8q_kv_calib_create",
+    "fp8q_kv_calib_observe", "fp8q_kv_calib_decide", "fp8q_kv_calib_scales",
+    "fp8q_kv_calib_get_info", "fp8q_kv_calib_destroy",
+)
+
+
+class Fp8qError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+class KvTarget(ctypes.Structure):
+    _fields_ = [
+        ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+        ("slot_mapping", ctypes.c_void_p), ("block_size", ctypes.c_int32),
+        ("key_stride", ctypes.c_int32), ("value_stride", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("cache_stride", ctypes.c_int64),
+        ("num_blocks", ctypes.c_int64),
+    ]
+
+
+class KvCalibInfo(ctypes.Structure):
+    _fields_ = [
+        ("window_tokens", ctypes.c_int32), ("requested_tokens", ctypes.c_int32),
+        ("frozen", ctypes.c_int32), ("staged_batches", ctypes.c_int32),
+        ("tokens_seen", ctypes.c_int64), ("staged_tokens", ctypes.c_int64),
+        ("unstaged_tokens", ctypes.c_int64), ("replayed_tokens", ctypes.c_int64),
+        ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+        ("k_amax", ctypes.c_float), ("v_amax", ctypes.c_float),
+        ("headroom", ctypes.c_float), ("provisional_scale", ctypes.c_float),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libfp8q.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    sig = {
+        "fp8q_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "fp8q_version": (ctypes.c_int, []),
+        "fp8_group_quant": (ctypes.c_int, [P, P, P, I64, I32, P]),
+        "fp8_block_quant": (ctypes.c_int, [P, P, P, I32, I32, P]),
+        "fp8_e4m3_encode": (ctypes.c_int, [P, P, I64, P]),
+        "w8a8_block_gemm": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, P]),
+        "fp8_kv_write": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, I64, F32, F32,
+                                        I32, I32, I64, P]),
+        "fp8_kv_amax": (ctypes.c_int, [P, P, I64, P, P]),
+        "fp8q_kv_calib_create": (ctypes.c_int, [I32, F32, ctypes.POINTER(P)]),
+        "fp8q_kv_calib_observe": (ctypes.c_int, [P, P, P, I32, I32, I32,
+                                                 ctypes.POINTER(KvTarget), P]),
+        "fp8q_kv_calib_decide": (ctypes.c_int, [P, I32, I32]),
+        "fp8q_kv_calib_scales": (ctypes.c_int, [P, ctypes.POINTER(F32), ctypes.POINTER(F32)]),
+        "fp8q_kv_calib_get_info": (ctypes.c_int, [P, ctypes.POINTER(KvCalibInfo)]),
+        "fp8q_kv_calib_destroy": (None, [P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load().fp8q_strerror(status).decode()
+
+
+def check(fn: str, status: int) -> None:
+    if status != FP8Q_OK:
+        raise Fp8qError(fn, status, strerror(status))
+
+
+def current_stream(device=None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype, contiguous: bool = True) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live in GPU memory (got {t.device})")
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+# ------------------------------------------------------------------------- entry points
+
+
+def fp8_group_quant(x: torch.Tensor, q: torch.Tensor | None = None,
+                    scales: torch.Tensor | None = None, stream: int | None = None):
+    """bf16 [m, k] -> (E4M3 codes uint8 [m, k], fp32 scales [m, k/128])."""
+    if x.dim() != 2:
+        raise ValueError("x must be [m, k]")
+    m, k = x.shape
+    if q is None:
+        q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((m, max(k // 128, 1)), dtype=torch.float32, device=x.device)
+    if tuple(q.shape) != (m, k) or scales.numel() < m * (k // 128):
+        raise ValueError("output shapes do not match x")
+    st = load().fp8_group_quant(_dev(x, "x", _BF16), _dev(q, "q", _U8),
+                                _dev(scales, "scales", torch.float32), m, k,
+                                current_stream(x.device) if stream is None else stream)
+    check("fp8_group_quant", st)
+    return q, scales
+
+
+def fp8_block_quant(w: torch.Tensor, wq: torch.Tensor | None = None,
+                    ws: torch.Tensor | None = None, stream: int | None = None):
+    """bf16 [n, k] -> (E4M3 codes [n, k], fp32 block scales [ceil(n/128), ceil(k/128)])."""
+    n, k = w.shape
+    if wq is None:
+        wq = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    if ws is None:
+        ws = torch.empty(((n + 127) // 128, (k + 127) // 128), dtype=torch.float32,
+                         device=w.device)
+    if tuple(wq.shape) != (n, k) or ws.numel() < ((n + 127) // 128) * ((k + 127) // 128):
+        raise ValueError("output shapes do not match w")
+    st = load().fp8_block_quant(_dev(w, "w", _BF16), _dev(wq, "wq", _U8),
+                                _dev(ws, "ws", torch.float32), n, k,
+                                current_stream(w.device) if stream is None else stream)
+    check("fp8_block_quant", st)
+    return wq, ws
+
+
+def fp8_e4m3_encode(x: torch.Tensor, q: torch.Tensor | None = None,
+                    stream: int | None = None) -> torch.Tensor:
+    """fp32 [...] -> E4M3 codes (saturating round-to-nearest-even, no scale)."""
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if q.numel() != x.numel():
+        raise ValueError("q must have as many elements as x")
+    st = load().fp8_e4m3_encode(_dev(x, "x", torch.float32), _dev(q, "q", _U8), x.numel(),
+                                current_stream(x.device) if stream is None else stream)
+    check("fp8_e4m3_encode", st)
+    return q
+
+
+def w8a8_block_gemm(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tensor,
+                    w_scale: torch.Tensor, out: torch.Tensor | None = None,
+                    ldc: int | None = None, stream: int | None = None) -> torch.Tensor:
+    """E4M3 a_q [m, k] x E4M3 w_q [n, k]^T with block scales -> bf16 out [m, ldc]."""
+    m, k = a_q.shape
+    n = w_q.shape[0]
+    if w_q.shape[1] != k:
+        raise ValueError("a_q and w_q disagree on k")
+    if a_scale.numel() != m * (k // 128) or w_scale.numel() != (n // 128) * (k // 128):
+        raise ValueError("scale grids do not match the operand shapes")
+    if out is None:
+        ldc = n if ldc is None else ldc
+        out = torch.empty((m, ldc), dtype=torch.bfloat16, device=a_q.device)
+    else:
+        ldc = out.shape[-1] if ldc is None else ldc
+        if out.numel() < (m - 1) * ldc + n:
+            raise ValueError("out is smaller than (m - 1) * ldc + n elements")
+    st = load().w8a8_block_gemm(_dev(a_q, "a_q", _U8), _dev(a_scale, "a_scale", torch.float32),
+                                _dev(w_q, "w_q", _U8), _dev(w_scale, "w_scale", torch.float32),
+                                _dev(out, "out", _BF16), m, n, k, ldc,
+                                current_stream(a_q.device) if stream is None else stream)
+    check("w8a8_block_gemm", st)
+    return out
+
+
+def fp8_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                 v_cache: torch.Tensor, slot_mapping: torch.Tensor, num_kv_heads: int,
+                 head_dim: int, block_size: int, k_scale: float, v_scale: float,
+                 key_stride: int | None = None, value_stride: int | None = None,
+                 cache_stride: int | None = None, num_tokens: int | None = None,
+                 stream: int | None = None) -> None:
+    """Slot-mapped E4M3 scatter of bf16 K/V rows into paged pools [blocks, bs*H*D]."""
+    e = num_kv_heads * head_dim
+    t = slot_mapping.numel() if num_tokens is None else num_tokens
+    key_stride = e if key_stride is None else key_stride
+    value_stride = e if value_stride is None else value_stride
+    cache_stride = block_size * e if cache_stride is None else cache_stride
+    if k_cache.numel() != v_cache.numel() or k_cache.numel() % cache_stride:
+        raise ValueError("pools must be equal and a whole number of blocks")
+    num_blocks = k_cache.numel() // cache_stride
+    for name, src, stride in (("k", k, key_stride), ("v", v, value_stride)):
+        if t > 0 and src.numel() < (t - 1) * stride + e:
+            raise ValueError(f"{name} is smaller than its rows")
+    st = load().fp8_kv_write(_dev(k, "k", _BF16, False), _dev(v, "v", _BF16, False),
+                             _dev(k_cache, "k_cache", _U8), _dev(v_cache, "v_cache", _U8),
+                             _dev(slot_mapping, "slot_mapping", torch.int64), t, num_kv_heads,
+                             head_dim, block_size, num_blocks, k_scale, v_scale, key_stride,
+                             value_stride, cache_stride,
+                             current_stream(k.device) if stream is None else stream)
+    check("fp8_kv_write", st)
+
+
+def fp8_kv_amax(k: torch.Tensor, v: torch.Tensor, amax2: torch.Tensor,
+                stream: int | None = None) -> torch.Tensor:
+    """amax2[0] = max(amax2[0], max|k|), amax2[1] = max(amax2[1], max|v|) (packed k, v)."""
+    if k.numel() != v.numel() or amax2.numel() < 2:
+        raise ValueError("k and v must have equal sizes; amax2 holds two floats")
+    st = load().fp8_kv_amax(_dev(k, "k", _BF16), _dev(v, "v", _BF16), k.numel(),
+                            _dev(amax2, "amax2", torch.float32),
+                            current_stream(k.device) if stream is None else stream)
+    check("fp8_kv_amax", st)
+    return amax2
+
+
+class KvCalibrator:
+    """One attention layer's online FP8 KV scale calibration (fp8q_kv_calib_*)."""
+
+    def __init__(self, window_tokens: int, headroom: float = 1.0):
+        lib = load()
+        h = ctypes.c_void_p()
+        check("fp8q_kv_calib_create", lib.fp8q_kv_calib_create(window_tokens, headroom,
+                                                                 ctypes.byref(h)))
+        self._h = h.value
+
+    def decide(self, num_tokens: int, elems_per_token: int) -> int:
+        st = load().fp8q_kv_calib_decide(self._h, num_tokens, elems_per_token)
+        if st < 0:
+            check("fp8q_kv_calib_decide", st)
+        return st
+
+    def observe(self, k: torch.Tensor, v: torch.Tensor, num_kv_heads: int, head_dim: int,
+                k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                block_size: int, key_stride: int | None = None,
+                value_stride: int | None = None, cache_stride: int | None = None,
+                stream: int | None = None) -> None:
+        e = num_kv_heads * head_dim
+        cs = block_size * e if cache_stride is None else cache_stride
+        tgt = KvTarget(k_pool=_dev(k_cache, "k_cache", _U8),
+                       v_pool=_dev(v_cache, "v_cache", _U8),
+                       slot_mapping=_dev(slot_mapping, "slot_mapping", torch.int64),
+                       block_size=block_size,
+                       key_stride=e if key_stride is None else key_stride,
+                       value_stride=e if value_stride is None else value_stride,
+                       reserved=0, cache_stride=cs, num_blocks=k_cache.numel() // cs)
+        st = load().fp8q_kv_calib_observe(
+            self._h, _dev(k, "k", _BF16, False), _dev(v, "v", _BF16, False),
+            slot_mapping.numel(), num_kv_heads, head_dim, ctypes.byref(tgt),
+            current_stream(k.device) if stream is None else stream)
+        check("fp8q_kv_calib_observe", st)
+
+    def scales(self):
+        ks, vs = ctypes.c_float(), ctypes.c_float()
+        check("fp8q_kv_calib_scales",
+              load().fp8q_kv_calib_scales(self._h, ctypes.byref(ks), ctypes.byref(vs)))
+        return ks.value, vs.value
+
+    def info(self) -> dict:
+        inf = KvCalibInfo()
+        check("fp8q_kv_calib_get_info", load().fp8q_kv_calib_get_info(self._h,
+                                                                         ctypes.byref(inf)))
+        return {name: getattr(inf, name) for name, _ in KvCalibInfo._fields_}
+
+    def close(self) -> None:
+        if self._h:
+            load().fp8q_kv_calib_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,78 @@
+// fp8q_device.h -- gfx950 device helpers: bf16 unpacking, E4M3 packing through the
+// hardware converter, DPP lane reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8q_math.h"
+
+#pragma clang fp contract(off)
+
+namespace fp8q {
+
+// ---------------------------------------------------------------- bf16 unpacking
+// A 32-bit word holds two bf16 values: element 0 in bits 15:0, element 1 in 31:16.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ------------------------------------------------------------------ E4M3 packing
+// gfx950's v_cvt_pk_fp8_f32 rounds binary32 to OCP E4M3 to nearest even; values are
+// clipped to +-448 first so an out-of-range quotient saturates instead of becoming NaN.
+__device__ __forceinline__ float clip448(float v) {
+  return __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max);
+}
+
+// Four finite binary32 values -> four E4M3 codes, a in byte 0 ... d in byte 3.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clip448(a), clip448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clip448(c), clip448(d), w, true);
+  return uint32_t(w);
+}
+
+// Eight bf16 (one 16-byte load) divided by a scale and packed into eight E4M3 codes.
+// `clipped` selects the estimate clip needed when the scale may be far below |x|/448.
+template <bool kClipped>
+__device__ __forceinline__ uint2 quant8(uint4 w, float s, float y) {
+  auto dq = [&](float x) {
+    return kClipped ? div_by_scale_clipped(x, s, y) : div_by_scale(x, s, y);
+  };
+  uint2 r;
+  r.x = e4m3x4(dq(bf16_lo(w.x)), dq(bf16_hi(w.x)), dq(bf16_lo(w.y)), dq(bf16_hi(w.y)));
+  r.y = e4m3x4(dq(bf16_lo(w.z)), dq(bf16_hi(w.z)), dq(bf16_lo(w.w)), dq(bf16_hi(w.w)));
+  return r;
+}
+
+// max |x| of eight bf16 packed in a 16-byte word, as binary32.
+__device__ __forceinline__ float absmax8(uint4 w) {
+  float m0 = fmaxf(fabsf(bf16_lo(w.x)), fabsf(bf16_hi(w.x)));
+  float m1 = fmaxf(fabsf(bf16_lo(w.y)), fabsf(bf16_hi(w.y)));
+  float m2 = fmaxf(fabsf(bf16_lo(w.z)), fabsf(bf16_hi(w.z)));
+  float m3 = fmaxf(fabsf(bf16_lo(w.w)), fabsf(bf16_hi(w.w)));
+  return fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+}
+
+// --------------------------------------------------------------- DPP reductions
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF,
+                                                    false));
+}
+
+// Max over each aligned group of 8 lanes; every lane of the group gets the result.
+__device__ __forceinline__ float max_over_8_lanes(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]: partner lane ^ 1
+  v = fmaxf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]: partner lane ^ 2
+  v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror: lane i <-> 7 - i within 8 lanes
+  return v;
+}
+
+// Max over the whole 64-lane wave (result valid in every lane).
+__device__ __forceinline__ float max_over_wave(float v) {
+  v = max_over_8_lanes(v);
+  v = fmaxf(v, dpp<0x140>(v));  // row_mirror: lane i <-> 15 - i within 16 lanes
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+}  // namespace fp8q

@@ -1,0 +1,214 @@
+// fp8q_kv.hip -- paged FP8 KV-cache write at a per-tensor scale, and the K/V absolute
+// maximum that feeds the online calibration.
+//
+// staging.rs page: Fp8KvWriteTarget (strides in elements, pool stride = block_size *
+// heads * head_dim per block) and replay_and_release (the write's argument list); module
+// doc (one scale per tensor; chronological rewrites, last writer wins).
+// fp8_calibration.rs page: Fp8KvCalibration::absmax (max |K| and max |V|,
+// max-accumulated into a zeroed float pair).
+//
+// Layout inside a block is [offset][head][dim] (the pages give only the per-block stride
+// block_size*H*D, which this reading fills exactly), so one token's H*D codes are
+// contiguous: the write is a gather-free row copy-convert into a slot-addressed row.
+// Vector path: a thread converts 8 elements of K and the same 8 of V (two 16-byte loads,
+// two 8-byte stores); with H*D = 512 a wave covers one token, so the slot load is a
+// broadcast.  Division by the scale is the remainder-corrected reciprocal product with
+// an estimate clip (any positive scale is accepted; out-of-range values saturate).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8q.h"
+#include "fp8q_device.h"
+#include "fp8q_kv_internal.h"
+#include "fp8q_launch.h"
+
+#pragma clang fp contract(off)
+
+namespace fp8q {
+namespace {
+
+constexpr int kKvBlock = 256;
+
+__device__ __forceinline__ bool slot_to_block(int64_t slot, int64_t nslots, int bs,
+                                              int64_t* blk, int64_t* off) {
+  if (slot < 0 || slot >= nslots) return false;
+  if (nslots <= 0x7FFFFFFF) {
+    const uint32_t s = uint32_t(slot);
+    *blk = int64_t(s / uint32_t(bs));
+    *off = int64_t(s % uint32_t(bs));
+  } else {
+    *blk = slot / bs;
+    *off = slot % bs;
+  }
+  return true;
+}
+
+// Thread layout for every kernel below: blockDim = (64, 4), one wave per token row, so
+// a row's slot is uniform across the wave and read once into a scalar register.
+constexpr int kRowsPerBlock = 4;
+
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+// ept = elements per token / 8; ks8, vs8 = source row strides / 8; cs8 = pool stride / 8.
+__global__ __launch_bounds__(kKvBlock) void kv_write_vec_kernel(
+    const uint4* __restrict__ k, const uint4* __restrict__ v, uint2* __restrict__ kc,
+    uint2* __restrict__ vc, const int64_t* __restrict__ slots, int64_t num_tokens, int ept,
+    int64_t ks8, int64_t vs8, int64_t cs8, int bs, int64_t nslots, float k_scale,
+    float k_inv, float v_scale, float v_inv) {
+  for (int64_t t = int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.y; t < num_tokens;
+       t += int64_t(gridDim.x) * kRowsPerBlock) {
+    int64_t blk, off;
+    if (!slot_to_block(uniform(slots[t]), nslots, bs, &blk, &off)) continue;
+    const uint4* kr = k + t * ks8;
+    const uint4* vr = v + t * vs8;
+    uint2* kd = kc + blk * cs8 + off * ept;
+    uint2* vd = vc + blk * cs8 + off * ept;
+    for (int c = threadIdx.x; c < ept; c += 64) {
+      const uint4 kx = kr[c];
+      const uint4 vx = vr[c];
+      kd[c] = quant8<true>(kx, k_scale, k_inv);
+      vd[c] = quant8<true>(vx, v_scale, v_inv);
+    }
+  }
+}
+
+__device__ __forceinline__ uint8_t e4m3_one(float v) {
+  return uint8_t(__builtin_amdgcn_cvt_pk_fp8_f32(clip448(v), 0.0f, 0, false) & 0xFF);
+}
+
+// Element-wise path for any geometry and alignment.
+__global__ __launch_bounds__(kKvBlock) void kv_write_scalar_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint8_t* __restrict__ kc,
+    uint8_t* __restrict__ vc, const int64_t* __restrict__ slots, int64_t num_tokens, int e,
+    int64_t ks, int64_t vs, int64_t cs, int bs, int64_t nslots, float k_scale, float k_inv,
+    float v_scale, float v_inv) {
+  for (int64_t t = int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.y; t < num_tokens;
+       t += int64_t(gridDim.x) * kRowsPerBlock) {
+    int64_t blk, off;
+    if (!slot_to_block(uniform(slots[t]), nslots, bs, &blk, &off)) continue;
+    const int64_t dst = blk * cs + off * e;
+    for (int c = threadIdx.x; c < e; c += 64) {
+      kc[dst + c] = e4m3_one(div_by_scale_clipped(bf16_to_f32(k[t * ks + c]), k_scale, k_inv));
+      vc[dst + c] = e4m3_one(div_by_scale_clipped(bf16_to_f32(v[t * vs + c]), v_scale, v_inv));
+    }
+  }
+}
+
+// max |x| over a packed run of n8 16-byte words; blockIdx.y picks K (0) or V (1).
+__global__ __launch_bounds__(kKvBlock) void amax_flat_kernel(const uint4* __restrict__ k,
+                                                             const uint4* __restrict__ v,
+                                                             int64_t n8,
+                                                             float* __restrict__ amax2) {
+  const uint4* x = blockIdx.y ? v : k;
+  const int64_t stride = int64_t(gridDim.x) * kKvBlock;
+  float m = 0.0f;
+  for (int64_t i = int64_t(blockIdx.x) * kKvBlock + threadIdx.x; i < n8; i += stride)
+    m = fmaxf(m, absmax8(x[i]));
+  m = max_over_wave(m);
+  if ((threadIdx.x & 63) == 0 && m > 0.0f)
+    atomicMax(reinterpret_cast<unsigned int*>(amax2 + blockIdx.y), __float_as_uint(m));
+}
+
+// max |x| over `rows` rows of `row_elems` bf16 at row strides ks / vs (any alignment).
+__global__ __launch_bounds__(kKvBlock) void amax_rows_kernel(const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v,
+                                                             int64_t rows, int row_elems,
+                                                             int64_t ks, int64_t vs,
+                                                             float* __restrict__ amax2) {
+  const uint16_t* x = blockIdx.y ? v : k;
+  const int64_t s = blockIdx.y ? vs : ks;
+  float m = 0.0f;
+  for (int64_t r = int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.y; r < rows;
+       r += int64_t(gridDim.x) * kRowsPerBlock)
+    for (int c = threadIdx.x; c < row_elems; c += 64)
+      m = fmaxf(m, fabsf(bf16_to_f32(x[r * s + c])));
+  m = max_over_wave(m);
+  if (threadIdx.x == 0 && m > 0.0f)
+    atomicMax(reinterpret_cast<unsigned int*>(amax2 + blockIdx.y), __float_as_uint(m));
+}
+
+}  // namespace
+
+int kv_amax_rows(const uint16_t* k, const uint16_t* v, int64_t rows, int64_t row_elems,
+                 int64_t key_stride, int64_t value_stride, float* amax2, hipStream_t stream) {
+  if (rows == 0 || row_elems == 0) return FP8Q_OK;
+  const int64_t n = rows * row_elems;
+  if (key_stride == row_elems && value_stride == row_elems && n % 8 == 0 && aligned(k, 16) &&
+      aligned(v, 16)) {
+    // a few hundred thousand threads saturate the read; more would only add atomics
+    int64_t blocks = (n / 8 + kKvBlock - 1) / kKvBlock;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(amax_flat_kernel, dim3(unsigned(blocks), 2), dim3(kKvBlock), 0, stream,
+                       reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
+                       n / 8, amax2);
+  } else {
+    if (row_elems > 0x7FFFFFFF) return FP8Q_EINVAL;
+    int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(amax_rows_kernel, dim3(unsigned(blocks), 2), dim3(64, kRowsPerBlock), 0,
+                       stream, k, v, rows, int(row_elems), key_stride, value_stride, amax2);
+  }
+  return launch_status();
+}
+
+int kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t* v_cache,
+             const int64_t* slot_mapping, int32_t num_tokens, int32_t heads, int32_t head_dim,
+             int32_t block_size, int64_t num_blocks, float k_scale, float v_scale,
+             int64_t key_stride, int64_t value_stride, int64_t cache_stride,
+             hipStream_t stream) {
+  const int64_t e = int64_t(heads) * head_dim;
+  const int64_t nslots = num_blocks * block_size;
+  // reciprocals on the host: IEEE binary32 division, RN(1/scale)
+  const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;
+  const bool vec = e % 8 == 0 && key_stride % 8 == 0 && value_stride % 8 == 0 &&
+                   cache_stride % 8 == 0 && aligned(k, 16) && aligned(v, 16) &&
+                   aligned(k_cache, 8) && aligned(v_cache, 8);
+  const int64_t blocks = clamp_grid((int64_t(num_tokens) + kRowsPerBlock - 1) / kRowsPerBlock);
+  if (vec)
+    hipLaunchKernelGGL(kv_write_vec_kernel, dim3(unsigned(blocks)), dim3(64, kRowsPerBlock), 0,
+                       stream, reinterpret_cast<const uint4*>(k),
+                       reinterpret_cast<const uint4*>(v), reinterpret_cast<uint2*>(k_cache),
+                       reinterpret_cast<uint2*>(v_cache), slot_mapping, int64_t(num_tokens),
+                       int(e / 8), key_stride / 8, value_stride / 8, cache_stride / 8,
+                       block_size, nslots, k_scale, k_inv, v_scale, v_inv);
+  else
+    hipLaunchKernelGGL(kv_write_scalar_kernel, dim3(unsigned(blocks)), dim3(64, kRowsPerBlock),
+                       0, stream, k, v, k_cache, v_cache, slot_mapping, int64_t(num_tokens),
+                       int(e), key_stride, value_stride, cache_stride, block_size, nslots,
+                       k_scale, k_inv, v_scale, v_inv);
+  return launch_status();
+}
+
+}  // namespace fp8q
+
+using namespace fp8q;
+
+extern "C" int fp8_kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache,
+                            uint8_t* v_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int64_t num_blocks, float k_scale, float v_scale,
+                            int32_t key_stride, int32_t value_stride, int64_t cache_stride,
+                            hipStream_t stream) {
+  const int rc = kv_write_check(num_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                                k_scale, v_scale, key_stride, value_stride, cache_stride);
+  if (rc != FP8Q_OK) return rc;
+  if (num_tokens == 0) return FP8Q_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return FP8Q_ENULL;
+  if (!aligned(slot_mapping, 8)) return FP8Q_EALIGN;
+  return kv_write(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                  block_size, num_blocks, k_scale, v_scale, key_stride, value_stride,
+                  cache_stride, stream);
+}
+
+extern "C" int fp8_kv_amax(const uint16_t* k, const uint16_t* v, int64_t n_elems,
+                           float* amax2, hipStream_t stream) {
+  if (n_elems < 0) return FP8Q_EINVAL;
+  if (n_elems == 0) return FP8Q_OK;
+  if (!k || !v || !amax2) return FP8Q_ENULL;
+  if (!aligned(amax2, 4)) return FP8Q_EALIGN;
+  return kv_amax_rows(k, v, 1, n_elems, n_elems, n_elems, amax2, stream);
+}

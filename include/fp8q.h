@@ -1,0 +1,231 @@
+/*
+ * fp8q.h -- C ABI of libfp8q.so: the FP8 (OCP E4M3) quantize-and-consume path on
+ * AMD MI355X (gfx950).
+ *
+ * Conventions for every call
+ *   - Device buffers are plain device pointers owned by the caller; the library never
+ *     keeps them past the call (the calibrator keeps only its own staging copies).
+ *   - bf16 data is passed as its 16-bit pattern (uint16_t), E4M3 codes as uint8_t, scales
+ *     as IEEE binary32.  E4M3 is the OCP "FN" encoding: bias 7, no infinities,
+ *     S.1111.111 = NaN, largest finite 448.  Encoding is round-to-nearest-even after one
+ *     IEEE binary32 division by the scale, saturating to +-448 (never NaN); the sign is
+ *     kept, so a negative value that rounds to zero is 0x80.
+ *   - Work is enqueued on `stream` (0 = the null stream) and returns without waiting.
+ *     No call allocates or synchronizes, except the calibrator as documented.
+ *   - Arguments are validated on the host before anything is enqueued; a bad argument
+ *     returns a negative FP8Q_E* code and enqueues nothing.  0 means success.  No C++
+ *     exception crosses this boundary.
+ *
+ * Sources (the pages this path comes from, cited by page title and the item on it):
+ *   [actq]    spark_model/layers/ops/fp8_act_quant.rs
+ *   [decode]  spark_model/layers/ops/dispatch_proj_decode.rs
+ *   [staging] spark_model/layers/fp8_calibration/staging.rs
+ *   [calib]   metrale_model_layers/layers/fp8_calibration.rs
+ *   [resid]   fp8_residency.rs (weight loader page), fp8_twin_bytes
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ----------------------------------------------------------------- status codes */
+#define FP8Q_OK 0
+#define FP8Q_EINVAL (-1) /* a size, stride or scale outside the contract */
+#define FP8Q_ENULL (-2)  /* a required pointer is NULL */
+#define FP8Q_EALIGN (-3) /* a pointer or stride breaks the documented alignment */
+#define FP8Q_ELAUNCH (-4) /* the kernel launch was rejected by the HIP runtime */
+#define FP8Q_EHIP (-5)   /* another HIP runtime call failed (alloc, copy, sync) */
+#define FP8Q_ESTATE (-6) /* calibrator used against its contract (e.g. new device) */
+
+/* Human-readable text for a status code (static storage). */
+const char* fp8q_strerror(int status);
+/* Library version, major*10000 + minor*100 + patch. */
+int fp8q_version(void);
+
+/* ------------------------------------------------ per-token 1x128 group quant
+ * [actq] module doc: one FP32 scale per 128-wide K-group of one token row;
+ * [decode] decode_w8a8_quant_act: the activation is quantized once and shared by every
+ * projection that reads it, scales in token-major [m, k/128] order.
+ *
+ * For every row r < m and group g < k/128:
+ *   amax = max_j |x[r, 128g + j]|            (exact)
+ *   s    = max(amax, 1e-10f) / 448.0f        (binary32, correctly rounded)
+ *   scales[r * (k/128) + g] = s
+ *   q[r, 128g + j] = E4M3(x[r, 128g + j] / s)
+ *
+ *   x       device, bf16 [m, k] row-major, 16-byte aligned
+ *   q       device, uint8 [m, k] row-major, 16-byte aligned
+ *   scales  device, fp32 [m, k/128] row-major, 4-byte aligned
+ *   m       rows, 0 <= m (0 is a no-op); m * k < 2^62
+ *   k       columns, k > 0 and k % 128 == 0 (the pages' grid is k/128 groups)
+ * Errors: FP8Q_EINVAL (k, m), FP8Q_ENULL, FP8Q_EALIGN, FP8Q_ELAUNCH. */
+int fp8_group_quant(const uint16_t* x, uint8_t* q, float* scales, int64_t m, int32_t k,
+                    hipStream_t stream);
+
+/* ---------------------------------------------- 128x128 weight block quant
+ * [decode] module doc, NUMERICS: E4M3 weights carry one FP32 scale per 128x128 block;
+ * [resid] fp8_twin_bytes: the grid has ceil(n/128) * ceil(k/128) fp32 entries.
+ * The same formula as fp8_group_quant over each 128x128 block (edge blocks clipped):
+ *   ws[nb * ceil(k/128) + kb] = max(amax_block, 1e-10f) / 448.0f
+ *   wq[i, j] = E4M3(w[i, j] / ws[i/128, j/128])
+ *   w   device, bf16 [n, k] row-major; wq device, uint8 [n, k]; ws device, fp32 grid
+ *   n, k > 0.  A preparation utility (weights arrive pre-quantized on the pages).
+ * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_ELAUNCH. */
+int fp8_block_quant(const uint16_t* w, uint8_t* wq, float* ws, int32_t n, int32_t k,
+                    hipStream_t stream);
+
+/* -------------------------------------------- element-wise binary32 -> E4M3
+ * The encoder every kernel above uses, exposed on its own: q[i] = E4M3(x[i]) for finite
+ * x, round-to-nearest-even, saturating to +-448 (no scale).
+ *   x device fp32 [n], q device uint8 [n], n >= 0.  Errors: FP8Q_EINVAL, FP8Q_ENULL,
+ *   FP8Q_ELAUNCH. */
+int fp8_e4m3_encode(const float* x, uint8_t* q, int64_t n, hipStream_t stream);
+
+/* ----------------------------------------------- block-scaled W8A8 decode GEMM
+ * [decode] decode_w8a8_gemm and module doc NUMERICS: out = act_fp8 @ weight^T with the
+ * per-token 1x128 activation scales and the 128x128 weight block scales folded in an
+ * FP32 epilogue; DecodeW8a8Plan / decode_w8a8_selected: n % 128 == 0, k % 128 == 0,
+ * ldc >= n; DECODE_W8A8_ROWS: the decode band is up to 16 rows; strided_out_extent_elems:
+ * a call touches (rows - 1) * ldc + n elements of `out`.
+ *
+ *   out[r, c] = bf16_rne( sum_g a_scale[r, g] * w_scale[c/128, g]
+ *                                * sum_{j<128} dec(a_q[r, 128g+j]) * dec(w_q[c, 128g+j]) )
+ * with FP32 products and accumulation.  Only rows 0..m-1 are written: exactly the
+ * (m - 1) * ldc + n elements starting at `out`, columns n..ldc-1 of each row untouched.
+ *
+ *   a_q      device, uint8 [m, k] row-major (E4M3 codes), 16-byte aligned
+ *   a_scale  device, fp32 [m, k/128] token-major (fp8_group_quant's own order)
+ *   w_q      device, uint8 [n, k] row-major (K contiguous), 16-byte aligned
+ *   w_scale  device, fp32 [n/128, k/128]; block (nb, kb) at nb * (k/128) + kb
+ *   out      device, bf16 [m, ldc] row-major, 2-byte aligned
+ *   1 <= m <= 16; n > 0, n % 128 == 0; k > 0, k % 128 == 0, k <= 131072; ldc >= n.
+ * Codes 0x7F/0xFF (NaN) in a_q or w_q propagate NaN into the affected outputs.
+ * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EALIGN, FP8Q_ELAUNCH. */
+int w8a8_block_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
+                    const float* w_scale, uint16_t* out, int32_t m, int32_t n, int32_t k,
+                    int32_t ldc, hipStream_t stream);
+
+/* --------------------------------------------------------- paged FP8 KV write
+ * [staging] Fp8KvWriteTarget and replay_and_release (the write's arguments: strides in
+ * elements, pool stride = block_size * heads * head_dim); [staging] module doc: one scale
+ * per tensor, later writes of a slot replace earlier ones.
+ *
+ * For each token t < num_tokens with 0 <= slot < num_blocks * block_size (slot =
+ * slot_mapping[t]; other slots are skipped -- negative ones are padding):
+ *   b = slot / block_size, o = slot % block_size, for all h < H, d < D:
+ *   k_cache[b * cache_stride + (o * H + h) * D + d] = E4M3(k[t * key_stride + h*D + d] / k_scale)
+ *   v_cache[... same index ...]                       = E4M3(v[t * value_stride + h*D + d] / v_scale)
+ * Slots must be distinct within one call (two tokens on one slot race).
+ *
+ *   k, v            device bf16 rows of key_stride / value_stride elements
+ *   k_cache,v_cache device uint8 pools of num_blocks * cache_stride bytes each
+ *   slot_mapping    device int64 [num_tokens]
+ *   num_tokens >= 0 (0 is a no-op); num_kv_heads, head_dim, block_size, num_blocks > 0;
+ *   key_stride, value_stride >= H*D; cache_stride >= block_size*H*D;
+ *   k_scale, v_scale in [2^-64, 2^64] (dequantization multipliers).
+ * The vector path needs 16-byte aligned k/v/pools and H*D, strides, cache_stride all
+ * multiples of 8; anything else takes an element-wise path with the same results.
+ * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_ELAUNCH. */
+int fp8_kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t* v_cache,
+                 const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                 int32_t head_dim, int32_t block_size, int64_t num_blocks, float k_scale,
+                 float v_scale, int32_t key_stride, int32_t value_stride,
+                 int64_t cache_stride, hipStream_t stream);
+
+/* ------------------------------------------------------------- KV absolute max
+ * [calib] Fp8KvCalibration::absmax: max |K| and max |V| of a batch, max-accumulated into
+ * a device float[2] that the caller zeroes once (so a window's running max can stay on
+ * the device).
+ *   amax2[0] = max(amax2[0], max_i |k[i]|), amax2[1] = max(amax2[1], max_i |v[i]|)
+ *   k, v device bf16 [n_elems] packed; amax2 device fp32[2], 4-byte aligned, >= +0.0
+ *   n_elems >= 0.  Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_ELAUNCH. */
+int fp8_kv_amax(const uint16_t* k, const uint16_t* v, int64_t n_elems, float* amax2,
+                hipStream_t stream);
+
+/* ----------------------------------------------- online KV scale calibrator
+ * [calib] module doc, PROVISIONAL_SCALE, Fp8KvCalibration::{new, observe, scales};
+ * [staging] module doc ("The fix, and its tradeoff"), KvStaging::{stage,
+ * replay_and_release, release}, MAX_STAGED_TOKENS.
+ *
+ * One attention layer's per-tensor K/V scale calibration.  Inside the window each
+ * observed batch's |K|/|V| maximum folds into a running maximum kept on the device, and
+ * the batch (bf16 rows + slots) is copied into packed staging; the caller then writes
+ * it at the provisional scale 2.0.  The observe whose token count reaches the window
+ * freezes scale = (max(amax, 1e-10) * headroom) / 448 for K and V over every observed
+ * token including its own batch, replays the staged batches in observation order at the
+ * frozen scales into the target pools, and frees the staging; the caller then writes
+ * that batch at the frozen scales.  Later observes do nothing.  A batch whose heads x
+ * head_dim differ from the first staged batch is not staged (it keeps the provisional
+ * scale).  The window is clamped to 4096 tokens and headroom to >= 1.
+ * Call order per batch: fp8q_kv_calib_observe, then fp8q_kv_calib_scales, then the
+ * caller's fp8_kv_write of that batch, all on one stream. */
+typedef struct fp8q_kv_calib fp8q_kv_calib;
+
+/* Where the replay writes (the live write's own pools and geometry). */
+typedef struct fp8q_kv_target {
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  const int64_t* slot_mapping; /* this batch's slots, int64 [num_tokens] */
+  int32_t block_size;
+  int32_t key_stride;          /* row stride of the observed K, elements */
+  int32_t value_stride;        /* row stride of the observed V, elements */
+  int32_t reserved;
+  int64_t cache_stride;        /* elements per block = block_size * H * D or more */
+  int64_t num_blocks;          /* blocks in each pool */
+} fp8q_kv_target;
+
+typedef struct fp8q_kv_calib_info {
+  int32_t window_tokens;    /* after the 4096 clamp */
+  int32_t requested_tokens; /* as passed to create */
+  int32_t frozen;
+  int32_t staged_batches;
+  int64_t tokens_seen;
+  int64_t staged_tokens;
+  int64_t unstaged_tokens;  /* tokens of declined batches */
+  int64_t replayed_tokens;  /* tokens rewritten at the freeze */
+  float k_scale;            /* provisional until frozen */
+  float v_scale;
+  float k_amax;             /* running maxima read at the freeze (0 before) */
+  float v_amax;
+  float headroom;           /* after the >= 1 clamp */
+  float provisional_scale;
+} fp8q_kv_calib_info;
+
+/* What observe would do with a batch, without doing it. */
+#define FP8Q_CALIB_STAGE 0
+#define FP8Q_CALIB_DECLINE 1
+#define FP8Q_CALIB_FREEZE 2
+#define FP8Q_CALIB_FROZEN 3
+
+/* window_tokens > 0 (window 0 means no calibrator: FP8Q_EINVAL); headroom finite.
+ * Allocates host state only; device buffers are allocated on the first observe, on the
+ * device current then.  *out receives the handle. */
+int fp8q_kv_calib_create(int32_t window_tokens, float headroom, fp8q_kv_calib** out);
+/* Fold one batch in (see above).  k, v: device bf16 [num_tokens] rows at the target's
+ * key/value strides.  Enqueues work on `stream`; synchronizes `stream` only at the freeze
+ * (to read the 8-byte running maximum, and again before freeing the staging).  The
+ * first staged batch allocates the staging (window * H * D * 2 * 2 + window * 8 bytes).
+ * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EHIP, FP8Q_ELAUNCH, FP8Q_ESTATE. */
+int fp8q_kv_calib_observe(fp8q_kv_calib* c, const uint16_t* k, const uint16_t* v,
+                          int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                          const fp8q_kv_target* target, hipStream_t stream);
+/* Pure query: FP8Q_CALIB_* for a batch of num_tokens x elems_per_token, or < 0. */
+int fp8q_kv_calib_decide(const fp8q_kv_calib* c, int32_t num_tokens,
+                         int32_t elems_per_token);
+/* The scales the caller writes with now (provisional 2.0 until the freeze). */
+int fp8q_kv_calib_scales(const fp8q_kv_calib* c, float* k_scale, float* v_scale);
+int fp8q_kv_calib_get_info(const fp8q_kv_calib* c, fp8q_kv_calib_info* info);
+/* Frees staging and device state (synchronizing the device that owns them). NULL ok. */
+void fp8q_kv_calib_destroy(fp8q_kv_calib* c);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

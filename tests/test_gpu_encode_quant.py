@@ -1,0 +1,125 @@
+"""GPU parity: the element-wise E4M3 encoder, the per-token 1x128 group quantizer and the
+128x128 block quantizer against the CPU oracle, bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_e4m3_quantization_amd as fq
+from fp8_e4m3_quantization_amd import synth
+from tests.gpu_util import DEV, bf16_dev, host, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(_):
+    need_gpu()
+
+
+def test_encode_every_binary32_in_range_matches_oracle():
+    """All binary32 patterns with 2^-12 <= |v| < 2^10 (both signs), 2^24 at a time."""
+    lo = int(np.float32(2.0 ** -12).view(np.uint32))
+    hi = int(np.float32(1024.0).view(np.uint32))
+    step = 1 << 24
+    for a in range(lo, hi, step):
+        bits = np.arange(a, min(a + step, hi), dtype=np.uint32)
+        v = bits.view(np.float32)
+        for vv in (v, -v):
+            x = torch.from_numpy(vv).to(DEV)
+            got = host(fq.fp8_e4m3_encode(x))
+            ref = oracle.e4m3_encode(vv)
+            if not np.array_equal(got, ref):
+                i = int(np.flatnonzero(got != ref)[0])
+                pytest.fail(f"v={vv[i]!r} gpu={got[i]:#x} oracle={ref[i]:#x}")
+
+
+def test_encode_special_values():
+    v = np.array([0.0, -0.0, 1e-30, -1e-30, 1e-45, -1e-45, 2.0 ** -10, -(2.0 ** -10),
+                  448.0, -448.0, 463.99, 464.0, -464.0, 1e6, -1e6, 3.4e38, -3.4e38],
+                 dtype=np.float32)
+    got = host(fq.fp8_e4m3_encode(torch.from_numpy(v).to(DEV)))
+    assert np.array_equal(got, oracle.e4m3_encode(v)), (got, oracle.e4m3_encode(v))
+
+
+def _gq(x_bits):
+    q, s = fq.fp8_group_quant(bf16_dev(x_bits))
+    return host(q), host(s)
+
+
+def _assert_quant_equal(x_bits):
+    q, s = _gq(x_bits)
+    q_ref, s_ref = oracle.group_quant(x_bits)
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32)), "scales differ"
+    if not np.array_equal(q, q_ref):
+        idx = np.argwhere(q != q_ref)[0]
+        pytest.fail(f"code differs at {tuple(idx)}: gpu={q[tuple(idx)]:#x} "
+                    f"oracle={q_ref[tuple(idx)]:#x} x={x_bits[tuple(idx)]:#x}")
+
+
+def test_group_quant_tiny_end_to_end_activation():
+    a, _ = synth.tiny_e2e(seed=0)
+    _assert_quant_equal(a)
+
+
+@pytest.mark.parametrize("k", synth.PREFILL_K)
+def test_group_quant_prefill_full_size(k):
+    _assert_quant_equal(synth.prefill_activation(k, seed=3000 + k))
+
+
+@pytest.mark.parametrize("m", synth.SWEEP_M + (1, 3))
+def test_group_quant_decode_rows(m):
+    _assert_quant_equal(synth.decode_activation(m, seed=2000 + m))
+
+
+@pytest.mark.parametrize("m,k", [(1, 128), (2, 256), (3, 384), (7, 640), (33, 128),
+                                 (5, 1152), (129, 256)])
+def test_group_quant_ragged_shapes(m, k):
+    rng = np.random.default_rng(m * 1000 + k)
+    _assert_quant_equal(synth.to_bf16_bits(
+        synth.normal_with_outliers(rng, (m, k), 2.0, 0.01, 50.0)))
+
+
+def test_group_quant_edge_values():
+    rng = np.random.default_rng(7)
+    x = synth.to_bf16_bits(rng.normal(0, 1, size=(6, 256)))
+    x[0, :] = 0                       # all-zero group -> floor scale, zero codes
+    x[1, :128] = 0x8000               # negative zeros
+    x[1, 128:] = 0x0001               # smallest bf16 subnormal
+    x[2, :128] = 0x7F7F               # bf16 max magnitude
+    x[2, 64] = 0xFF7F
+    x[3, :] = synth.to_bf16_bits(rng.normal(0, 1e-20, size=256))  # tiny group
+    x[4, :128] = synth.to_bf16_bits(rng.normal(0, 1, size=128)) | 0x8000  # all negative
+    _assert_quant_equal(x)
+
+
+def test_group_quant_ties_through_the_whole_path():
+    """amax = 448 gives s = 1 exactly, so quotients are the inputs: every E4M3 midpoint
+    that bf16 can hold lands on a tie and must round to the even code."""
+    vals = oracle.e4m3_decode_table()[:0x7F]
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    bits = synth.to_bf16_bits(mids)
+    exact = synth.bf16_bits_to_f32(bits) == mids
+    row = np.concatenate([bits[exact], (bits[exact] | 0x8000)])
+    row = np.resize(row, 128 * 2).astype(np.uint16)
+    row[0] = synth.to_bf16_bits(np.array([448.0]))[0]
+    row[128] = synth.to_bf16_bits(np.array([-448.0]))[0]
+    x = np.stack([row, row[::-1].copy()])
+    q, s = _gq(x)
+    assert np.all(s == 1.0)
+    _assert_quant_equal(x)
+
+
+def test_group_quant_zero_rows_is_a_noop():
+    x = torch.zeros((0, 256), dtype=torch.bfloat16, device=DEV)
+    q, s = fq.fp8_group_quant(x)
+    assert q.numel() == 0
+
+
+@pytest.mark.parametrize("n,k", [(1024, 512), (384, 5120), (200, 300), (130, 1)])
+def test_block_quant_matches_oracle(n, k):
+    rng = np.random.default_rng(n + k)
+    w = synth.to_bf16_bits(rng.normal(0, 0.02, size=(n, k)))
+    wq, ws = fq.fp8_block_quant(bf16_dev(w))
+    wq_ref, ws_ref = oracle.block_quant(w)
+    assert np.array_equal(host(ws).view(np.uint32), ws_ref.view(np.uint32))
+    assert np.array_equal(host(wq), wq_ref)

@@ -1,0 +1,179 @@
+"""GPU parity: paged FP8 KV write, K/V absmax and the online scale calibrator against the
+CPU oracle -- pool bytes, scales and counters bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_e4m3_quantization_amd as fq
+from fp8_e4m3_quantization_amd import synth
+from tests.gpu_util import DEV, bf16_dev, host, i64_dev, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+H, D, BS, NB = synth.KV_HEADS, synth.KV_HEAD_DIM, synth.KV_BLOCK_SIZE, synth.KV_NUM_BLOCKS
+E = H * D
+CS = BS * E
+
+
+def setup_module(_):
+    need_gpu()
+
+
+def _pools(fill_k=0xAA, fill_v=0x55, nblk=NB, cs=CS):
+    kc = np.full(nblk * cs, fill_k, dtype=np.uint8)
+    vc = np.full(nblk * cs, fill_v, dtype=np.uint8)
+    return kc, vc, torch.from_numpy(kc.copy()).to(DEV), torch.from_numpy(vc.copy()).to(DEV)
+
+
+def test_full_pool_write_matches_oracle():
+    b = synth.kv_full_pool()
+    kc, vc, kcd, vcd = _pools()
+    ks, vs = 3.0 * 17.0 / 448.0, 0.0625
+    fq.fp8_kv_write(bf16_dev(b.k), bf16_dev(b.v), kcd, vcd, i64_dev(b.slots), H, D, BS, ks, vs)
+    oracle.kv_write(b.k, b.v, kc, vc, b.slots, len(b.slots), H, D, BS, ks, vs, E, E, CS)
+    assert np.array_equal(host(kcd), kc) and np.array_equal(host(vcd), vc)
+
+
+def test_batches_provisional_scale_and_skips():
+    batches, _ = synth.kv_batches(num_tokens_total=400, seed=5010)
+    kc, vc, kcd, vcd = _pools()
+    for i, b in enumerate(batches):
+        slots = b.slots.copy()
+        if i % 3 == 0:
+            slots[0] = -1                   # padding token
+        if i % 4 == 1:
+            slots[-1] = NB * BS + 5         # outside the pool: skipped, never written
+        fq.fp8_kv_write(bf16_dev(b.k), bf16_dev(b.v), kcd, vcd, i64_dev(slots), H, D, BS,
+                        2.0, 2.0)
+        valid = np.where((slots >= 0) & (slots < NB * BS), slots, -1)
+        oracle.kv_write(b.k, b.v, kc, vc, valid, len(slots), H, D, BS, 2.0, 2.0, E, E, CS)
+    assert np.array_equal(host(kcd), kc) and np.array_equal(host(vcd), vc)
+
+
+def test_strided_sources_and_padded_pool_stride():
+    rng = np.random.default_rng(3)
+    t, ks, vs, cs = 50, E + 64, E + 8, CS + 128
+    k = synth.to_bf16_bits(rng.normal(0, 3, size=t * ks))
+    v = synth.to_bf16_bits(rng.normal(0, 3, size=t * vs))
+    slots = rng.permutation(64 * BS)[:t].astype(np.int64)
+    kc, vc, kcd, vcd = _pools(nblk=64, cs=cs)
+    fq.fp8_kv_write(bf16_dev(k), bf16_dev(v), kcd, vcd, i64_dev(slots), H, D, BS, 0.3, 0.7,
+                    key_stride=ks, value_stride=vs, cache_stride=cs, num_tokens=t)
+    oracle.kv_write(k, v, kc, vc, slots, t, H, D, BS, 0.3, 0.7, ks, vs, cs)
+    assert np.array_equal(host(kcd), kc) and np.array_equal(host(vcd), vc)
+
+
+@pytest.mark.parametrize("h,d,offset", [(3, 5, 0), (2, 64, 1), (1, 8, 3)])
+def test_elementwise_path_odd_geometry_and_alignment(h, d, offset):
+    rng = np.random.default_rng(h * d + offset)
+    e, t, bs, nblk = h * d, 37, 4, 16
+    ks = e + 3
+    kbuf = synth.to_bf16_bits(rng.normal(0, 3, size=t * ks + offset))
+    vbuf = synth.to_bf16_bits(rng.normal(0, 3, size=t * ks + offset))
+    slots = rng.permutation(nblk * bs)[:t].astype(np.int64)
+    cs = bs * e
+    kc, vc, kcd, vcd = _pools(nblk=nblk, cs=cs)
+    kd, vd = bf16_dev(kbuf)[offset:], bf16_dev(vbuf)[offset:]
+    fq.fp8_kv_write(kd, vd, kcd, vcd, i64_dev(slots), h, d, bs, 0.5, 3.0, key_stride=ks,
+                    value_stride=ks, num_tokens=t)
+    oracle.kv_write(kbuf[offset:].copy(), vbuf[offset:].copy(), kc, vc, slots, t, h, d, bs,
+                    0.5, 3.0, ks, ks, cs)
+    assert np.array_equal(host(kcd), kc) and np.array_equal(host(vcd), vc)
+
+
+def test_scale_far_below_values_saturates_with_sign():
+    rng = np.random.default_rng(9)
+    k = synth.to_bf16_bits(rng.normal(0, 1e3, size=(8, E)))
+    slots = np.arange(8, dtype=np.int64)
+    kc, vc, kcd, vcd = _pools(nblk=1)
+    fq.fp8_kv_write(bf16_dev(k), bf16_dev(k), kcd, vcd, i64_dev(slots), H, D, BS, 2.0 ** -60,
+                    2.0 ** 60)
+    oracle.kv_write(k, k, kc, vc, slots, 8, H, D, BS, 2.0 ** -60, 2.0 ** 60, E, E, CS)
+    assert np.array_equal(host(kcd), kc) and np.array_equal(host(vcd), vc)
+
+
+def test_amax_matches_oracle_and_accumulates():
+    batches, _ = synth.kv_batches(num_tokens_total=300, seed=5020)
+    amax2 = torch.zeros(2, dtype=torch.float32, device=DEV)
+    km = vm = np.float32(0)
+    for b in batches:
+        fq.fp8_kv_amax(bf16_dev(b.k), bf16_dev(b.v), amax2)
+        km = max(km, oracle.amax(b.k))
+        vm = max(vm, oracle.amax(b.v))
+        assert host(amax2).tolist() == [float(km), float(vm)]
+    odd = synth.to_bf16_bits(np.random.default_rng(1).normal(0, 1e4, size=1001))
+    fq.fp8_kv_amax(bf16_dev(odd), bf16_dev(odd), amax2)
+    assert host(amax2)[0] == max(km, oracle.amax(odd))
+
+
+def _calibrate_on_gpu(batches, window, headroom=1.0, decline_at=None):
+    kc, vc, kcd, vcd = _pools()
+    cal = fq.KvCalibrator(window, headroom)
+    for i, b in enumerate(batches):
+        if i == decline_at:
+            k2, v2 = np.ascontiguousarray(b.k[:, :256]), np.ascontiguousarray(b.v[:, :256])
+            kd, vd, h = bf16_dev(k2), bf16_dev(v2), 2
+        else:
+            kd, vd, h = bf16_dev(b.k), bf16_dev(b.v), H
+        sd = i64_dev(b.slots)
+        cal.observe(kd, vd, h, D, kcd, vcd, sd, BS, cache_stride=CS)
+        ks, vs = cal.scales()
+        fq.fp8_kv_write(kd, vd, kcd, vcd, sd, h, D, BS, ks, vs, cache_stride=CS)
+    info = cal.info()
+    cal.close()
+    return host(kcd), host(vcd), info
+
+
+def _calibrate_oracle(batches, window, headroom=1.0, decline_at=None):
+    kc, vc, _, _ = _pools()
+    cal = oracle.Calibrator(window, headroom)
+    for i, b in enumerate(batches):
+        if i == decline_at:
+            k2, v2 = np.ascontiguousarray(b.k[:, :256]), np.ascontiguousarray(b.v[:, :256])
+            cal._lib.oracle_calib_observe_and_write(
+                cal._c, k2.ctypes.data, v2.ctypes.data, b.slots.ctypes.data, len(b.slots),
+                2, D, BS, CS, kc.ctypes.data, vc.ctypes.data)
+        else:
+            cal.observe_and_write(b.k, b.v, b.slots, H, D, BS, CS, kc, vc)
+    info = cal.info()
+    cal.close()
+    return kc, vc, info
+
+
+@pytest.mark.parametrize("window,headroom,seed", [(256, 1.0, 5000), (256, 1.5, 5001),
+                                                  (1, 1.0, 5002), (100, 0.5, 5003)])
+def test_calibration_matches_oracle(window, headroom, seed):
+    batches, reuse = synth.kv_batches(num_tokens_total=synth.KV_WINDOW + 96, seed=seed)
+    kc, vc, info = _calibrate_on_gpu(batches, window, headroom)
+    kc_ref, vc_ref, ref = _calibrate_oracle(batches, window, headroom)
+    assert info["frozen"] == 1 and ref["frozen"] == 1
+    for key in ("k_scale", "v_scale", "k_amax", "v_amax"):
+        ref_key = key.replace("amax", "max")
+        assert np.float32(info[key]) == ref[ref_key], key
+    assert info["tokens_seen"] == ref["tokens_seen"]
+    assert info["replayed_tokens"] == ref["replayed_tokens"]
+    assert info["staged_batches"] == ref["staged_batches"]
+    assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+
+
+def test_calibration_with_a_declined_batch_matches_oracle():
+    batches, _ = synth.kv_batches(num_tokens_total=synth.KV_WINDOW + 96, seed=5004)
+    kc, vc, info = _calibrate_on_gpu(batches, synth.KV_WINDOW, decline_at=1)
+    kc_ref, vc_ref, ref = _calibrate_oracle(batches, synth.KV_WINDOW, decline_at=1)
+    assert info["unstaged_tokens"] == ref["unstaged_tokens"] == len(batches[1].slots)
+    assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+
+
+def test_calibration_reuse_inside_window_equals_single_pass():
+    """A slot rewritten after free/re-allocation inside the window: the replayed pools
+    equal one chronological pass over every batch at the frozen scales."""
+    batches, reuse = synth.kv_batches(num_tokens_total=synth.KV_WINDOW + 96, seed=5000)
+    kc, vc, info = _calibrate_on_gpu(batches, synth.KV_WINDOW)
+    cross = int(np.searchsorted(np.cumsum([len(b.slots) for b in batches]), synth.KV_WINDOW))
+    assert any(bi <= cross for bi, _ in reuse)
+    kc2, vc2, _, _ = _pools()
+    for b in batches:
+        oracle.kv_write(b.k, b.v, kc2, vc2, b.slots, len(b.slots), H, D, BS, info["k_scale"],
+                        info["v_scale"], E, E, CS)
+    assert np.array_equal(kc, kc2) and np.array_equal(vc, vc2)
