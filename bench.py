@@ -1,0 +1,466 @@
+"""Benchmark of the FP8 (E4M3) quantize-and-consume path on one MI355X.
+
+One step = one pass of the whole hot path over one decode batch:
+  per-token 1x128 group quant of the activation [16 x 5120] (bf16 -> E4M3 + scales),
+  the four decode projections sharing it (W8A8 block-scaled GEMM, M=16, K=5120,
+  N = 16384, 12288, 5120, 1024), the K/V absmax and the paged FP8 KV write of the batch's
+  16 new tokens (4 KV heads x 128 dims) at the calibrated scale.
+The step is captured once per buffer set in a HIP graph; inputs rotate over >= 1 GB of
+buffer sets so the 256 MB MALL cannot serve repeated reads.  value = algorithmic bytes
+per step / measured step time (GB/s).
+
+Also measured (same process, same rotation rule): each kernel on its own, timed with HIP
+events around every launch while the stream is held busy so no host latency leaks into
+an interval -- the group quantizer on the 4593-token prefill (K = 5120 and 16384), the
+GEMM at each N, the quant+GEMM pair at M = 5, 8, 12, 16 (N = 16384), and the KV write and
+absmax over a full 2048-block pool.  The roofline object covers the dominant kernel (the
+N=16384 GEMM); cpu_baseline times the CPU oracle on one full step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, published
+ROTATE_BYTES = 1 << 30     # >= 4x the 256 MB MALL
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--iters", type=int, default=100, help="launches per kernel measurement")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", default="", help="comma list: step,quant,gemm,sweep,kv")
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ algorithmic bytes
+
+M_DECODE, K_DECODE = 16, 5120
+N_DECODE = (16384, 12288, 5120, 1024)
+KV_H, KV_D, KV_BS, KV_NB = 4, 128, 16, 2048
+
+
+def quant_bytes(m, k):
+    return m * k * 2 + m * k + m * (k // 128) * 4
+
+
+def gemm_bytes(m, n, k):
+    g = k // 128
+    return n * k + (n // 128) * g * 4 + m * k + m * g * 4 + m * n * 2
+
+
+def gemm_weight_bytes(n, k):
+    return n * k + (n // 128) * (k // 128) * 4
+
+
+def kv_write_bytes(t, e=KV_H * KV_D):
+    return t * (2 * e * 2 + 2 * e + 8)
+
+
+def kv_amax_bytes(t, e=KV_H * KV_D):
+    return 2 * t * e * 2
+
+
+def grouped_gemm_bytes(m, ns, k):
+    """Several projections of one activation in one launch: the activation is read once."""
+    return sum(gemm_bytes(m, n, k) for n in ns) - (len(ns) - 1) * (m * k + m * (k // 128) * 4)
+
+
+def step_bytes():
+    return (quant_bytes(M_DECODE, K_DECODE) + grouped_gemm_bytes(M_DECODE, N_DECODE, K_DECODE)
+            + kv_amax_bytes(M_DECODE) + kv_write_bytes(M_DECODE))
+
+
+# ------------------------------------------------------------------------- timing
+
+
+class Timer:
+    """Kernel durations from HIP events recorded by the kernel dispatch itself: the library
+    launches its next kernel with hipExtLaunchKernelGGL(start, stop) after
+    fp8q_time_next_launch, so an event pair spans exactly one kernel's execution."""
+
+    def __init__(self, torch, lib):
+        import ctypes
+
+        self.torch = torch
+        self.lib = lib
+        self.hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+        self.ct = ctypes
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pool = [self._event() for _ in range(2 * 512)]
+
+    def _event(self):
+        ev = self.ct.c_void_p()
+        if self.hip.hipEventCreate(self.ct.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev
+
+    def kernel_us(self, launches, iters):
+        """launches: callables each enqueueing one library kernel, cycled over; returns
+        (mean_us, median_us) of the kernels' own durations."""
+        assert iters <= len(self.pool) // 2
+        self.torch.cuda.synchronize()
+        for i in range(iters):
+            a, b = self.pool[2 * i], self.pool[2 * i + 1]
+            self.lib.fp8q_time_next_launch(a, b)
+            launches[i % len(launches)]()
+        self.torch.cuda.synchronize()
+        us = []
+        ms = self.ct.c_float()
+        for i in range(iters):
+            a, b = self.pool[2 * i], self.pool[2 * i + 1]
+            self.hip.hipEventSynchronize(b)
+            self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+            us.append(ms.value * 1e3)
+        us.sort()
+        return sum(us) / len(us), us[len(us) // 2]
+
+
+def rotation_sets(bytes_per_set):
+    return max(2, -(-ROTATE_BYTES // bytes_per_set))
+
+
+# ---------------------------------------------------------------------- workloads
+
+
+def bf16_dev(torch, bits):
+    import numpy as np
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def build_decode(torch, fq, synth):
+    """Rotation sets for the decode step: activation, quantized weights per N, outputs,
+    KV batch, pools."""
+    import numpy as np
+
+    w_master = {}
+    for n in N_DECODE:
+        w = bf16_dev(torch, synth.decode_weight(n, K_DECODE, seed=2100 + n))
+        w_master[n] = fq.fp8_block_quant(w)
+        del w
+    per_set = sum(gemm_bytes(M_DECODE, n, K_DECODE) for n in N_DECODE)
+    nsets = rotation_sets(per_set)
+    rng = np.random.default_rng(2900)
+    sets = []
+    e = KV_H * KV_D
+    kc = torch.zeros(KV_NB * KV_BS * e, dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    for i in range(nsets):
+        s = {}
+        s["a"] = bf16_dev(torch, synth.decode_activation(M_DECODE, seed=2000 + i))
+        s["q"] = torch.empty((M_DECODE, K_DECODE), dtype=torch.uint8, device="cuda")
+        s["s"] = torch.empty((M_DECODE, K_DECODE // 128), dtype=torch.float32, device="cuda")
+        s["w"] = {n: (wq.clone(), ws.clone()) for n, (wq, ws) in w_master.items()}
+        s["out"] = {n: torch.empty((M_DECODE, n), dtype=torch.bfloat16, device="cuda")
+                    for n in N_DECODE}
+        s["k"] = bf16_dev(torch, synth.to_bf16_bits(rng.normal(0, 3, size=(M_DECODE, e))))
+        s["v"] = bf16_dev(torch, synth.to_bf16_bits(rng.normal(0, 3, size=(M_DECODE, e))))
+        s["slots"] = torch.from_numpy(
+            rng.permutation(KV_NB * KV_BS)[:M_DECODE].astype(np.int64)).cuda()
+        s["amax"] = torch.zeros(2, dtype=torch.float32, device="cuda")
+        sets.append(s)
+    return sets, kc, vc, w_master
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures a single GPU (got --gpus {args.gpus}): a sharded run executes "
+              "these same kernels on each GPU's share of the shapes; run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import fp8_e4m3_quantization_amd as fq
+    from fp8_e4m3_quantization_amd import synth
+
+    torch.cuda.set_device(0)
+    fq.load()
+    timer = Timer(torch, fq.load())
+    only = set(args.only.split(",")) if args.only else {"step", "quant", "gemm", "sweep", "kv"}
+    kernels = {}
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- decode step
+    log("building decode-step buffers")
+    sets, kc, vc, w_master = build_decode(torch, fq, synth)
+    cal = fq.KvCalibrator(1)  # frozen after its first observe (window of one token)
+    e = KV_H * KV_D
+    s0 = sets[0]
+    cal.observe(s0["k"], s0["v"], KV_H, KV_D, kc, vc, s0["slots"], KV_BS)
+    k_scale, v_scale = cal.scales()
+
+    def run_step(s):
+        fq.fp8_group_quant(s["a"], s["q"], s["s"])
+        fq.w8a8_block_gemm_grouped(s["q"], s["s"], [(s["w"][n][0], s["w"][n][1], s["out"][n])
+                                                    for n in N_DECODE])
+        cal.observe(s["k"], s["v"], KV_H, KV_D, kc, vc, s["slots"], KV_BS)  # frozen: no-op
+        fq.fp8_kv_amax(s["k"], s["v"], s["amax"])
+        fq.fp8_kv_write(s["k"], s["v"], kc, vc, s["slots"], KV_H, KV_D, KV_BS, k_scale, v_scale)
+
+    result = {}
+    if "step" in only:
+        log(f"capturing {len(sets)} step graphs")
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for s in sets:
+                run_step(s)  # eager warm-up of every launch on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for s in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_step(s)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        # timed region: exactly K steps, synchronized on both sides
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(args.steps):
+            graphs[i % len(graphs)].replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        step_ms = ev0.elapsed_time(ev1) / args.steps
+        sb = step_bytes()
+        result["step"] = dict(ms=step_ms, bytes=sb, gbs=sb / (step_ms * 1e-3) / 1e9)
+        log(f"step: {step_ms * 1e3:.2f} us, {result['step']['gbs']:.1f} GB/s")
+        del graphs
+
+    # ------------------------------------------------------------- GEMM per N
+    if "gemm" in only or "step" in only:
+        for n in N_DECODE:
+            launches = [(lambda s=s, n=n: fq.w8a8_block_gemm(s["q"], s["s"], s["w"][n][0],
+                                                             s["w"][n][1], s["out"][n]))
+                        for s in sets]
+            for s in sets:
+                fq.fp8_group_quant(s["a"], s["q"], s["s"])
+            mean_us, med_us = timer.kernel_us(launches, args.iters)
+            b = gemm_bytes(M_DECODE, n, K_DECODE)
+            fl = 2.0 * M_DECODE * n * K_DECODE
+            kernels[f"w8a8_gemm_m16_n{n}_k5120"] = dict(
+                us=round(mean_us, 3), us_median=round(med_us, 3),
+                gbs=round(b / (mean_us * 1e-6) / 1e9, 1),
+                frac_hbm=round(b / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                weight_gbs=round(gemm_weight_bytes(n, K_DECODE) / (mean_us * 1e-6) / 1e9, 1),
+                tflops=round(fl / (mean_us * 1e-6) / 1e12, 2), bytes=b)
+            log(f"gemm n={n}: {mean_us:.2f} us (median {med_us:.2f}) "
+                f"{kernels[f'w8a8_gemm_m16_n{n}_k5120']['gbs']} GB/s")
+
+        launches = [(lambda s=s: fq.w8a8_block_gemm_grouped(
+            s["q"], s["s"], [(s["w"][n][0], s["w"][n][1], s["out"][n]) for n in N_DECODE]))
+            for s in sets]
+        mean_us, med_us = timer.kernel_us(launches, args.iters)
+        b = grouped_gemm_bytes(M_DECODE, N_DECODE, K_DECODE)
+        kernels["w8a8_gemm_grouped_m16_k5120_4proj"] = dict(
+            us=round(mean_us, 3), us_median=round(med_us, 3),
+            gbs=round(b / (mean_us * 1e-6) / 1e9, 1),
+            frac_hbm=round(b / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), bytes=b,
+            tflops=round(2.0 * M_DECODE * sum(N_DECODE) * K_DECODE / (mean_us * 1e-6) / 1e12, 2))
+        log(f"grouped gemm (4 projections): {mean_us:.2f} us "
+            f"{kernels['w8a8_gemm_grouped_m16_k5120_4proj']['gbs']} GB/s")
+
+    # ----------------------------------------------------------- width sweep
+    if "sweep" in only:
+        n = 16384
+        sweep = {}
+        for m in synth.SWEEP_M:
+            acts = [bf16_dev(torch, synth.decode_activation(m, seed=4000 + m + 10 * i))
+                    for i in range(len(sets))]
+            qs = [torch.empty((m, K_DECODE), dtype=torch.uint8, device="cuda") for _ in sets]
+            ss = [torch.empty((m, K_DECODE // 128), dtype=torch.float32, device="cuda")
+                  for _ in sets]
+            outs = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for _ in sets]
+
+            lq = [(lambda i=i: fq.fp8_group_quant(acts[i], qs[i], ss[i])) for i in range(len(sets))]
+            lg = [(lambda i=i: fq.w8a8_block_gemm(qs[i], ss[i], sets[i]["w"][n][0],
+                                                  sets[i]["w"][n][1], outs[i]))
+                  for i in range(len(sets))]
+            for f in lq:
+                f()
+            tq, _ = timer.kernel_us(lq, args.iters)
+            tg, _ = timer.kernel_us(lg, args.iters)
+            wb = gemm_weight_bytes(n, K_DECODE)
+            t = tq + tg
+            sweep[str(m)] = dict(us_quant=round(tq, 3), us_gemm=round(tg, 3), us=round(t, 3),
+                                 weight_gbs=round(wb / (t * 1e-6) / 1e9, 1),
+                                 frac_hbm=round(wb / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                 gemm_gbs=round(gemm_bytes(m, n, K_DECODE) / (tg * 1e-6) / 1e9, 1))
+            log(f"sweep m={m}: quant {tq:.2f} us + gemm {tg:.2f} us, "
+                f"{sweep[str(m)]['weight_gbs']} GB/s of weights")
+        kernels["quant_gemm_pair_n16384_k5120"] = sweep
+
+    # ------------------------------------------------------------- prefill quant
+    if "quant" in only:
+        for k in synth.PREFILL_K:
+            m = synth.PREFILL_TOKENS
+            x_master = bf16_dev(torch, synth.prefill_activation(k, seed=3000 + k))
+            nset = rotation_sets(quant_bytes(m, k))
+            xs = [x_master.clone() for _ in range(nset)]
+            qs = [torch.empty((m, k), dtype=torch.uint8, device="cuda") for _ in range(nset)]
+            ss = [torch.empty((m, k // 128), dtype=torch.float32, device="cuda")
+                  for _ in range(nset)]
+            launches = [(lambda i=i: fq.fp8_group_quant(xs[i], qs[i], ss[i])) for i in range(nset)]
+            for f in launches:
+                f()
+            mean_us, med_us = timer.kernel_us(launches, args.iters)
+            b = quant_bytes(m, k)
+            kernels[f"group_quant_m{m}_k{k}"] = dict(
+                us=round(mean_us, 3), us_median=round(med_us, 3),
+                gbs=round(b / (mean_us * 1e-6) / 1e9, 1),
+                frac_hbm=round(b / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), bytes=b)
+            log(f"group quant k={k}: {mean_us:.2f} us {kernels[f'group_quant_m{m}_k{k}']['gbs']} GB/s")
+            del xs, qs, ss, x_master
+
+    # ---------------------------------------------------------------- KV pool
+    if "kv" in only:
+        full = synth.kv_full_pool()
+        t = len(full.slots)
+        per = kv_write_bytes(t) + KV_NB * KV_BS * e * 2
+        nset = rotation_sets(per)
+        kd = bf16_dev(torch, full.k)
+        vd = bf16_dev(torch, full.v)
+        sd = torch.from_numpy(full.slots).cuda()
+        bufs = [(kd.clone(), vd.clone(), sd.clone(), torch.zeros_like(kc), torch.zeros_like(vc),
+                 torch.zeros(2, dtype=torch.float32, device="cuda")) for _ in range(nset)]
+        ks_, vs_ = 3.0 * 20.0 / 448.0, 3.0 * 20.0 / 448.0
+        wl = [(lambda b=b: fq.fp8_kv_write(b[0], b[1], b[3], b[4], b[2], KV_H, KV_D, KV_BS,
+                                           ks_, vs_)) for b in bufs]
+        al = [(lambda b=b: fq.fp8_kv_amax(b[0], b[1], b[5])) for b in bufs]
+        for f in wl + al:
+            f()
+        for name, launches, b in (("kv_write_full_pool", wl, kv_write_bytes(t)),
+                                  ("kv_amax_full_pool", al, kv_amax_bytes(t))):
+            mean_us, med_us = timer.kernel_us(launches, args.iters)
+            kernels[f"{name}_t{t}"] = dict(
+                us=round(mean_us, 3), us_median=round(med_us, 3),
+                gbs=round(b / (mean_us * 1e-6) / 1e9, 1),
+                frac_hbm=round(b / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), bytes=b)
+            log(f"{name}: {mean_us:.2f} us {kernels[f'{name}_t{t}']['gbs']} GB/s")
+        del bufs
+
+    # ---------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline and "step" in only:
+        cpu = cpu_baseline(synth, log)
+
+    # --------------------------------------------------------------- report
+    dom_name = "w8a8_gemm_grouped_m16_k5120_4proj"
+    dom = kernels.get(dom_name)
+    roof = None
+    if dom:
+        roof = dict(bound="hbm", achieved=dom["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(dom["gbs"] / HBM_PEAK_GBS, 4),
+                    traffic=profiled_traffic(dom_name),
+                    kernel="w8a8_persistent_kernel<5> (4 decode projections, one launch)",
+                    bytes_per_launch=dom["bytes"], us_per_launch=dom["us"])
+    st = result.get("step")
+    line = {
+        "metric": "HBM GB/s (% of 8 TB/s) for W8A8 decode GEMM M=16 and group quant",
+        "value": round(st["gbs"], 1) if st else None,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(st["ms"], 5) if st else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 x fp8_e4m3 -> f32 (quantizer f32)",
+        "data": "synthetic (seeded; weights ~N(0,0.02) block-quantized on the GPU)",
+        "config": {
+            "workload": "decode step: group quant [16x5120] + W8A8 GEMM M=16 K=5120 "
+                        "N=16384,12288,5120,1024 + KV amax/write 16 tokens (4x128, bs 16)",
+            "M": M_DECODE, "K": K_DECODE, "N": list(N_DECODE), "kv_tokens": M_DECODE,
+            "kv_heads": KV_H, "head_dim": KV_D, "block_size": KV_BS,
+            "bytes_per_step": step_bytes(), "rotation_sets": len(sets),
+            "parallelism": "single GPU",
+        },
+        "frac_hbm": round(st["gbs"] / HBM_PEAK_GBS, 4) if st else None,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def profiled_traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source (else null)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(name)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_sha(rec.get("source", "")):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def source_sha(rel):
+    try:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+
+
+def cpu_baseline(synth, log):
+    """The CPU oracle, as it stands, on one full decode step (single thread)."""
+    import numpy as np
+
+    import oracle
+
+    log("cpu baseline: oracle on one full decode step")
+    a = synth.decode_activation(M_DECODE, seed=2000)
+    ws = {n: oracle.block_quant(synth.decode_weight(n, K_DECODE, seed=2100 + n))
+          for n in N_DECODE}
+    rng = np.random.default_rng(2900)
+    e = KV_H * KV_D
+    k = synth.to_bf16_bits(rng.normal(0, 3, size=(M_DECODE, e)))
+    v = synth.to_bf16_bits(rng.normal(0, 3, size=(M_DECODE, e)))
+    slots = rng.permutation(KV_NB * KV_BS)[:M_DECODE].astype(np.int64)
+    kc = np.zeros(KV_NB * KV_BS * e, dtype=np.uint8)
+    vc = np.zeros_like(kc)
+    t0 = time.perf_counter()
+    q, s = oracle.group_quant(a)
+    for n in N_DECODE:
+        oracle.gemm(q, s, *ws[n])
+    oracle.amax(k)
+    oracle.amax(v)
+    oracle.kv_write(k, v, kc, vc, slots, M_DECODE, KV_H, KV_D, KV_BS, 0.1, 0.1, e, e,
+                    KV_BS * e)
+    dt = time.perf_counter() - t0
+    gbs = step_bytes() / dt / 1e9
+    log(f"cpu baseline: {dt:.2f} s per step, {gbs:.4f} GB/s")
+    return dict(value=round(gbs, 5), unit="GB/s", cores=1, kind="oracle",
+                sample="one full decode step (same shapes as the GPU step), "
+                       f"{dt:.2f} s single-threaded C oracle, FP64 GEMM")
+
+
+if __name__ == "__main__":
+    main()

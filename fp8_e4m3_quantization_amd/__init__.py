@@ -20,4 +20,5 @@ from ._lib import (  # noqa: F401
     load,
     strerror,
     w8a8_block_gemm,
+    w8a8_block_gemm_grouped,
 )

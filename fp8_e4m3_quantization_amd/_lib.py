@@ -20,8 +20,8 @@ FP8Q_CALIB_STAGE, FP8Q_CALIB_DECLINE, FP8Q_CALIB_FREEZE, FP8Q_CALIB_FROZEN = 0, 
 
 # Every symbol include/fp8q.h declares.
 EXPORTS = (
-    "fp8q_strerror", "fp8q_version", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
-    "w8a8_block_gemm", "fp8_kv_write", "fp8_kv_amax", "fp8q_kv_calib_create",
+    "fp8q_strerror", "fp8q_version", "fp8q_time_next_launch", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
+    "w8a8_block_gemm", "w8a8_block_gemm_grouped", "fp8_kv_write", "fp8_kv_amax", "fp8q_kv_calib_create",
     "fp8q_kv_calib_observe", "fp8q_kv_calib_decide", "fp8q_kv_calib_scales",
     "fp8q_kv_calib_get_info", "fp8q_kv_calib_destroy",
 )
@@ -41,6 +41,11 @@ class KvTarget(ctypes.Structure):
         ("reserved", ctypes.c_int32), ("cache_stride", ctypes.c_int64),
         ("num_blocks", ctypes.c_int64),
     ]
+
+
+class GemmProj(ctypes.Structure):
+    _fields_ = [("w_q", ctypes.c_void_p), ("w_scale", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("n", ctypes.c_int32), ("ldc", ctypes.c_int32)]
 
 
 class KvCalibInfo(ctypes.Structure):
@@ -71,10 +76,13 @@ def load() -> ctypes.CDLL:
     sig = {
         "fp8q_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "fp8q_version": (ctypes.c_int, []),
+        "fp8q_time_next_launch": (ctypes.c_int, [P, P]),
         "fp8_group_quant": (ctypes.c_int, [P, P, P, I64, I32, P]),
         "fp8_block_quant": (ctypes.c_int, [P, P, P, I32, I32, P]),
         "fp8_e4m3_encode": (ctypes.c_int, [P, P, I64, P]),
         "w8a8_block_gemm": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, P]),
+        "w8a8_block_gemm_grouped": (ctypes.c_int, [P, P, ctypes.POINTER(GemmProj), I32, I32,
+                                                   I32, P]),
         "fp8_kv_write": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, I64, F32, F32,
                                         I32, I32, I64, P]),
         "fp8_kv_amax": (ctypes.c_int, [P, P, I64, P, P]),
@@ -199,6 +207,35 @@ def w8a8_block_gemm(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tensor,
                                 current_stream(a_q.device) if stream is None else stream)
     check("w8a8_block_gemm", st)
     return out
+
+
+def w8a8_block_gemm_grouped(a_q: torch.Tensor, a_scale: torch.Tensor, projections,
+                            stream: int | None = None):
+    """One launch over several projections of the same activation.  projections: list of
+    (w_q [n, k], w_scale [n/128, k/128], out [m, ldc] or None); returns the outputs."""
+    m, k = a_q.shape
+    arr = (GemmProj * len(projections))()
+    outs = []
+    for i, (w_q, w_scale, out) in enumerate(projections):
+        n = w_q.shape[0]
+        if w_q.shape[1] != k or w_scale.numel() != (n // 128) * (k // 128):
+            raise ValueError(f"projection {i} does not match the activation")
+        if out is None:
+            out = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+        ldc = out.shape[-1]
+        if out.numel() < (m - 1) * ldc + n:
+            raise ValueError(f"projection {i}: out is smaller than (m - 1) * ldc + n")
+        arr[i] = GemmProj(_dev(w_q, "w_q", _U8), _dev(w_scale, "w_scale", torch.float32),
+                          _dev(out, "out", _BF16), n, ldc)
+        outs.append(out)
+    if a_scale.numel() != m * (k // 128):
+        raise ValueError("a_scale does not match a_q")
+    st = load().w8a8_block_gemm_grouped(_dev(a_q, "a_q", _U8),
+                                        _dev(a_scale, "a_scale", torch.float32), arr,
+                                        len(projections), m, k,
+                                        current_stream(a_q.device) if stream is None else stream)
+    check("w8a8_block_gemm_grouped", st)
+    return outs
 
 
 def fp8_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,

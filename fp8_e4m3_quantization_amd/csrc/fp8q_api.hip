@@ -1,5 +1,6 @@
 // fp8q_api.hip -- status strings and version of the C ABI.
 #include "fp8q.h"
+#include "fp8q_launch.h"
 
 extern "C" const char* fp8q_strerror(int status) {
   switch (status) {
@@ -15,3 +16,9 @@ extern "C" const char* fp8q_strerror(int status) {
 }
 
 extern "C" int fp8q_version(void) { return 10000; }
+
+extern "C" int fp8q_time_next_launch(hipEvent_t start, hipEvent_t stop) {
+  fp8q::g_next_launch_events.start = start;
+  fp8q::g_next_launch_events.stop = stop;
+  return FP8Q_OK;
+}

@@ -128,30 +128,275 @@ __global__ __launch_bounds__(64 * kWaves) void w8a8_gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Persistent form: one 8-wave workgroup per CU walks output strips of 16 columns.
+// Wave w owns a fixed slice of K-groups: its activation fragments and scales for that
+// slice are loaded once and stay in registers for the whole kernel, so the only global
+// traffic in the strip loop is the weight stream.  Each wave prefetches the next strip's
+// weight slice while it multiplies the current one; the 8 K-slice partials of a strip
+// meet in LDS (double-buffered, one barrier per strip) and one pass writes bf16.
+// Several projections that read the same activation can share one launch: strips are
+// numbered across them.
+constexpr int kMaxProj = 8;
+constexpr int kPWaves = 8;
+
+struct ProjSet {
+  const uint8_t* w[kMaxProj];
+  const float* ws[kMaxProj];
+  uint16_t* out[kMaxProj];
+  int ldc[kMaxProj];
+  int strip_end[kMaxProj];  // cumulative strip count after projection p
+  int count;
+};
+
+// s_waitcnt lgkmcnt(0) + s_barrier: orders the LDS partials without waiting on the
+// weight prefetches that are still in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
+}
+
+// One strip's weight slice for this wave plus its block scales, issued together so that
+// waiting for them never waits for a later prefetch (vmcnt retires loads in order).
+// Every load is unconditional (the compiler then tracks the counts exactly): a wave
+// whose slice is shorter than kGpw re-reads its last group, and the matching
+// activation fragment is zero.
+template <int kGpw>
+struct Slice {
+  v8i b[kGpw];
+  float ws[kGpw];
+};
+
+template <int kGpw>
+__global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
+    const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale, ProjSet ps, int m,
+    int k, int total_strips) {
+  __shared__ float s_part[2][kPWaves * 4 * 64];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int groups = k >> 7;
+  const int g0 = (groups * wv) / kPWaves;
+  const int cnt = (groups * (wv + 1)) / kPWaves - g0;  // 0 <= cnt <= kGpw
+  const int row = lane & 15, koff = (lane >> 4) * 32;
+  int goff[kGpw];  // byte offset of slice group u (clamped into the slice)
+#pragma unroll
+  for (int u = 0; u < kGpw; ++u) goff[u] = (g0 + max(0, min(u, cnt - 1))) * 128;
+
+  // activation slice: fragments (rows >= m and groups past the slice are zero) and the
+  // 4 row scales per group this lane's accumulators need
+  v8i a[kGpw];
+  float4 as[kGpw];
+  {
+    const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    const uint8_t* ap = a_q + int64_t(row < m ? row : 0) * k + koff;
+    const int r0 = 4 * (lane >> 4);
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u) {
+      const bool live = u < cnt;
+      const v8i f = load32(ap + goff[u]);
+      a[u] = (live && row < m) ? f : zero8;
+      const int g = goff[u] >> 7;
+      as[u].x = (live && r0 + 0 < m) ? a_scale[int64_t(r0 + 0) * groups + g] : 0.0f;
+      as[u].y = (live && r0 + 1 < m) ? a_scale[int64_t(r0 + 1) * groups + g] : 0.0f;
+      as[u].z = (live && r0 + 2 < m) ? a_scale[int64_t(r0 + 2) * groups + g] : 0.0f;
+      as[u].w = (live && r0 + 3 < m) ? a_scale[int64_t(r0 + 3) * groups + g] : 0.0f;
+    }
+  }
+
+  // strip s -> (projection, first column); uniform across the workgroup
+  auto locate = [&](int s, int* p_out, int* n0) {
+    int p = 0;
+    while (p + 1 < ps.count && s >= ps.strip_end[p]) ++p;
+    *p_out = p;
+    *n0 = (s - (p ? ps.strip_end[p - 1] : 0)) * 16;
+  };
+  auto fetch = [&](int s, Slice<kGpw>& sl) {
+    int p, n0;
+    locate(s, &p, &n0);
+    const uint8_t* wp = ps.w[p] + int64_t(n0 + row) * k + koff;
+    const float* wsp = ps.ws[p] + int64_t(n0 >> 7) * groups;
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u) sl.b[u] = load32(wp + goff[u]);
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u) sl.ws[u] = wsp[goff[u] >> 7];
+  };
+  auto compute = [&](int s, const Slice<kGpw>& cur, float* part) {
+    int p, n0;
+    locate(s, &p, &n0);
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u) {
+      const v4f c = mfma_group(a[u], cur.b[u]);
+      const float w = cur.ws[u];
+      acc[0] = __builtin_fmaf(c[0], as[u].x * w, acc[0]);
+      acc[1] = __builtin_fmaf(c[1], as[u].y * w, acc[1]);
+      acc[2] = __builtin_fmaf(c[2], as[u].z * w, acc[2]);
+      acc[3] = __builtin_fmaf(c[3], as[u].w * w, acc[3]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) part[(wv * 4 + j) * 64 + lane] = acc[j];
+    lds_barrier();
+    if (threadIdx.x < 256) {
+      const int j = threadIdx.x >> 6, l = threadIdx.x & 63;
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kPWaves; ++w) sum += part[(w * 4 + j) * 64 + l];
+      const int r = 4 * (l >> 4) + j, c = l & 15;
+      if (r < m) ps.out[p][int64_t(r) * ps.ldc[p] + n0 + c] = f32_to_bf16_rne(sum);
+    }
+  };
+
+  // strips of this workgroup: blockIdx.x, +gridDim.x, ...; the last one has no prefetch
+  const int stride = int(gridDim.x);
+  const int nit = (total_strips - int(blockIdx.x) + stride - 1) / stride;
+  if (nit <= 0) return;
+  Slice<kGpw> b0, b1;
+  int s = blockIdx.x;
+  fetch(s, b0);
+  int i = 0;
+  for (; i + 2 < nit; i += 2) {
+    fetch(s + stride, b1);
+    compute(s, b0, s_part[0]);
+    s += stride;
+    fetch(s + stride, b0);
+    compute(s, b1, s_part[1]);
+    s += stride;
+  }
+  if (nit - i == 2) {
+    fetch(s + stride, b1);
+    compute(s, b0, s_part[0]);
+    compute(s + stride, b1, s_part[1]);
+  } else {
+    compute(s, b0, s_part[0]);
+  }
+}
+
 template <int kWaves, int kChunk>
 int launch_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
                 const float* w_scale, uint16_t* out, int m, int n, int k, int ldc,
                 hipStream_t stream) {
   const size_t lds = size_t(k / 128) * 16 * sizeof(float) + size_t(kWaves) * 256 * sizeof(float);
-  hipLaunchKernelGGL((w8a8_gemm_kernel<kWaves, kChunk>), dim3(n / 16), dim3(64 * kWaves),
+  launch((w8a8_gemm_kernel<kWaves, kChunk>), dim3(n / 16), dim3(64 * kWaves),
                      lds, stream, a_q, a_scale, w_q, w_scale, out, m, k, ldc);
   return launch_status();
 }
+
+int num_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+template <int kGpw>
+int launch_persistent(const uint8_t* a_q, const float* a_scale, const ProjSet& ps, int m,
+                      int k, int total, hipStream_t stream) {
+  const int grid = total < num_cus() ? total : num_cus();
+  launch((w8a8_persistent_kernel<kGpw>), dim3(grid), dim3(64 * kPWaves), 0,
+                     stream, a_q, a_scale, ps, m, k, total);
+  return launch_status();
+}
+
+// Persistent kernel for k <= 8 * 8 * 128 (each wave holds at most 8 groups).
+int run_persistent(const uint8_t* a_q, const float* a_scale, const ProjSet& ps, int m,
+                   int k, hipStream_t stream) {
+  const int total = ps.strip_end[ps.count - 1];
+  const int gpw = (k / 128 + kPWaves - 1) / kPWaves;
+  switch (gpw) {
+    case 1: return launch_persistent<1>(a_q, a_scale, ps, m, k, total, stream);
+    case 2: return launch_persistent<2>(a_q, a_scale, ps, m, k, total, stream);
+    case 3: return launch_persistent<3>(a_q, a_scale, ps, m, k, total, stream);
+    case 4: return launch_persistent<4>(a_q, a_scale, ps, m, k, total, stream);
+    case 5: return launch_persistent<5>(a_q, a_scale, ps, m, k, total, stream);
+    case 6: return launch_persistent<6>(a_q, a_scale, ps, m, k, total, stream);
+    case 7: return launch_persistent<7>(a_q, a_scale, ps, m, k, total, stream);
+    case 8: return launch_persistent<8>(a_q, a_scale, ps, m, k, total, stream);
+    default: return FP8Q_EINVAL;
+  }
+}
+
+constexpr int kPersistentMaxK = kPWaves * 8 * 128;
 
 }  // namespace
 }  // namespace fp8q
 
 using namespace fp8q;
 
+namespace {
+int check_gemm_common(const uint8_t* a_q, const float* a_scale, int32_t m, int32_t k) {
+  if (m < 1 || m > 16 || k <= 0 || k % 128 != 0 || k > kMaxGemmK) return FP8Q_EINVAL;
+  if (!a_q || !a_scale) return FP8Q_ENULL;
+  if (!aligned(a_q, 16) || !aligned(a_scale, 4)) return FP8Q_EALIGN;
+  return FP8Q_OK;
+}
+
+int check_proj(const uint8_t* w_q, const float* w_scale, const uint16_t* out, int32_t n,
+               int32_t ldc) {
+  if (n <= 0 || n % 128 != 0 || ldc < n) return FP8Q_EINVAL;
+  if (!w_q || !w_scale || !out) return FP8Q_ENULL;
+  if (!aligned(w_q, 16) || !aligned(w_scale, 4) || !aligned(out, 2)) return FP8Q_EALIGN;
+  return FP8Q_OK;
+}
+}  // namespace
+
 extern "C" int w8a8_block_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
                                const float* w_scale, uint16_t* out, int32_t m, int32_t n,
                                int32_t k, int32_t ldc, hipStream_t stream) {
-  if (m < 1 || m > 16 || n <= 0 || n % 128 != 0 || k <= 0 || k % 128 != 0 || ldc < n ||
-      k > kMaxGemmK)
-    return FP8Q_EINVAL;
-  if (!a_q || !a_scale || !w_q || !w_scale || !out) return FP8Q_ENULL;
-  if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(a_scale, 4) ||
-      !aligned(w_scale, 4) || !aligned(out, 2))
-    return FP8Q_EALIGN;
+  int rc = check_gemm_common(a_q, a_scale, m, k);
+  if (rc == FP8Q_OK && (n <= 0 || n % 128 != 0 || ldc < n)) rc = FP8Q_EINVAL;
+  if (rc == FP8Q_OK) rc = check_proj(w_q, w_scale, out, n, ldc);
+  if (rc != FP8Q_OK) return rc;
+  if (k <= kPersistentMaxK) {
+    ProjSet ps = {};
+    ps.w[0] = w_q;
+    ps.ws[0] = w_scale;
+    ps.out[0] = out;
+    ps.ldc[0] = ldc;
+    ps.strip_end[0] = n / 16;
+    ps.count = 1;
+    return run_persistent(a_q, a_scale, ps, m, k, stream);
+  }
   return launch_gemm<4, 5>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, stream);
+}
+
+extern "C" int w8a8_block_gemm_grouped(const uint8_t* a_q, const float* a_scale,
+                                       const fp8q_gemm_proj* projs, int32_t count, int32_t m,
+                                       int32_t k, hipStream_t stream) {
+  if (count < 1 || count > kMaxProj) return FP8Q_EINVAL;
+  if (!projs) return FP8Q_ENULL;
+  int rc = check_gemm_common(a_q, a_scale, m, k);
+  if (rc != FP8Q_OK) return rc;
+  int64_t strips = 0;
+  for (int p = 0; p < count; ++p) {
+    rc = check_proj(projs[p].w_q, projs[p].w_scale, projs[p].out, projs[p].n, projs[p].ldc);
+    if (rc != FP8Q_OK) return rc;
+    strips += projs[p].n / 16;
+  }
+  if (strips > 0x7FFFFFFF) return FP8Q_EINVAL;
+  if (k > kPersistentMaxK) {
+    for (int p = 0; p < count; ++p) {
+      rc = launch_gemm<4, 5>(a_q, a_scale, projs[p].w_q, projs[p].w_scale, projs[p].out, m,
+                             projs[p].n, k, projs[p].ldc, stream);
+      if (rc != FP8Q_OK) return rc;
+    }
+    return FP8Q_OK;
+  }
+  ProjSet ps = {};
+  int end = 0;
+  for (int p = 0; p < count; ++p) {
+    ps.w[p] = projs[p].w_q;
+    ps.ws[p] = projs[p].w_scale;
+    ps.out[p] = projs[p].out;
+    ps.ldc[p] = projs[p].ldc;
+    end += projs[p].n / 16;
+    ps.strip_end[p] = end;
+  }
+  ps.count = count;
+  return run_persistent(a_q, a_scale, ps, m, k, stream);
 }

@@ -54,24 +54,43 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
 }
 
 // ept = elements per token / 8; ks8, vs8 = source row strides / 8; cs8 = pool stride / 8.
+// A wave takes kTokPerWave consecutive tokens: their slots are read first (scalar loads),
+// then every 16-byte load of the group is issued before any conversion, so each wave
+// keeps 2 * kTokPerWave loads in flight instead of waiting on one token at a time.
+constexpr int kTokPerWave = 4;
+
 __global__ __launch_bounds__(kKvBlock) void kv_write_vec_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v, uint2* __restrict__ kc,
     uint2* __restrict__ vc, const int64_t* __restrict__ slots, int64_t num_tokens, int ept,
     int64_t ks8, int64_t vs8, int64_t cs8, int bs, int64_t nslots, float k_scale,
     float k_inv, float v_scale, float v_inv) {
-  for (int64_t t = int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.y; t < num_tokens;
-       t += int64_t(gridDim.x) * kRowsPerBlock) {
-    int64_t blk, off;
-    if (!slot_to_block(uniform(slots[t]), nslots, bs, &blk, &off)) continue;
-    const uint4* kr = k + t * ks8;
-    const uint4* vr = v + t * vs8;
-    uint2* kd = kc + blk * cs8 + off * ept;
-    uint2* vd = vc + blk * cs8 + off * ept;
+  const int64_t step = int64_t(gridDim.x) * kRowsPerBlock * kTokPerWave;
+  for (int64_t t0 = (int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.y) * kTokPerWave;
+       t0 < num_tokens; t0 += step) {
+    int64_t tok[kTokPerWave], dst[kTokPerWave];
+    bool ok[kTokPerWave];
+#pragma unroll
+    for (int i = 0; i < kTokPerWave; ++i) {
+      const int64_t t = t0 + i;
+      tok[i] = t < num_tokens ? t : num_tokens - 1;  // clamped: loads stay in bounds
+      int64_t blk = 0, off = 0;
+      ok[i] = t < num_tokens && slot_to_block(uniform(slots[tok[i]]), nslots, bs, &blk, &off);
+      dst[i] = blk * cs8 + off * ept;
+    }
     for (int c = threadIdx.x; c < ept; c += 64) {
-      const uint4 kx = kr[c];
-      const uint4 vx = vr[c];
-      kd[c] = quant8<true>(kx, k_scale, k_inv);
-      vd[c] = quant8<true>(vx, v_scale, v_inv);
+      uint4 kx[kTokPerWave], vx[kTokPerWave];
+#pragma unroll
+      for (int i = 0; i < kTokPerWave; ++i) {
+        kx[i] = k[tok[i] * ks8 + c];
+        vx[i] = v[tok[i] * vs8 + c];
+      }
+#pragma unroll
+      for (int i = 0; i < kTokPerWave; ++i) {
+        if (ok[i]) {
+          kc[dst[i] + c] = quant8<true>(kx[i], k_scale, k_inv);
+          vc[dst[i] + c] = quant8<true>(vx[i], v_scale, v_inv);
+        }
+      }
     }
   }
 }
@@ -98,7 +117,26 @@ __global__ __launch_bounds__(kKvBlock) void kv_write_scalar_kernel(
   }
 }
 
-// max |x| over a packed run of n8 16-byte words; blockIdx.y picks K (0) or V (1).
+// Folds a workgroup's maximum into amax2[which]: one LDS reduction, then a single atomic,
+// skipped when the value already there is at least as large (it only grows).
+__device__ __forceinline__ void fold_block_max(float m, float* amax2, int which) {
+  __shared__ float red[kKvBlock / 64];
+  const int tid = threadIdx.x + threadIdx.y * blockDim.x;
+  m = max_over_wave(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) {
+    float b = red[0];
+    for (int w = 1; w < kKvBlock / 64; ++w) b = fmaxf(b, red[w]);
+    unsigned int* dst = reinterpret_cast<unsigned int*>(amax2 + which);
+    if (b > 0.0f && __float_as_uint(b) > __hip_atomic_load(dst, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(dst, __float_as_uint(b));
+  }
+}
+
+// max |x| over a packed run of n8 16-byte words; blockIdx.y picks K (0) or V (1).  Four
+// independent 16-byte loads per thread per step keep enough bytes in flight.
 __global__ __launch_bounds__(kKvBlock) void amax_flat_kernel(const uint4* __restrict__ k,
                                                              const uint4* __restrict__ v,
                                                              int64_t n8,
@@ -106,11 +144,13 @@ __global__ __launch_bounds__(kKvBlock) void amax_flat_kernel(const uint4* __rest
   const uint4* x = blockIdx.y ? v : k;
   const int64_t stride = int64_t(gridDim.x) * kKvBlock;
   float m = 0.0f;
-  for (int64_t i = int64_t(blockIdx.x) * kKvBlock + threadIdx.x; i < n8; i += stride)
-    m = fmaxf(m, absmax8(x[i]));
-  m = max_over_wave(m);
-  if ((threadIdx.x & 63) == 0 && m > 0.0f)
-    atomicMax(reinterpret_cast<unsigned int*>(amax2 + blockIdx.y), __float_as_uint(m));
+  int64_t i = int64_t(blockIdx.x) * kKvBlock + threadIdx.x;
+  for (; i + 3 * stride < n8; i += 4 * stride) {
+    const uint4 a = x[i], b = x[i + stride], c = x[i + 2 * stride], d = x[i + 3 * stride];
+    m = fmaxf(m, fmaxf(fmaxf(absmax8(a), absmax8(b)), fmaxf(absmax8(c), absmax8(d))));
+  }
+  for (; i < n8; i += stride) m = fmaxf(m, absmax8(x[i]));
+  fold_block_max(m, amax2, blockIdx.y);
 }
 
 // max |x| over `rows` rows of `row_elems` bf16 at row strides ks / vs (any alignment).
@@ -126,9 +166,7 @@ __global__ __launch_bounds__(kKvBlock) void amax_rows_kernel(const uint16_t* __r
        r += int64_t(gridDim.x) * kRowsPerBlock)
     for (int c = threadIdx.x; c < row_elems; c += 64)
       m = fmaxf(m, fabsf(bf16_to_f32(x[r * s + c])));
-  m = max_over_wave(m);
-  if (threadIdx.x == 0 && m > 0.0f)
-    atomicMax(reinterpret_cast<unsigned int*>(amax2 + blockIdx.y), __float_as_uint(m));
+  fold_block_max(m, amax2, blockIdx.y);
 }
 
 }  // namespace
@@ -139,17 +177,17 @@ int kv_amax_rows(const uint16_t* k, const uint16_t* v, int64_t rows, int64_t row
   const int64_t n = rows * row_elems;
   if (key_stride == row_elems && value_stride == row_elems && n % 8 == 0 && aligned(k, 16) &&
       aligned(v, 16)) {
-    // a few hundred thousand threads saturate the read; more would only add atomics
-    int64_t blocks = (n / 8 + kKvBlock - 1) / kKvBlock;
-    if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(amax_flat_kernel, dim3(unsigned(blocks), 2), dim3(kKvBlock), 0, stream,
+    // four 16-byte words per thread per step; enough blocks to fill every CU
+    int64_t blocks = (n / 8 + 4 * kKvBlock - 1) / (4 * kKvBlock);
+    if (blocks > 4096) blocks = 4096;
+    launch(amax_flat_kernel, dim3(unsigned(blocks), 2), dim3(kKvBlock), 0, stream,
                        reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
                        n / 8, amax2);
   } else {
     if (row_elems > 0x7FFFFFFF) return FP8Q_EINVAL;
     int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
     if (blocks > 1024) blocks = 1024;
-    hipLaunchKernelGGL(amax_rows_kernel, dim3(unsigned(blocks), 2), dim3(64, kRowsPerBlock), 0,
+    launch(amax_rows_kernel, dim3(unsigned(blocks), 2), dim3(64, kRowsPerBlock), 0,
                        stream, k, v, rows, int(row_elems), key_stride, value_stride, amax2);
   }
   return launch_status();
@@ -167,16 +205,17 @@ int kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t* v_
   const bool vec = e % 8 == 0 && key_stride % 8 == 0 && value_stride % 8 == 0 &&
                    cache_stride % 8 == 0 && aligned(k, 16) && aligned(v, 16) &&
                    aligned(k_cache, 8) && aligned(v_cache, 8);
-  const int64_t blocks = clamp_grid((int64_t(num_tokens) + kRowsPerBlock - 1) / kRowsPerBlock);
+  const int64_t rows_per_block = vec ? kRowsPerBlock * kTokPerWave : kRowsPerBlock;
+  const int64_t blocks = clamp_grid((int64_t(num_tokens) + rows_per_block - 1) / rows_per_block);
   if (vec)
-    hipLaunchKernelGGL(kv_write_vec_kernel, dim3(unsigned(blocks)), dim3(64, kRowsPerBlock), 0,
+    launch(kv_write_vec_kernel, dim3(unsigned(blocks)), dim3(64, kRowsPerBlock), 0,
                        stream, reinterpret_cast<const uint4*>(k),
                        reinterpret_cast<const uint4*>(v), reinterpret_cast<uint2*>(k_cache),
                        reinterpret_cast<uint2*>(v_cache), slot_mapping, int64_t(num_tokens),
                        int(e / 8), key_stride / 8, value_stride / 8, cache_stride / 8,
                        block_size, nslots, k_scale, k_inv, v_scale, v_inv);
   else
-    hipLaunchKernelGGL(kv_write_scalar_kernel, dim3(unsigned(blocks)), dim3(64, kRowsPerBlock),
+    launch(kv_write_scalar_kernel, dim3(unsigned(blocks)), dim3(64, kRowsPerBlock),
                        0, stream, k, v, k_cache, v_cache, slot_mapping, int64_t(num_tokens),
                        int(e), key_stride, value_stride, cache_stride, block_size, nslots,
                        k_scale, k_inv, v_scale, v_inv);

@@ -1,5 +1,6 @@
 // fp8q_launch.h -- host-side helpers shared by the C-ABI entry points.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -15,6 +16,27 @@ inline bool aligned(const void* p, uintptr_t a) {
 inline int64_t clamp_grid(int64_t blocks) {
   const int64_t cap = int64_t(1) << 20;
   return blocks < 1 ? 1 : (blocks > cap ? cap : blocks);
+}
+
+// Events the next kernel launched by this host thread records when it starts and when
+// it ends (set through fp8q_time_next_launch; consumed by that launch).
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+inline thread_local LaunchEvents g_next_launch_events;
+
+// Every kernel of the library is enqueued through here.
+template <typename Kernel, typename... Args>
+inline void launch(Kernel kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                   Args... args) {
+  const LaunchEvents ev = g_next_launch_events;
+  if (ev.start || ev.stop) {
+    g_next_launch_events = LaunchEvents();
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ev.start, ev.stop, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+  }
 }
 
 // Status of the launch just enqueued on this thread.

@@ -111,7 +111,7 @@ extern "C" int fp8_group_quant(const uint16_t* x, uint8_t* q, float* scales, int
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4)) return FP8Q_EALIGN;
   const int64_t groups = m * (k / 128);
   const int64_t blocks = clamp_grid((groups + kGroupsPerBlock - 1) / kGroupsPerBlock);
-  hipLaunchKernelGGL(group_quant_kernel, dim3(unsigned(blocks)), dim3(kQuantBlock), 0,
+  launch(group_quant_kernel, dim3(unsigned(blocks)), dim3(kQuantBlock), 0,
                      stream, reinterpret_cast<const uint4*>(x), reinterpret_cast<uint4*>(q),
                      scales, groups);
   return launch_status();
@@ -124,7 +124,7 @@ extern "C" int fp8_block_quant(const uint16_t* w, uint8_t* wq, float* ws, int32_
   if (!aligned(ws, 4)) return FP8Q_EALIGN;
   const int nblocks = (n + 127) / 128, kblocks = (k + 127) / 128;
   if (nblocks > 65535) return FP8Q_EINVAL;
-  hipLaunchKernelGGL(block_quant_kernel, dim3(kblocks, nblocks), dim3(256), 0, stream, w,
+  launch(block_quant_kernel, dim3(kblocks, nblocks), dim3(256), 0, stream, w,
                      wq, ws, n, k, kblocks);
   return launch_status();
 }
@@ -135,6 +135,6 @@ extern "C" int fp8_e4m3_encode(const float* x, uint8_t* q, int64_t n, hipStream_
   if (!x || !q) return FP8Q_ENULL;
   if (!aligned(x, 4)) return FP8Q_EALIGN;
   const int64_t blocks = clamp_grid((n + 255) / 256);
-  hipLaunchKernelGGL(encode_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, x, q, n);
+  launch(encode_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, x, q, n);
   return launch_status();
 }

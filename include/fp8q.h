@@ -47,6 +47,12 @@ extern "C" {
 const char* fp8q_strerror(int status);
 /* Library version, major*10000 + minor*100 + patch. */
 int fp8q_version(void);
+/* Measurement hook: the next kernel this host thread enqueues through the library records
+ * `start` as it begins executing and `stop` as it completes (hipExtLaunchKernelGGL), so
+ * the events' elapsed time is that kernel's own duration.  Either may be NULL.  Every
+ * entry point below enqueues exactly one kernel per call, except calls that enqueue
+ * nothing (zero sizes, errors) and the calibrator.  Always returns FP8Q_OK. */
+int fp8q_time_next_launch(hipEvent_t start, hipEvent_t stop);
 
 /* ------------------------------------------------ per-token 1x128 group quant
  * [actq] module doc: one FP32 scale per 128-wide K-group of one token row;
@@ -110,6 +116,26 @@ int fp8_e4m3_encode(const float* x, uint8_t* q, int64_t n, hipStream_t stream);
 int w8a8_block_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
                     const float* w_scale, uint16_t* out, int32_t m, int32_t n, int32_t k,
                     int32_t ldc, hipStream_t stream);
+
+/* ---------------------------------------------- grouped W8A8 decode GEMM
+ * [decode] decode_w8a8_quant_act: several projections that read the same activation
+ * (attention Q/K/V, a layer's projections) share one quantization; DecodeW8a8Plan::strided:
+ * outputs may be written at their own row pitch.  One launch computes, for each
+ * projection p < count, exactly what w8a8_block_gemm(a_q, a_scale, projs[p].w_q,
+ * projs[p].w_scale, projs[p].out, m, projs[p].n, k, projs[p].ldc) computes (same
+ * arithmetic, same bits).  `projs` is host memory read during the call; 1 <= count <= 8;
+ * every projection obeys w8a8_block_gemm's rules.  Errors as w8a8_block_gemm. */
+typedef struct fp8q_gemm_proj {
+  const uint8_t* w_q;    /* device, uint8 [n, k] */
+  const float* w_scale;  /* device, fp32 [n/128, k/128] */
+  uint16_t* out;         /* device, bf16 [m, ldc] */
+  int32_t n;
+  int32_t ldc;
+} fp8q_gemm_proj;
+
+int w8a8_block_gemm_grouped(const uint8_t* a_q, const float* a_scale,
+                            const fp8q_gemm_proj* projs, int32_t count, int32_t m, int32_t k,
+                            hipStream_t stream);
 
 /* --------------------------------------------------------- paged FP8 KV write
  * [staging] Fp8KvWriteTarget and replay_and_release (the write's arguments: strides in

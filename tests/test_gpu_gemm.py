@@ -190,3 +190,58 @@ def test_invalid_shapes_rejected_before_launch(args, code):
     d = torch.zeros(1 << 16, dtype=torch.uint8, device=DEV)
     p = d.data_ptr()
     assert lib.w8a8_block_gemm(p, p, p, p, p, m, n, k, ldc, 0) == code
+
+
+def test_grouped_matches_single_calls_bit_for_bit():
+    """The four decode projections in one launch give exactly the bytes of four calls."""
+    a = synth.decode_activation(16, seed=2000)
+    q, s = fq.fp8_group_quant(bf16_dev(a))
+    projs, singles = [], []
+    for n in synth.DECODE_N:
+        wq, ws = _weights(n, synth.DECODE_K, 2100 + n)
+        wq_d, ws_d = u8_dev(wq), f32_dev(ws)
+        projs.append((wq_d, ws_d, None))
+        singles.append((host(fq.w8a8_block_gemm(q, s, wq_d, ws_d)), wq, ws))
+    outs = fq.w8a8_block_gemm_grouped(q, s, projs)
+    q_ref, s_ref = oracle.group_quant(a)
+    for out, (single, wq, ws) in zip(outs, singles):
+        got = host(out)
+        assert np.array_equal(got, single)
+        ok, worst = gemm_tolerance_ok(got, oracle.gemm(q_ref, s_ref, wq, ws))
+        assert ok, worst
+
+
+def test_grouped_strided_outputs_into_one_buffer():
+    """Q/K/V-style: three projections written side by side into one [m, ldc] buffer."""
+    m, k = 9, 1024
+    a = synth.decode_activation(m, k=k, seed=71)
+    q, s = fq.fp8_group_quant(bf16_dev(a))
+    ns = [512, 128, 256]
+    ldc = sum(ns) + 64
+    buf = torch.full((m, ldc), 3.0, dtype=torch.bfloat16, device=DEV)
+    projs, refs, col = [], [], 0
+    q_ref, s_ref = oracle.group_quant(a)
+    for i, n in enumerate(ns):
+        wq, ws = _weights(n, k, 300 + i)
+        projs.append((u8_dev(wq), f32_dev(ws), buf[:, col:col + n]))
+        refs.append((col, n, oracle.gemm(q_ref, s_ref, wq, ws)))
+        col += n
+    # strided column views: pass the row pitch explicitly through the C ABI
+    lib = fq.load()
+    from fp8_e4m3_quantization_amd import _lib
+    arr = (_lib.GemmProj * 3)()
+    for i, (wq, ws, view) in enumerate(projs):
+        arr[i] = _lib.GemmProj(wq.data_ptr(), ws.data_ptr(), view.data_ptr(), ns[i], ldc)
+    assert lib.w8a8_block_gemm_grouped(q.data_ptr(), s.data_ptr(), arr, 3, m, k, 0) == 0
+    got = host(buf)
+    for col, n, ref in refs:
+        ok, worst = gemm_tolerance_ok(got[:, col:col + n], ref)
+        assert ok, worst
+    assert np.all(bf16_host_to_f64(got[:, sum(ns):]) == 3.0)
+
+
+@pytest.mark.parametrize("k", [8192, 8320, 16384])
+def test_long_k_both_kernel_forms(k):
+    """k <= 8192 runs the persistent form; longer k the K-split form."""
+    wq, ws = _weights(384, k, 5)
+    _check(synth.decode_activation(7, k=k, seed=k), wq, ws)
