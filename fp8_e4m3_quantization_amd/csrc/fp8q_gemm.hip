@@ -156,29 +156,57 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// One strip's weight slice for this wave plus its block scales, issued together so that
-// waiting for them never waits for a later prefetch (vmcnt retires loads in order).
-// Every load is unconditional (the compiler then tracks the counts exactly): a wave
-// whose slice is shorter than kGpw re-reads its last group, and the matching
-// activation fragment is zero.
+// Weight loads go through a buffer descriptor per strip (base = the strip's first row,
+// 16*k bytes).  A strip past the end gets a zero-size descriptor: its loads return zeros
+// without touching memory, so every prefetch is issued unconditionally and the compiler
+// tracks the in-order load counter exactly (no branch around any load).
+#ifndef FP8Q_GEMM_AUX
+#define FP8Q_GEMM_AUX 0  // cache-policy bits of the weight loads
+#endif
+constexpr uint32_t kBufferDword3 = 0x00020000;  // raw 32-bit buffer format (gfx9 family)
+
+// Weight block scales are read-only for the whole launch and uniform per wave: reading
+// them through the constant address space makes them scalar loads (counted apart from
+// the vector weight loads, so waiting for a scale never drains the weight prefetch).
+typedef const __attribute__((address_space(4))) float const_float;
+
 template <int kGpw>
 struct Slice {
   v8i b[kGpw];
   float ws[kGpw];
 };
 
-template <int kGpw>
+template <int kAux>
+__device__ __forceinline__ v8i buffer_load32(__amdgpu_buffer_rsrc_t r, int off) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAux);
+  const v4u y = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kAux);
+  v8i o;
+  o[0] = int(x[0]); o[1] = int(x[1]); o[2] = int(x[2]); o[3] = int(x[3]);
+  o[4] = int(y[0]); o[5] = int(y[1]); o[6] = int(y[2]); o[7] = int(y[3]);
+  return o;
+}
+
+// Strips are processed in rounds of kRound: a wave multiplies its K-slice of kRound strips
+// back to back (its partial tiles stay in registers), then all waves meet once -- partials
+// to LDS, one barrier, a fixed-order sum over the waves, bf16 stores.  Per-strip barriers
+// would tie every strip to the slowest wave's load latency.  The LDS partial area is
+// double-buffered across rounds, so one barrier per round suffices.
+template <int kGpw, int kDepth, int kAux, int kRound>
 __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
     const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale, ProjSet ps, int m,
     int k, int total_strips) {
-  __shared__ float s_part[2][kPWaves * 4 * 64];
+  static_assert(kRound % (kDepth + 1) == 0, "buffer index must be static within a round");
+  static_assert(kRound * 256 == kPWaves * 64 * 2, "reduce: two outputs per lane");
+  __shared__ float s_part[2][kRound * kPWaves * 4 * 64];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int groups = k >> 7;
   const int g0 = (groups * wv) / kPWaves;
   const int cnt = (groups * (wv + 1)) / kPWaves - g0;  // 0 <= cnt <= kGpw
   const int row = lane & 15, koff = (lane >> 4) * 32;
-  int goff[kGpw];  // byte offset of slice group u (clamped into the slice)
+  int goff[kGpw];  // byte offset of slice group u (a short slice re-reads its last group,
+                   // whose activation fragment below is zero)
 #pragma unroll
   for (int u = 0; u < kGpw; ++u) goff[u] = (g0 + max(0, min(u, cnt - 1))) * 128;
 
@@ -211,18 +239,18 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
     *n0 = (s - (p ? ps.strip_end[p - 1] : 0)) * 16;
   };
   auto fetch = [&](int s, Slice<kGpw>& sl) {
+    const bool valid = s < total_strips;
     int p, n0;
-    locate(s, &p, &n0);
-    const uint8_t* wp = ps.w[p] + int64_t(n0 + row) * k + koff;
-    const float* wsp = ps.ws[p] + int64_t(n0 >> 7) * groups;
+    locate(valid ? s : total_strips - 1, &p, &n0);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(ps.w[p] + int64_t(n0) * k), 0, valid ? 16 * k : 0, kBufferDword3);
+    const_float* wsp = (const_float*)(ps.ws[p] + int64_t(n0 >> 7) * groups);
 #pragma unroll
-    for (int u = 0; u < kGpw; ++u) sl.b[u] = load32(wp + goff[u]);
+    for (int u = 0; u < kGpw; ++u) sl.b[u] = buffer_load32<kAux>(r, row * k + koff + goff[u]);
 #pragma unroll
     for (int u = 0; u < kGpw; ++u) sl.ws[u] = wsp[goff[u] >> 7];
   };
-  auto compute = [&](int s, const Slice<kGpw>& cur, float* part) {
-    int p, n0;
-    locate(s, &p, &n0);
+  auto multiply = [&](const Slice<kGpw>& cur) {
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int u = 0; u < kGpw; ++u) {
@@ -233,41 +261,54 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
       acc[2] = __builtin_fmaf(c[2], as[u].z * w, acc[2]);
       acc[3] = __builtin_fmaf(c[3], as[u].w * w, acc[3]);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) part[(wv * 4 + j) * 64 + lane] = acc[j];
-    lds_barrier();
-    if (threadIdx.x < 256) {
-      const int j = threadIdx.x >> 6, l = threadIdx.x & 63;
-      float sum = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kPWaves; ++w) sum += part[(w * 4 + j) * 64 + l];
-      const int r = 4 * (l >> 4) + j, c = l & 15;
-      if (r < m) ps.out[p][int64_t(r) * ps.ldc[p] + n0 + c] = f32_to_bf16_rne(sum);
-    }
+    return acc;
   };
 
-  // strips of this workgroup: blockIdx.x, +gridDim.x, ...; the last one has no prefetch
+  // this workgroup's strips: blockIdx.x + i * gridDim.x for i < nit; kDepth ahead in flight
   const int stride = int(gridDim.x);
-  const int nit = (total_strips - int(blockIdx.x) + stride - 1) / stride;
+  const int first = int(blockIdx.x);
+  const int nit = (total_strips - first + stride - 1) / stride;
   if (nit <= 0) return;
-  Slice<kGpw> b0, b1;
-  int s = blockIdx.x;
-  fetch(s, b0);
-  int i = 0;
-  for (; i + 2 < nit; i += 2) {
-    fetch(s + stride, b1);
-    compute(s, b0, s_part[0]);
-    s += stride;
-    fetch(s + stride, b0);
-    compute(s, b1, s_part[1]);
-    s += stride;
-  }
-  if (nit - i == 2) {
-    fetch(s + stride, b1);
-    compute(s, b0, s_part[0]);
-    compute(s + stride, b1, s_part[1]);
-  } else {
-    compute(s, b0, s_part[0]);
+  Slice<kGpw> buf[kDepth + 1];
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j) fetch(first + j * stride, buf[j]);
+  int par = 0;
+  for (int i = 0; i < nit; i += kRound) {
+    float* part = s_part[par];  // [round strip][wave][4][64]
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) {
+      fetch(first + (i + j + kDepth) * stride, buf[(j + kDepth) % (kDepth + 1)]);
+      if (i + j < nit) {
+        const v4f acc = multiply(buf[j % (kDepth + 1)]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) part[((j * kPWaves + wv) * 4 + q) * 64 + lane] = acc[q];
+      }
+    }
+    lds_barrier();
+    // Reduce: wave w owns half of round strip w/2 (128 of its 256 outputs, 2 per lane).
+    // All LDS reads come before the two stores: a store retires through the same in-order
+    // counter as the prefetch loads, so nothing after a store may wait on that counter.
+    {
+      const int j = wv >> 1;                  // wave-uniform
+      const int q0 = (wv & 1) * 2;
+      float sum[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int w = 0; w < kPWaves; ++w) sum[x] += part[((j * kPWaves + w) * 4 + q0 + x) * 64 + lane];
+      if (i + j < nit) {
+        int p, n0;
+        locate(first + (i + j) * stride, &p, &n0);
+        uint16_t* o = ps.out[p] + n0 + (lane & 15);
+        const int ldc = ps.ldc[p];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int r = 4 * (lane >> 4) + q0 + x;
+          if (r < m) o[int64_t(r) * ldc] = f32_to_bf16_rne(sum[x]);
+        }
+      }
+    }
+    par ^= 1;
   }
 }
 
@@ -298,7 +339,11 @@ template <int kGpw>
 int launch_persistent(const uint8_t* a_q, const float* a_scale, const ProjSet& ps, int m,
                       int k, int total, hipStream_t stream) {
   const int grid = total < num_cus() ? total : num_cus();
-  launch((w8a8_persistent_kernel<kGpw>), dim3(grid), dim3(64 * kPWaves), 0,
+  // deeper prefetch only while the buffers still fit in registers without spilling
+  constexpr int kDepth = 1;
+  constexpr int kRound = 4;
+  launch((w8a8_persistent_kernel<kGpw, kDepth, FP8Q_GEMM_AUX, kRound>), dim3(grid),
+         dim3(64 * kPWaves), 0,
                      stream, a_q, a_scale, ps, m, k, total);
   return launch_status();
 }
