@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
 FP8_MFMA_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, published
 ROTATE_BYTES = 1 << 30     # >= 4x the 256 MB MALL
+COPY_CALIB_BYTES = 256 << 20
 
 
 def parse():
@@ -40,7 +41,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--iters", type=int, default=100, help="launches per kernel measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--only", default="", help="comma list: step,quant,gemm,sweep,kv")
+    p.add_argument("--only", default="",
+                   help="comma list of sections: step,gemm,grouped,sweep,quant,kv (default all)")
     return p.parse_args()
 
 
@@ -194,11 +196,20 @@ def main():
     torch.cuda.set_device(0)
     fq.load()
     timer = Timer(torch, fq.load())
-    only = set(args.only.split(",")) if args.only else {"step", "quant", "gemm", "sweep", "kv"}
+    only = (set(args.only.split(",")) if args.only
+            else {"step", "gemm", "grouped", "sweep", "quant", "kv"})
     kernels = {}
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    # A plain device copy of known size: the reference that scales the rocprofv3 HBM
+    # counters (FETCH_SIZE / WRITE_SIZE) to bytes.
+    calib_src = torch.empty(COPY_CALIB_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
 
     # ---------------------------------------------------------------- decode step
     log("building decode-step buffers")
@@ -251,7 +262,7 @@ def main():
         del graphs
 
     # ------------------------------------------------------------- GEMM per N
-    if "gemm" in only or "step" in only:
+    if "gemm" in only:
         for n in N_DECODE:
             launches = [(lambda s=s, n=n: fq.w8a8_block_gemm(s["q"], s["s"], s["w"][n][0],
                                                              s["w"][n][1], s["out"][n]))
@@ -270,6 +281,9 @@ def main():
             log(f"gemm n={n}: {mean_us:.2f} us (median {med_us:.2f}) "
                 f"{kernels[f'w8a8_gemm_m16_n{n}_k5120']['gbs']} GB/s")
 
+    if "grouped" in only:
+        for s in sets:
+            fq.fp8_group_quant(s["a"], s["q"], s["s"])
         launches = [(lambda s=s: fq.w8a8_block_gemm_grouped(
             s["q"], s["s"], [(s["w"][n][0], s["w"][n][1], s["out"][n]) for n in N_DECODE]))
             for s in sets]
@@ -408,17 +422,21 @@ def main():
 
 
 def profiled_traffic(name):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
-    on the current kernel source (else null)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/traffic.txt: '<kernel key> <bytes per launch> <source file> <sha256>'), if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
     try:
         with open(path) as f:
-            rec = json.load(f).get(name)
-    except (OSError, ValueError):
+            for line in f:
+                parts = line.split()
+                if len(parts) == 4 and parts[0] == name:
+                    if source_sha(parts[2]) == parts[3]:
+                        return int(parts[1])
+                    return None
+    except OSError:
         return None
-    if not rec or rec.get("source_sha256") != source_sha(rec.get("source", "")):
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    return None
 
 
 def source_sha(rel):
