@@ -42,6 +42,13 @@ __device__ __forceinline__ uint2 quant8(uint4 w, float s, float y) {
   return r;
 }
 
+// 16-byte load with the non-temporal (streaming) hint.
+__device__ __forceinline__ uint4 load16_nt(const uint4* p) {
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // max |x| of eight bf16 packed in a 16-byte word, as binary32.
 __device__ __forceinline__ float absmax8(uint4 w) {
   float m0 = fmaxf(fabsf(bf16_lo(w.x)), fabsf(bf16_hi(w.x)));

@@ -322,19 +322,6 @@ int launch_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
   return launch_status();
 }
 
-int num_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cus[dev]) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    cus[dev] = v;
-  }
-  return cus[dev];
-}
-
 template <int kGpw>
 int launch_persistent(const uint8_t* a_q, const float* a_scale, const ProjSet& ps, int m,
                       int k, int total, hipStream_t stream) {

@@ -57,7 +57,19 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
 // A wave takes kTokPerWave consecutive tokens: their slots are read first (scalar loads),
 // then every 16-byte load of the group is issued before any conversion, so each wave
 // keeps 2 * kTokPerWave loads in flight instead of waiting on one token at a time.
-constexpr int kTokPerWave = 4;
+#ifndef FP8Q_KV_TOKENS_PER_WAVE
+#define FP8Q_KV_TOKENS_PER_WAVE 4
+#endif
+#ifndef FP8Q_KV_BLOCKS_PER_CU
+#define FP8Q_KV_BLOCKS_PER_CU 0  // 0: one pass per wave; else a persistent grid
+#endif
+#ifndef FP8Q_KV_NT_LOAD
+#define FP8Q_KV_NT_LOAD 0
+#endif
+#ifndef FP8Q_KV_NT_STORE
+#define FP8Q_KV_NT_STORE 1
+#endif
+constexpr int kTokPerWave = FP8Q_KV_TOKENS_PER_WAVE;
 
 __global__ __launch_bounds__(kKvBlock) void kv_write_vec_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v, uint2* __restrict__ kc,
@@ -87,10 +99,84 @@ __global__ __launch_bounds__(kKvBlock) void kv_write_vec_kernel(
 #pragma unroll
       for (int i = 0; i < kTokPerWave; ++i) {
         if (ok[i]) {
+#if FP8Q_KV_NT_STORE
+          const uint2 kq = quant8<true>(kx[i], k_scale, k_inv);
+          const uint2 vq = quant8<true>(vx[i], v_scale, v_inv);
+          __builtin_nontemporal_store(uint64_t(kq.x) | (uint64_t(kq.y) << 32),
+                                      reinterpret_cast<uint64_t*>(kc + dst[i] + c));
+          __builtin_nontemporal_store(uint64_t(vq.x) | (uint64_t(vq.y) << 32),
+                                      reinterpret_cast<uint64_t*>(vc + dst[i] + c));
+#else
           kc[dst[i] + c] = quant8<true>(kx[i], k_scale, k_inv);
           vc[dst[i] + c] = quant8<true>(vx[i], v_scale, v_inv);
+#endif
         }
       }
+    }
+  }
+}
+
+// Wide form for rows of e = 16 * lpt elements with 2 * lpt dividing 64 (e = 16 .. 512):
+// a token takes 2 * lpt lanes -- the first lpt convert 16 elements of its K row each (two
+// 16-byte loads, one 16-byte store), the next lpt the same 16 elements of its V row -- so a
+// wave covers 64 / (2 * lpt) tokens per step and every store instruction writes whole
+// 16-byte lanes.  kSteps such steps are loaded before any is converted.
+#ifndef FP8Q_KV_WIDE_STEPS
+#define FP8Q_KV_WIDE_STEPS 1
+#endif
+constexpr int kWideSteps = FP8Q_KV_WIDE_STEPS;
+
+__device__ __forceinline__ void store16_nt(uint4 v, uint8_t* p) {
+#if FP8Q_KV_NT_STORE
+  __builtin_nontemporal_store(uint64_t(v.x) | (uint64_t(v.y) << 32), reinterpret_cast<uint64_t*>(p));
+  __builtin_nontemporal_store(uint64_t(v.z) | (uint64_t(v.w) << 32), reinterpret_cast<uint64_t*>(p + 8));
+#else
+  *reinterpret_cast<uint4*>(p) = v;
+#endif
+}
+
+__global__ __launch_bounds__(kKvBlock) void kv_write_wide_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint8_t* __restrict__ kc,
+    uint8_t* __restrict__ vc, const int64_t* __restrict__ slots, int64_t num_tokens, int lpt,
+    int64_t ks, int64_t vs, int64_t cs, int bs, int64_t nslots, float k_scale, float k_inv,
+    float v_scale, float v_inv) {
+  const int lane = threadIdx.x & 63;
+  const int tpw = 64 / (2 * lpt);               // tokens per wave per step
+  const int slot_in_wave = lane / (2 * lpt);    // which of those tokens
+  const int half = (lane / lpt) & 1;            // 0: K, 1: V
+  const int chunk = lane % lpt;                 // 16-element chunk within the row
+  const int e = 16 * lpt;
+  const uint16_t* src = half ? v : k;
+  const int64_t sstride = half ? vs : ks;
+  uint8_t* dpool = half ? vc : kc;
+  const float sc = half ? v_scale : k_scale, inv = half ? v_inv : k_inv;
+  const int64_t wave = (int64_t(blockIdx.x) * kKvBlock + threadIdx.x) >> 6;
+  const int64_t nwaves = (int64_t(gridDim.x) * kKvBlock) >> 6;
+  const int64_t per_iter = int64_t(tpw) * kWideSteps;
+  for (int64_t t0 = wave * per_iter; t0 < num_tokens; t0 += nwaves * per_iter) {
+    uint4 x0[kWideSteps], x1[kWideSteps];
+    int64_t tok[kWideSteps];
+#pragma unroll
+    for (int st = 0; st < kWideSteps; ++st) {
+      tok[st] = t0 + st * tpw + slot_in_wave;
+      const int64_t tl = tok[st] < num_tokens ? tok[st] : num_tokens - 1;  // in bounds
+      const uint4* p = reinterpret_cast<const uint4*>(src + tl * sstride + chunk * 16);
+#if FP8Q_KV_NT_LOAD
+      x0[st] = load16_nt(p);
+      x1[st] = load16_nt(p + 1);
+#else
+      x0[st] = p[0];
+      x1[st] = p[1];
+#endif
+    }
+#pragma unroll
+    for (int st = 0; st < kWideSteps; ++st) {
+      int64_t blk = 0, off = 0;
+      const int64_t tl = tok[st] < num_tokens ? tok[st] : num_tokens - 1;
+      const bool ok = tok[st] < num_tokens && slot_to_block(slots[tl], nslots, bs, &blk, &off);
+      const uint2 a = quant8<true>(x0[st], sc, inv);
+      const uint2 b = quant8<true>(x1[st], sc, inv);
+      if (ok) store16_nt(make_uint4(a.x, a.y, b.x, b.y), dpool + blk * cs + off * e + chunk * 16);
     }
   }
 }
@@ -202,11 +288,26 @@ int kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t* v_
   const int64_t nslots = num_blocks * block_size;
   // reciprocals on the host: IEEE binary32 division, RN(1/scale)
   const float k_inv = 1.0f / k_scale, v_inv = 1.0f / v_scale;
+  const bool wide = e % 16 == 0 && e <= 512 && 64 % (2 * (e / 16)) == 0 &&
+                    key_stride % 8 == 0 && value_stride % 8 == 0 && cache_stride % 16 == 0 &&
+                    aligned(k, 16) && aligned(v, 16) && aligned(k_cache, 16) &&
+                    aligned(v_cache, 16);
+  if (wide) {
+    const int lpt = int(e / 16);
+    const int64_t per_block = int64_t(kKvBlock / 64) * (64 / (2 * lpt)) * kWideSteps;
+    const int64_t blocks = clamp_grid((int64_t(num_tokens) + per_block - 1) / per_block);
+    launch(kv_write_wide_kernel, dim3(unsigned(blocks)), dim3(kKvBlock), 0, stream, k, v,
+           k_cache, v_cache, slot_mapping, int64_t(num_tokens), lpt, key_stride, value_stride,
+           cache_stride, block_size, nslots, k_scale, k_inv, v_scale, v_inv);
+    return launch_status();
+  }
   const bool vec = e % 8 == 0 && key_stride % 8 == 0 && value_stride % 8 == 0 &&
                    cache_stride % 8 == 0 && aligned(k, 16) && aligned(v, 16) &&
                    aligned(k_cache, 8) && aligned(v_cache, 8);
   const int64_t rows_per_block = vec ? kRowsPerBlock * kTokPerWave : kRowsPerBlock;
-  const int64_t blocks = clamp_grid((int64_t(num_tokens) + rows_per_block - 1) / rows_per_block);
+  int64_t blocks = clamp_grid((int64_t(num_tokens) + rows_per_block - 1) / rows_per_block);
+  if (FP8Q_KV_BLOCKS_PER_CU > 0 && blocks > int64_t(FP8Q_KV_BLOCKS_PER_CU) * num_cus())
+    blocks = int64_t(FP8Q_KV_BLOCKS_PER_CU) * num_cus();
   if (vec)
     launch(kv_write_vec_kernel, dim3(unsigned(blocks)), dim3(64, kRowsPerBlock), 0,
                        stream, reinterpret_cast<const uint4*>(k),

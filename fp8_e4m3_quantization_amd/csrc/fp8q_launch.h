@@ -39,6 +39,21 @@ inline void launch(Kernel kernel, dim3 grid, dim3 block, size_t lds, hipStream_t
   }
 }
 
+// Compute units of the current device (cached per device).
+inline int num_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
 // Status of the launch just enqueued on this thread.
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? FP8Q_OK : FP8Q_ELAUNCH;

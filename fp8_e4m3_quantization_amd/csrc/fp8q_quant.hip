@@ -29,6 +29,19 @@ namespace {
 
 constexpr int kQuantBlock = 256;           // 4 waves
 constexpr int kGroupsPerWave = 8;
+#ifndef FP8Q_QUANT_UNROLL
+#define FP8Q_QUANT_UNROLL 1  // wave tiles whose loads are issued together per iteration
+#endif
+#ifndef FP8Q_QUANT_BLOCKS_PER_CU
+#define FP8Q_QUANT_BLOCKS_PER_CU 0  // 0: one tile per wave; else a persistent grid
+#endif
+#ifndef FP8Q_QUANT_NT_LOAD
+#define FP8Q_QUANT_NT_LOAD 0
+#endif
+#ifndef FP8Q_QUANT_NT_STORE
+#define FP8Q_QUANT_NT_STORE 1  // codes written with the non-temporal hint
+#endif
+constexpr int kQuantUnroll = FP8Q_QUANT_UNROLL;
 constexpr int kGroupsPerBlock = kGroupsPerWave * (kQuantBlock / 64);
 
 __global__ __launch_bounds__(kQuantBlock) void group_quant_kernel(
@@ -38,23 +51,40 @@ __global__ __launch_bounds__(kQuantBlock) void group_quant_kernel(
   const int sub = lane & 7;  // lane within its group
   const int64_t wave = (int64_t(blockIdx.x) * kQuantBlock + threadIdx.x) >> 6;
   const int64_t wave_stride = (int64_t(gridDim.x) * kQuantBlock) >> 6;
-  for (int64_t base = wave * kGroupsPerWave; base < num_groups;
-       base += wave_stride * kGroupsPerWave) {
-    const int64_t g = base + (lane >> 3);
-    const bool live = g < num_groups;
-    uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
-    if (live) {
-      w0 = x[g * 16 + sub * 2];
-      w1 = x[g * 16 + sub * 2 + 1];
+  for (int64_t base = wave * kGroupsPerWave * kQuantUnroll; base < num_groups;
+       base += wave_stride * kGroupsPerWave * kQuantUnroll) {
+    uint4 w0[kQuantUnroll], w1[kQuantUnroll];
+    int64_t g[kQuantUnroll];
+#pragma unroll
+    for (int t = 0; t < kQuantUnroll; ++t) {
+      g[t] = base + t * kGroupsPerWave + (lane >> 3);
+      // past the end: re-read the last group (in bounds), nothing is stored for it
+      const int64_t gl = g[t] < num_groups ? g[t] : num_groups - 1;
+#if FP8Q_QUANT_NT_LOAD
+      w0[t] = load16_nt(x + gl * 16 + sub * 2);
+      w1[t] = load16_nt(x + gl * 16 + sub * 2 + 1);
+#else
+      w0[t] = x[gl * 16 + sub * 2];
+      w1[t] = x[gl * 16 + sub * 2 + 1];
+#endif
     }
-    float amax = max_over_8_lanes(fmaxf(absmax8(w0), absmax8(w1)));
-    float s = group_scale_from_amax(amax);
-    float y = 1.0f / s;  // IEEE division: RN(1/s)
-    uint2 c0 = quant8<false>(w0, s, y);
-    uint2 c1 = quant8<false>(w1, s, y);
-    if (live) {
-      q[g * 8 + sub] = make_uint4(c0.x, c0.y, c1.x, c1.y);
-      if (sub == 0) scales[g] = s;
+#pragma unroll
+    for (int t = 0; t < kQuantUnroll; ++t) {
+      const float amax = max_over_8_lanes(fmaxf(absmax8(w0[t]), absmax8(w1[t])));
+      const float s = group_scale_from_amax(amax);
+      const float y = 1.0f / s;  // IEEE division: RN(1/s)
+      const uint2 c0 = quant8<false>(w0[t], s, y);
+      const uint2 c1 = quant8<false>(w1[t], s, y);
+      if (g[t] < num_groups) {
+#if FP8Q_QUANT_NT_STORE
+        uint64_t* qp = reinterpret_cast<uint64_t*>(q + g[t] * 8 + sub);
+        __builtin_nontemporal_store(uint64_t(c0.x) | (uint64_t(c0.y) << 32), qp);
+        __builtin_nontemporal_store(uint64_t(c1.x) | (uint64_t(c1.y) << 32), qp + 1);
+#else
+        q[g[t] * 8 + sub] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+#endif
+        if (sub == 0) scales[g[t]] = s;
+      }
     }
   }
 }
@@ -110,7 +140,10 @@ extern "C" int fp8_group_quant(const uint16_t* x, uint8_t* q, float* scales, int
   if (!x || !q || !scales) return FP8Q_ENULL;
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4)) return FP8Q_EALIGN;
   const int64_t groups = m * (k / 128);
-  const int64_t blocks = clamp_grid((groups + kGroupsPerBlock - 1) / kGroupsPerBlock);
+  int64_t blocks = clamp_grid((groups + kGroupsPerBlock * kQuantUnroll - 1) /
+                              (kGroupsPerBlock * kQuantUnroll));
+  if (FP8Q_QUANT_BLOCKS_PER_CU > 0 && blocks > int64_t(FP8Q_QUANT_BLOCKS_PER_CU) * num_cus())
+    blocks = int64_t(FP8Q_QUANT_BLOCKS_PER_CU) * num_cus();
   launch(group_quant_kernel, dim3(unsigned(blocks)), dim3(kQuantBlock), 0,
                      stream, reinterpret_cast<const uint4*>(x), reinterpret_cast<uint4*>(q),
                      scales, groups);
