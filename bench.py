@@ -1,10 +1,10 @@
 """Benchmark of the FP8 (E4M3) quantize-and-consume path on one MI355X.
 
 One step = one pass of the whole hot path over one decode batch:
-  per-token 1x128 group quant of the activation [16 x 5120] (bf16 -> E4M3 + scales),
+  per-token 1x128 group quant of the activation [16 x 5120] (bf16 -> E4M3 + scales) and
   the four decode projections sharing it (W8A8 block-scaled GEMM, M=16, K=5120,
-  N = 16384, 12288, 5120, 1024), the K/V absmax and the paged FP8 KV write of the batch's
-  16 new tokens (4 KV heads x 128 dims) at the calibrated scale.
+  N = 16384, 12288, 5120, 1024) in one fused launch, the K/V absmax and the paged FP8 KV
+  write of the batch's 16 new tokens (4 KV heads x 128 dims) at the calibrated scale.
 The step is captured once per buffer set in a HIP graph; inputs rotate over >= 1 GB of
 buffer sets so the 256 MB MALL cannot serve repeated reads.  value = algorithmic bytes
 per step / measured step time (GB/s).
@@ -79,8 +79,15 @@ def grouped_gemm_bytes(m, ns, k):
     return sum(gemm_bytes(m, n, k) for n in ns) - (len(ns) - 1) * (m * k + m * (k // 128) * 4)
 
 
+def fused_step_gemm_bytes(m, ns, k):
+    """Fused quant + grouped GEMM: bf16 activation read once, codes and scales written once,
+    weights, weight scales and outputs as in the grouped GEMM."""
+    return (m * k * 2 + m * k + m * (k // 128) * 4
+            + sum(gemm_weight_bytes(n, k) + m * n * 2 for n in ns))
+
+
 def step_bytes():
-    return (quant_bytes(M_DECODE, K_DECODE) + grouped_gemm_bytes(M_DECODE, N_DECODE, K_DECODE)
+    return (fused_step_gemm_bytes(M_DECODE, N_DECODE, K_DECODE)
             + kv_amax_bytes(M_DECODE) + kv_write_bytes(M_DECODE))
 
 
@@ -221,9 +228,10 @@ def main():
     k_scale, v_scale = cal.scales()
 
     def run_step(s):
-        fq.fp8_group_quant(s["a"], s["q"], s["s"])
-        fq.w8a8_block_gemm_grouped(s["q"], s["s"], [(s["w"][n][0], s["w"][n][1], s["out"][n])
-                                                    for n in N_DECODE])
+        # group quant fused into the grouped GEMM: one launch quantizes the activation (codes
+        # and scales also written out) and computes the four projections
+        fq.fp8_quant_w8a8_gemm_grouped(s["a"], [(s["w"][n][0], s["w"][n][1], s["out"][n])
+                                                for n in N_DECODE], q=s["q"], scales=s["s"])
         cal.observe(s["k"], s["v"], KV_H, KV_D, kc, vc, s["slots"], KV_BS)  # frozen: no-op
         fq.fp8_kv_amax(s["k"], s["v"], s["amax"])
         fq.fp8_kv_write(s["k"], s["v"], kc, vc, s["slots"], KV_H, KV_D, KV_BS, k_scale, v_scale)
@@ -296,6 +304,17 @@ def main():
             tflops=round(2.0 * M_DECODE * sum(N_DECODE) * K_DECODE / (mean_us * 1e-6) / 1e12, 2))
         log(f"grouped gemm (4 projections): {mean_us:.2f} us "
             f"{kernels['w8a8_gemm_grouped_m16_k5120_4proj']['gbs']} GB/s")
+        launches = [(lambda s=s: fq.fp8_quant_w8a8_gemm_grouped(
+            s["a"], [(s["w"][n][0], s["w"][n][1], s["out"][n]) for n in N_DECODE],
+            q=s["q"], scales=s["s"])) for s in sets]
+        mean_us, med_us = timer.kernel_us(launches, args.iters)
+        b = fused_step_gemm_bytes(M_DECODE, N_DECODE, K_DECODE)
+        kernels["quant_w8a8_gemm_fused_m16_k5120_4proj"] = dict(
+            us=round(mean_us, 3), us_median=round(med_us, 3),
+            gbs=round(b / (mean_us * 1e-6) / 1e9, 1),
+            frac_hbm=round(b / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), bytes=b)
+        log(f"fused quant + grouped gemm: {mean_us:.2f} us "
+            f"{kernels['quant_w8a8_gemm_fused_m16_k5120_4proj']['gbs']} GB/s")
 
     # ----------------------------------------------------------- width sweep
     if "sweep" in only:
@@ -382,14 +401,15 @@ def main():
         cpu = cpu_baseline(synth, log)
 
     # --------------------------------------------------------------- report
-    dom_name = "w8a8_gemm_grouped_m16_k5120_4proj"
+    dom_name = "quant_w8a8_gemm_fused_m16_k5120_4proj"
     dom = kernels.get(dom_name)
     roof = None
     if dom:
         roof = dict(bound="hbm", achieved=dom["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(dom["gbs"] / HBM_PEAK_GBS, 4),
                     traffic=profiled_traffic(dom_name),
-                    kernel="w8a8_persistent_kernel<5> (4 decode projections, one launch)",
+                    kernel="w8a8_persistent_kernel<5,...,quant> (group quant + 4 decode "
+                           "projections, one launch)",
                     bytes_per_launch=dom["bytes"], us_per_launch=dom["us"])
     st = result.get("step")
     line = {

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     fp8_group_quant,
     fp8_kv_amax,
     fp8_kv_write,
+    fp8_quant_w8a8_gemm_grouped,
     load,
     strerror,
     w8a8_block_gemm,

@@ -21,7 +21,7 @@ FP8Q_CALIB_STAGE, FP8Q_CALIB_DECLINE, FP8Q_CALIB_FREEZE, FP8Q_CALIB_FROZEN = 0, 
 # Every symbol include/fp8q.h declares.
 EXPORTS = (
     "fp8q_strerror", "fp8q_version", "fp8q_time_next_launch", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
-    "w8a8_block_gemm", "w8a8_block_gemm_grouped", "fp8_kv_write", "fp8_kv_amax", "fp8q_kv_calib_create",
+    "w8a8_block_gemm", "w8a8_block_gemm_grouped", "fp8_quant_w8a8_gemm_grouped", "fp8_kv_write", "fp8_kv_amax", "fp8q_kv_calib_create",
     "fp8q_kv_calib_observe", "fp8q_kv_calib_decide", "fp8q_kv_calib_scales",
     "fp8q_kv_calib_get_info", "fp8q_kv_calib_destroy",
 )
@@ -83,6 +83,8 @@ def load() -> ctypes.CDLL:
         "w8a8_block_gemm": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, P]),
         "w8a8_block_gemm_grouped": (ctypes.c_int, [P, P, ctypes.POINTER(GemmProj), I32, I32,
                                                    I32, P]),
+        "fp8_quant_w8a8_gemm_grouped": (ctypes.c_int, [P, P, P, ctypes.POINTER(GemmProj), I32,
+                                                       I32, I32, P]),
         "fp8_kv_write": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, I64, F32, F32,
                                         I32, I32, I64, P]),
         "fp8_kv_amax": (ctypes.c_int, [P, P, I64, P, P]),
@@ -209,11 +211,7 @@ def w8a8_block_gemm(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tensor,
     return out
 
 
-def w8a8_block_gemm_grouped(a_q: torch.Tensor, a_scale: torch.Tensor, projections,
-                            stream: int | None = None):
-    """One launch over several projections of the same activation.  projections: list of
-    (w_q [n, k], w_scale [n/128, k/128], out [m, ldc] or None); returns the outputs."""
-    m, k = a_q.shape
+def _proj_array(m, k, projections, device):
     arr = (GemmProj * len(projections))()
     outs = []
     for i, (w_q, w_scale, out) in enumerate(projections):
@@ -221,13 +219,22 @@ def w8a8_block_gemm_grouped(a_q: torch.Tensor, a_scale: torch.Tensor, projection
         if w_q.shape[1] != k or w_scale.numel() != (n // 128) * (k // 128):
             raise ValueError(f"projection {i} does not match the activation")
         if out is None:
-            out = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+            out = torch.empty((m, n), dtype=torch.bfloat16, device=device)
         ldc = out.shape[-1]
         if out.numel() < (m - 1) * ldc + n:
             raise ValueError(f"projection {i}: out is smaller than (m - 1) * ldc + n")
         arr[i] = GemmProj(_dev(w_q, "w_q", _U8), _dev(w_scale, "w_scale", torch.float32),
                           _dev(out, "out", _BF16), n, ldc)
         outs.append(out)
+    return arr, outs
+
+
+def w8a8_block_gemm_grouped(a_q: torch.Tensor, a_scale: torch.Tensor, projections,
+                            stream: int | None = None):
+    """One launch over several projections of the same activation.  projections: list of
+    (w_q [n, k], w_scale [n/128, k/128], out [m, ldc] or None); returns the outputs."""
+    m, k = a_q.shape
+    arr, outs = _proj_array(m, k, projections, a_q.device)
     if a_scale.numel() != m * (k // 128):
         raise ValueError("a_scale does not match a_q")
     st = load().w8a8_block_gemm_grouped(_dev(a_q, "a_q", _U8),
@@ -235,6 +242,26 @@ def w8a8_block_gemm_grouped(a_q: torch.Tensor, a_scale: torch.Tensor, projection
                                         len(projections), m, k,
                                         current_stream(a_q.device) if stream is None else stream)
     check("w8a8_block_gemm_grouped", st)
+    return outs
+
+
+def fp8_quant_w8a8_gemm_grouped(a: torch.Tensor, projections, q: torch.Tensor | None = None,
+                                scales: torch.Tensor | None = None,
+                                stream: int | None = None):
+    """bf16 activation [m, k] -> group quant fused into the grouped GEMM (one launch).
+    q / scales, if given, receive the codes and scales fp8_group_quant would produce."""
+    m, k = a.shape
+    arr, outs = _proj_array(m, k, projections, a.device)
+    if (q is None) != (scales is None):
+        raise ValueError("pass both q and scales, or neither")
+    qp = _dev(q, "q", _U8) if q is not None else None
+    sp = _dev(scales, "scales", torch.float32) if scales is not None else None
+    if q is not None and (q.numel() < m * k or scales.numel() < m * (k // 128)):
+        raise ValueError("q / scales too small")
+    st = load().fp8_quant_w8a8_gemm_grouped(_dev(a, "a", _BF16), qp, sp, arr, len(projections),
+                                            m, k,
+                                            current_stream(a.device) if stream is None else stream)
+    check("fp8_quant_w8a8_gemm_grouped", st)
     return outs
 
 

@@ -163,6 +163,9 @@ __device__ __forceinline__ void lds_barrier() {
 #ifndef FP8Q_GEMM_AUX
 #define FP8Q_GEMM_AUX 0  // cache-policy bits of the weight loads
 #endif
+#ifndef FP8Q_GEMM_NT_OUT
+#define FP8Q_GEMM_NT_OUT 1  // bf16 outputs written with the non-temporal hint
+#endif
 constexpr uint32_t kBufferDword3 = 0x00020000;  // raw 32-bit buffer format (gfx9 family)
 
 // Weight block scales are read-only for the whole launch and uniform per wave: reading
@@ -192,10 +195,21 @@ __device__ __forceinline__ v8i buffer_load32(__amdgpu_buffer_rsrc_t r, int off) 
 // to LDS, one barrier, a fixed-order sum over the waves, bf16 stores.  Per-strip barriers
 // would tie every strip to the slowest wave's load latency.  The LDS partial area is
 // double-buffered across rounds, so one barrier per round suffices.
-template <int kGpw, int kDepth, int kAux, int kRound>
+// Where the activation comes from: already quantized (codes + token-major scales), or
+// bf16, quantized by the GEMM itself (each wave quantizes its own K-slice in registers
+// with the group quantizer's arithmetic, so the codes are bit-identical to
+// fp8_group_quant's; workgroup 0 optionally writes them out).
+struct ActSrc {
+  const uint8_t* a_q;
+  const float* a_scale;
+  const uint16_t* a_bf16;
+  uint8_t* q_out;
+  float* s_out;
+};
+
+template <int kGpw, int kDepth, int kAux, int kRound, bool kQuant>
 __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
-    const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale, ProjSet ps, int m,
-    int k, int total_strips) {
+    ActSrc act, ProjSet ps, int m, int k, int total_strips) {
   static_assert(kRound % (kDepth + 1) == 0, "buffer index must be static within a round");
   static_assert(kRound * 256 == kPWaves * 64 * 2, "reduce: two outputs per lane");
   __shared__ float s_part[2][kRound * kPWaves * 4 * 64];
@@ -205,31 +219,11 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
   const int g0 = (groups * wv) / kPWaves;
   const int cnt = (groups * (wv + 1)) / kPWaves - g0;  // 0 <= cnt <= kGpw
   const int row = lane & 15, koff = (lane >> 4) * 32;
+  const int arow = row < m ? row : m - 1;  // activation loads stay in bounds
   int goff[kGpw];  // byte offset of slice group u (a short slice re-reads its last group,
                    // whose activation fragment below is zero)
 #pragma unroll
   for (int u = 0; u < kGpw; ++u) goff[u] = (g0 + max(0, min(u, cnt - 1))) * 128;
-
-  // activation slice: fragments (rows >= m and groups past the slice are zero) and the
-  // 4 row scales per group this lane's accumulators need
-  v8i a[kGpw];
-  float4 as[kGpw];
-  {
-    const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    const uint8_t* ap = a_q + int64_t(row < m ? row : 0) * k + koff;
-    const int r0 = 4 * (lane >> 4);
-#pragma unroll
-    for (int u = 0; u < kGpw; ++u) {
-      const bool live = u < cnt;
-      const v8i f = load32(ap + goff[u]);
-      a[u] = (live && row < m) ? f : zero8;
-      const int g = goff[u] >> 7;
-      as[u].x = (live && r0 + 0 < m) ? a_scale[int64_t(r0 + 0) * groups + g] : 0.0f;
-      as[u].y = (live && r0 + 1 < m) ? a_scale[int64_t(r0 + 1) * groups + g] : 0.0f;
-      as[u].z = (live && r0 + 2 < m) ? a_scale[int64_t(r0 + 2) * groups + g] : 0.0f;
-      as[u].w = (live && r0 + 3 < m) ? a_scale[int64_t(r0 + 3) * groups + g] : 0.0f;
-    }
-  }
 
   // strip s -> (projection, first column); uniform across the workgroup
   auto locate = [&](int s, int* p_out, int* n0) {
@@ -250,6 +244,89 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
 #pragma unroll
     for (int u = 0; u < kGpw; ++u) sl.ws[u] = wsp[goff[u] >> 7];
   };
+
+  const int stride = int(gridDim.x);
+  const int first = int(blockIdx.x);
+  const int nit = (total_strips - first + stride - 1) / stride;
+  if (nit <= 0) return;
+
+  // 1) raw activation loads, 2) the first weight prefetch, 3) activation fragments: the
+  // fragments wait only for the loads issued before the prefetch, so the weight stream
+  // starts without waiting for the activation (load counters retire in order).
+  v8i a[kGpw];
+  float4 as[kGpw];
+  Slice<kGpw> buf[kDepth + 1];
+  const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int r0 = 4 * (lane >> 4);
+  if constexpr (!kQuant) {
+    v8i raw[kGpw];
+    float4 rs[kGpw];
+    const uint8_t* ap = act.a_q + int64_t(arow) * k + koff;
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u) {
+      raw[u] = load32(ap + goff[u]);
+      const int g = goff[u] >> 7;
+      rs[u].x = act.a_scale[int64_t(min(r0 + 0, m - 1)) * groups + g];
+      rs[u].y = act.a_scale[int64_t(min(r0 + 1, m - 1)) * groups + g];
+      rs[u].z = act.a_scale[int64_t(min(r0 + 2, m - 1)) * groups + g];
+      rs[u].w = act.a_scale[int64_t(min(r0 + 3, m - 1)) * groups + g];
+    }
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) fetch(first + j * stride, buf[j]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the activation math
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u) {
+      const bool live = u < cnt;
+      a[u] = (live && row < m) ? raw[u] : zero8;
+      as[u].x = (live && r0 + 0 < m) ? rs[u].x : 0.0f;
+      as[u].y = (live && r0 + 1 < m) ? rs[u].y : 0.0f;
+      as[u].z = (live && r0 + 2 < m) ? rs[u].z : 0.0f;
+      as[u].w = (live && r0 + 3 < m) ? rs[u].w : 0.0f;
+    }
+  } else {
+    // lane l holds elements [32*(l>>4), +32) of row (l & 15) in each slice group: the four
+    // lanes l, l^16, l^32, l^48 together hold the row's 128-element group
+    uint4 raw[kGpw][4];
+    const uint4* xp = reinterpret_cast<const uint4*>(act.a_bf16 + int64_t(arow) * k + koff);
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) raw[u][c] = xp[(goff[u] >> 3) + c];
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) fetch(first + j * stride, buf[j]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the activation math
+    const bool write_out = blockIdx.x == 0 && act.q_out != nullptr;
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u) {
+      const bool live = u < cnt;
+      float amax = fmaxf(fmaxf(absmax8(raw[u][0]), absmax8(raw[u][1])),
+                         fmaxf(absmax8(raw[u][2]), absmax8(raw[u][3])));
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const float sc = group_scale_from_amax(amax);
+      const float y = 1.0f / sc;  // IEEE division: RN(1/s)
+      const uint2 c0 = quant8<false>(raw[u][0], sc, y), c1 = quant8<false>(raw[u][1], sc, y);
+      const uint2 c2 = quant8<false>(raw[u][2], sc, y), c3 = quant8<false>(raw[u][3], sc, y);
+      v8i f;
+      f[0] = int(c0.x); f[1] = int(c0.y); f[2] = int(c1.x); f[3] = int(c1.y);
+      f[4] = int(c2.x); f[5] = int(c2.y); f[6] = int(c3.x); f[7] = int(c3.y);
+      a[u] = (live && row < m) ? f : zero8;
+      // row r's scale sits in lane r (and r+16, r+32, r+48)
+      const float s0 = __shfl(sc, r0 + 0), s1 = __shfl(sc, r0 + 1);
+      const float s2 = __shfl(sc, r0 + 2), s3 = __shfl(sc, r0 + 3);
+      as[u].x = (live && r0 + 0 < m) ? s0 : 0.0f;
+      as[u].y = (live && r0 + 1 < m) ? s1 : 0.0f;
+      as[u].z = (live && r0 + 2 < m) ? s2 : 0.0f;
+      as[u].w = (live && r0 + 3 < m) ? s3 : 0.0f;
+      if (write_out && live && row < m) {
+        uint4* qo = reinterpret_cast<uint4*>(act.q_out + int64_t(row) * k + goff[u] + koff);
+        qo[0] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+        qo[1] = make_uint4(c2.x, c2.y, c3.x, c3.y);
+        if (lane < 16) act.s_out[int64_t(row) * groups + (goff[u] >> 7)] = sc;
+      }
+    }
+  }
+
   auto multiply = [&](const Slice<kGpw>& cur) {
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -264,14 +341,7 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
     return acc;
   };
 
-  // this workgroup's strips: blockIdx.x + i * gridDim.x for i < nit; kDepth ahead in flight
-  const int stride = int(gridDim.x);
-  const int first = int(blockIdx.x);
-  const int nit = (total_strips - first + stride - 1) / stride;
-  if (nit <= 0) return;
-  Slice<kGpw> buf[kDepth + 1];
-#pragma unroll
-  for (int j = 0; j < kDepth; ++j) fetch(first + j * stride, buf[j]);
+  // this workgroup's strips: first + i * stride for i < nit; kDepth ahead in flight
   int par = 0;
   for (int i = 0; i < nit; i += kRound) {
     float* part = s_part[par];  // [round strip][wave][4][64]
@@ -304,7 +374,11 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
           const int r = 4 * (lane >> 4) + q0 + x;
+#if FP8Q_GEMM_NT_OUT
+          if (r < m) __builtin_nontemporal_store(f32_to_bf16_rne(sum[x]), o + int64_t(r) * ldc);
+#else
           if (r < m) o[int64_t(r) * ldc] = f32_to_bf16_rne(sum[x]);
+#endif
         }
       }
     }
@@ -322,33 +396,31 @@ int launch_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
   return launch_status();
 }
 
-template <int kGpw>
-int launch_persistent(const uint8_t* a_q, const float* a_scale, const ProjSet& ps, int m,
-                      int k, int total, hipStream_t stream) {
+template <int kGpw, bool kQuant>
+int launch_persistent(const ActSrc& act, const ProjSet& ps, int m, int k, int total,
+                      hipStream_t stream) {
   const int grid = total < num_cus() ? total : num_cus();
-  // deeper prefetch only while the buffers still fit in registers without spilling
   constexpr int kDepth = 1;
   constexpr int kRound = 4;
-  launch((w8a8_persistent_kernel<kGpw, kDepth, FP8Q_GEMM_AUX, kRound>), dim3(grid),
-         dim3(64 * kPWaves), 0,
-                     stream, a_q, a_scale, ps, m, k, total);
+  launch((w8a8_persistent_kernel<kGpw, kDepth, FP8Q_GEMM_AUX, kRound, kQuant>), dim3(grid),
+         dim3(64 * kPWaves), 0, stream, act, ps, m, k, total);
   return launch_status();
 }
 
 // Persistent kernel for k <= 8 * 8 * 128 (each wave holds at most 8 groups).
-int run_persistent(const uint8_t* a_q, const float* a_scale, const ProjSet& ps, int m,
-                   int k, hipStream_t stream) {
+template <bool kQuant>
+int run_persistent(const ActSrc& act, const ProjSet& ps, int m, int k, hipStream_t stream) {
   const int total = ps.strip_end[ps.count - 1];
   const int gpw = (k / 128 + kPWaves - 1) / kPWaves;
   switch (gpw) {
-    case 1: return launch_persistent<1>(a_q, a_scale, ps, m, k, total, stream);
-    case 2: return launch_persistent<2>(a_q, a_scale, ps, m, k, total, stream);
-    case 3: return launch_persistent<3>(a_q, a_scale, ps, m, k, total, stream);
-    case 4: return launch_persistent<4>(a_q, a_scale, ps, m, k, total, stream);
-    case 5: return launch_persistent<5>(a_q, a_scale, ps, m, k, total, stream);
-    case 6: return launch_persistent<6>(a_q, a_scale, ps, m, k, total, stream);
-    case 7: return launch_persistent<7>(a_q, a_scale, ps, m, k, total, stream);
-    case 8: return launch_persistent<8>(a_q, a_scale, ps, m, k, total, stream);
+    case 1: return launch_persistent<1, kQuant>(act, ps, m, k, total, stream);
+    case 2: return launch_persistent<2, kQuant>(act, ps, m, k, total, stream);
+    case 3: return launch_persistent<3, kQuant>(act, ps, m, k, total, stream);
+    case 4: return launch_persistent<4, kQuant>(act, ps, m, k, total, stream);
+    case 5: return launch_persistent<5, kQuant>(act, ps, m, k, total, stream);
+    case 6: return launch_persistent<6, kQuant>(act, ps, m, k, total, stream);
+    case 7: return launch_persistent<7, kQuant>(act, ps, m, k, total, stream);
+    case 8: return launch_persistent<8, kQuant>(act, ps, m, k, total, stream);
     default: return FP8Q_EINVAL;
   }
 }
@@ -392,7 +464,8 @@ extern "C" int w8a8_block_gemm(const uint8_t* a_q, const float* a_scale, const u
     ps.ldc[0] = ldc;
     ps.strip_end[0] = n / 16;
     ps.count = 1;
-    return run_persistent(a_q, a_scale, ps, m, k, stream);
+    const ActSrc act = {a_q, a_scale, nullptr, nullptr, nullptr};
+    return run_persistent<false>(act, ps, m, k, stream);
   }
   return launch_gemm<4, 5>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, stream);
 }
@@ -430,5 +503,34 @@ extern "C" int w8a8_block_gemm_grouped(const uint8_t* a_q, const float* a_scale,
     ps.strip_end[p] = end;
   }
   ps.count = count;
-  return run_persistent(a_q, a_scale, ps, m, k, stream);
+  const ActSrc act = {a_q, a_scale, nullptr, nullptr, nullptr};
+  return run_persistent<false>(act, ps, m, k, stream);
+}
+
+extern "C" int fp8_quant_w8a8_gemm_grouped(const uint16_t* a, uint8_t* a_q, float* a_scale,
+                                           const fp8q_gemm_proj* projs, int32_t count,
+                                           int32_t m, int32_t k, hipStream_t stream) {
+  if (count < 1 || count > kMaxProj) return FP8Q_EINVAL;
+  if (m < 1 || m > 16 || k <= 0 || k % 128 != 0 || k > kPersistentMaxK) return FP8Q_EINVAL;
+  if (!a || !projs) return FP8Q_ENULL;
+  if ((a_q == nullptr) != (a_scale == nullptr)) return FP8Q_ENULL;
+  if (!aligned(a, 16) || (a_q && (!aligned(a_q, 16) || !aligned(a_scale, 4))))
+    return FP8Q_EALIGN;
+  ProjSet ps = {};
+  int64_t end = 0;
+  for (int p = 0; p < count; ++p) {
+    const int rc = check_proj(projs[p].w_q, projs[p].w_scale, projs[p].out, projs[p].n,
+                              projs[p].ldc);
+    if (rc != FP8Q_OK) return rc;
+    end += projs[p].n / 16;
+    if (end > 0x7FFFFFFF) return FP8Q_EINVAL;
+    ps.w[p] = projs[p].w_q;
+    ps.ws[p] = projs[p].w_scale;
+    ps.out[p] = projs[p].out;
+    ps.ldc[p] = projs[p].ldc;
+    ps.strip_end[p] = int(end);
+  }
+  ps.count = count;
+  const ActSrc act = {nullptr, nullptr, a, a_q, a_scale};
+  return run_persistent<true>(act, ps, m, k, stream);
 }

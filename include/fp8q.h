@@ -137,6 +137,21 @@ int w8a8_block_gemm_grouped(const uint8_t* a_q, const float* a_scale,
                             const fp8q_gemm_proj* projs, int32_t count, int32_t m, int32_t k,
                             hipStream_t stream);
 
+/* ------------------------------------- group quant fused into the grouped GEMM
+ * [actq] module doc and [decode] decode_w8a8_quant_act + decode_w8a8_gemm, in one launch:
+ * the activation is quantized per 1x128 group (exactly fp8_group_quant's arithmetic, so
+ * the codes and scales are bit-identical to it) inside the GEMM, each wave quantizing the
+ * K-slice it multiplies, then every projection is computed as w8a8_block_gemm_grouped
+ * would from those codes (same bits).
+ *   a        device, bf16 [m, k] row-major, 16-byte aligned
+ *   a_q, a_scale  optional outputs (both NULL or both set): the codes [m, k] and scales
+ *            [m, k/128] as fp8_group_quant writes them (16- / 4-byte aligned)
+ *   projs, count  as w8a8_block_gemm_grouped;  1 <= m <= 16;  k % 128 == 0, k <= 8192
+ * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EALIGN, FP8Q_ELAUNCH. */
+int fp8_quant_w8a8_gemm_grouped(const uint16_t* a, uint8_t* a_q, float* a_scale,
+                                const fp8q_gemm_proj* projs, int32_t count, int32_t m,
+                                int32_t k, hipStream_t stream);
+
 /* --------------------------------------------------------- paged FP8 KV write
  * [staging] Fp8KvWriteTarget and replay_and_release (the write's arguments: strides in
  * elements, pool stride = block_size * heads * head_dim); [staging] module doc: one scale

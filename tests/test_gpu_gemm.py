@@ -245,3 +245,51 @@ def test_long_k_both_kernel_forms(k):
     """k <= 8192 runs the persistent form; longer k the K-split form."""
     wq, ws = _weights(384, k, 5)
     _check(synth.decode_activation(7, k=k, seed=k), wq, ws)
+
+
+@pytest.mark.parametrize("m", [16, 5, 1])
+def test_fused_quant_gemm_matches_separate_calls(m):
+    """Quantizing inside the GEMM gives the standalone quantizer's codes/scales and the
+    grouped GEMM's outputs, bit for bit."""
+    a = synth.decode_activation(m, seed=2200 + m)
+    a_d = bf16_dev(a)
+    q, s = fq.fp8_group_quant(a_d)
+    projs = []
+    for n in synth.DECODE_N:
+        wq, ws = _weights(n, synth.DECODE_K, 2100 + n)
+        projs.append((u8_dev(wq), f32_dev(ws)))
+    ref = fq.w8a8_block_gemm_grouped(q, s, [(w, ws, None) for w, ws in projs])
+    q2 = torch.full_like(q, 0x5A)
+    s2 = torch.full_like(s, -1.0)
+    outs = fq.fp8_quant_w8a8_gemm_grouped(a_d, [(w, ws, None) for w, ws in projs], q=q2,
+                                          scales=s2)
+    assert np.array_equal(host(q2), host(q))
+    assert np.array_equal(host(s2).view(np.uint32), host(s).view(np.uint32))
+    for o, r in zip(outs, ref):
+        assert np.array_equal(host(o), host(r))
+    # without the optional outputs
+    outs2 = fq.fp8_quant_w8a8_gemm_grouped(a_d, [(w, ws, None) for w, ws in projs])
+    for o, r in zip(outs2, ref):
+        assert np.array_equal(host(o), host(r))
+
+
+def test_fused_quant_gemm_edge_activation_values():
+    """All-zero and negative-zero groups, a subnormal and huge values through the fused path."""
+    rng = np.random.default_rng(12)
+    m, k = 4, 1024
+    x = synth.to_bf16_bits(rng.normal(0, 1, size=(m, k)))
+    x[0, :128] = 0
+    x[1, 128:256] = 0x8000
+    x[2, 256] = 0x0001
+    x[3, 512:640] = 0x7F7F
+    a_d = bf16_dev(x)
+    wq, ws = _weights(256, k, 13)
+    q = torch.empty((m, k), dtype=torch.uint8, device=DEV)
+    s = torch.empty((m, k // 128), dtype=torch.float32, device=DEV)
+    out = fq.fp8_quant_w8a8_gemm_grouped(a_d, [(u8_dev(wq), f32_dev(ws), None)], q=q,
+                                         scales=s)[0]
+    q_ref, s_ref = oracle.group_quant(x)
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    ok, worst = gemm_tolerance_ok(host(out), oracle.gemm(q_ref, s_ref, wq, ws))
+    assert ok, worst
