@@ -13,6 +13,7 @@ Functions (all single-threaded, in the order the pages define them):
   gemm(a_q, a_s, w_q, w_s)           -> float64[m,n] reference
   amax(x_bf16)                       -> float32
   kv_write(...)                      in-place on the uint8 pools
+  kv_read(...)                       dequantizing gather of a paged history to bf16
   Calibrator                         one layer's online scale calibration model
 """
 import ctypes
@@ -55,6 +56,8 @@ def _load():
     lib.oracle_amax.argtypes = [_p, _i64, _p]
     lib.oracle_kv_write.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _f32, _f32,
                                     _i64, _i64, _i64]
+    lib.oracle_kv_read.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _f32, _f32, _p, _p,
+                                   _i64, _i64, _i64]
     lib.oracle_calib_create.restype = _p
     lib.oracle_calib_create.argtypes = [_i64, _f32, _f32]
     lib.oracle_calib_destroy.argtypes = [_p]
@@ -182,6 +185,18 @@ def kv_write(k_bf16, v_bf16, k_cache, v_cache, slots, num_tokens, num_kv_heads, 
     lib.oracle_kv_write(_ptr(kx), _ptr(vx), _ptr(k_cache), _ptr(v_cache), _ptr(sl),
                         num_tokens, num_kv_heads, head_dim, block_size, k_scale, v_scale,
                         key_stride, value_stride, cache_stride)
+
+
+def kv_read(k_cache, v_cache, slots, num_kv_heads, head_dim, block_size, num_blocks, k_scale,
+            v_scale, k_out, v_out, key_stride, value_stride, cache_stride):
+    """Dequantizing gather of a paged history; k_out / v_out (uint16 bf16 bits) updated in place."""
+    lib = _load()
+    sl = np.ascontiguousarray(slots, dtype=np.int64)
+    assert k_out.dtype == np.uint16 and v_out.dtype == np.uint16
+    assert k_out.flags["C_CONTIGUOUS"] and v_out.flags["C_CONTIGUOUS"]
+    lib.oracle_kv_read(_ptr(k_cache), _ptr(v_cache), _ptr(sl), sl.size, num_kv_heads, head_dim,
+                       block_size, num_blocks, k_scale, v_scale, _ptr(k_out), _ptr(v_out),
+                       key_stride, value_stride, cache_stride)
 
 
 class Calibrator:

@@ -306,6 +306,42 @@ void oracle_kv_write(const uint16_t* kx, const uint16_t* vx, uint8_t* kc, uint8_
   }
 }
 
+/* ------------------------------------------------------ paged KV read (dequantize) */
+
+/* bf16 bit pattern of a binary32, round to nearest even; NaN maps to the quiet 0x7FC0. */
+static uint16_t oracle_f32_to_bf16(float f) {
+  uint32_t b = f32_bits(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)(((b >> 16) & 0x8000u) | 0x7FC0u);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+/* Attention-side read of a paged history at one scale (staging module doc: a sequence's
+ * history is dequantized with one k_scale / v_scale): for each token with a slot in
+ * [0, num_blocks * block_size), every element is bf16(fp32(dec(code)) * scale), the
+ * product one binary32 multiplication rounded to nearest even, then rounded to bf16.
+ * Tokens with other slots are left untouched. */
+void oracle_kv_read(const uint8_t* kc, const uint8_t* vc, const int64_t* slots, int64_t T,
+                    int64_t H, int64_t D, int64_t block_size, int64_t num_blocks,
+                    float k_scale, float v_scale, uint16_t* ko, uint16_t* vo, int64_t ks,
+                    int64_t vs, int64_t cs) {
+  int64_t t, h, d;
+  for (t = 0; t < T; ++t) {
+    int64_t slot = slots[t], b, o;
+    if (slot < 0 || slot >= num_blocks * block_size) continue;
+    b = slot / block_size;
+    o = slot % block_size;
+    for (h = 0; h < H; ++h)
+      for (d = 0; d < D; ++d) {
+        int64_t src = b * cs + (o * H + h) * D + d;
+        float kd = (float)oracle_e4m3_decode(kc[src]);
+        float vd = (float)oracle_e4m3_decode(vc[src]);
+        ko[t * ks + h * D + d] = oracle_f32_to_bf16(kd * k_scale);
+        vo[t * vs + h * D + d] = oracle_f32_to_bf16(vd * v_scale);
+      }
+  }
+}
+
 /* ------------------------------------------------ C8: online KV scale calibration */
 
 /* One layer's calibrator, modelled step by step from [calib] and [staging]:

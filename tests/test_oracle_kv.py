@@ -179,3 +179,46 @@ def test_calibration_declined_batch_keeps_provisional_scale(orc):
             orc.kv_write(b.k, b.v, kc2, vc2, b.slots, len(b.slots), H, D, BS,
                          info["k_scale"], info["v_scale"], H * D, H * D, cs)
     assert np.array_equal(kc, kc2) and np.array_equal(vc, vc2)
+
+
+def test_kv_read_matches_torch_decode_and_round_trips(orc):
+    """bf16(fp32(dec(code)) * scale): decode by torch's float8 type, an fp32 multiply and
+    torch's own round-to-nearest-even bf16 conversion must give the oracle's bits; and
+    reading back what the writer stored stays within half an E4M3 step of the input."""
+    import torch
+    rng = np.random.default_rng(8)
+    t, nblk = 40, 8
+    e = H * D
+    k = synth.to_bf16_bits(rng.normal(0, 3, size=(t, e)))
+    v = synth.to_bf16_bits(rng.normal(0, 3, size=(t, e)))
+    slots = rng.permutation(nblk * BS)[:t].astype(np.int64)
+    slots[3] = -1
+    kc = np.zeros(nblk * BS * e, dtype=np.uint8)
+    vc = np.zeros_like(kc)
+    # per-tensor scales with headroom over the amax, so no value saturates
+    ks = float(np.float32(orc.amax(k)) * np.float32(1.25) / np.float32(448))
+    vs = float(np.float32(orc.amax(v)) * np.float32(1.5) / np.float32(448))
+    orc.kv_write(k, v, kc, vc, slots, t, H, D, BS, ks, vs, e, e, BS * e)
+    ko = np.full((t, e), 0x1234, dtype=np.uint16)
+    vo = np.full((t, e), 0x1234, dtype=np.uint16)
+    orc.kv_read(kc, vc, slots, H, D, BS, nblk, ks, vs, ko, vo, e, e, BS * e)
+    assert np.all(ko[3] == 0x1234) and np.all(vo[3] == 0x1234)
+    for pool, sc, out in ((kc, ks, ko), (vc, vs, vo)):
+        rows = []
+        for s_ in slots:
+            if s_ < 0:
+                rows.append(np.zeros(e, dtype=np.uint8))
+                continue
+            b, o = divmod(int(s_), BS)
+            rows.append(pool[b * BS * e + o * e: b * BS * e + (o + 1) * e])
+        codes = torch.from_numpy(np.stack(rows)).view(torch.float8_e4m3fn).to(torch.float32)
+        want = (codes * torch.tensor(sc, dtype=torch.float32)).to(torch.bfloat16)
+        want = want.view(torch.int16).numpy().view(np.uint16)
+        live = slots >= 0
+        assert np.array_equal(out[live], want[live])
+    live = slots >= 0
+    for src, out, sc in ((k, ko, ks), (v, vo, vs)):
+        x = synth.bf16_bits_to_f32(src).astype(np.float64)[live]
+        back = synth.bf16_bits_to_f32(out).astype(np.float64)[live]
+        # half an E4M3 step (2^-4 relative, 2^-10 * scale absolute) plus the bf16 rounding
+        assert np.all(np.abs(back - x) <= (2.0 ** -4 + 2.0 ** -8) * np.abs(x) + 2.0 ** -10 * sc)
