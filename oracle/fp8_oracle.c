@@ -308,10 +308,12 @@ void oracle_kv_write(const uint16_t* kx, const uint16_t* vx, uint8_t* kc, uint8_
 
 /* ------------------------------------------------------ paged KV read (dequantize) */
 
-/* bf16 bit pattern of a binary32, round to nearest even; NaN maps to the quiet 0x7FC0. */
+/* bf16 bit pattern of a binary32, round to nearest even; every NaN maps to the one quiet
+ * NaN 0x7FC0 (the pages never store a NaN code, so its read-back is only required to be a
+ * NaN; one fixed pattern keeps the result byte-comparable). */
 static uint16_t oracle_f32_to_bf16(float f) {
   uint32_t b = f32_bits(f);
-  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)(((b >> 16) & 0x8000u) | 0x7FC0u);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
   b += 0x7FFFu + ((b >> 16) & 1u);
   return (uint16_t)(b >> 16);
 }

@@ -222,3 +222,26 @@ def test_kv_read_matches_torch_decode_and_round_trips(orc):
         back = synth.bf16_bits_to_f32(out).astype(np.float64)[live]
         # half an E4M3 step (2^-4 relative, 2^-10 * scale absolute) plus the bf16 rounding
         assert np.all(np.abs(back - x) <= (2.0 ** -4 + 2.0 ** -8) * np.abs(x) + 2.0 ** -10 * sc)
+
+
+def test_kv_read_every_code(orc):
+    """Every one of the 256 codes read back at several scales: the finite ones equal torch's
+    float8 decode, one fp32 multiply and its bf16 rounding; the two NaN codes read as the
+    quiet NaN 0x7FC0; +-0 keep their sign."""
+    import torch
+    e, bs = 256, 1
+    codes = np.arange(256, dtype=np.uint8)
+    for sc in (1.0, 0.0234375, 2.0 ** -64, 2.0 ** 64, 3.0e-5, 1.7e9):
+        kc = codes.copy()
+        vc = codes[::-1].copy()
+        ko = np.zeros((1, e), dtype=np.uint16)
+        vo = np.zeros((1, e), dtype=np.uint16)
+        orc.kv_read(kc, vc, np.zeros(1, dtype=np.int64), 1, e, bs, 1, sc, sc, ko, vo, e, e, e)
+        for pool, out in ((kc, ko[0]), (vc, vo[0])):
+            dec = torch.from_numpy(pool).view(torch.float8_e4m3fn).to(torch.float32)
+            want = (dec * torch.tensor(sc, dtype=torch.float32)).to(torch.bfloat16)
+            want = want.view(torch.int16).numpy().view(np.uint16)
+            nan = (pool & 0x7F) == 0x7F
+            assert np.array_equal(out[~nan], want[~nan])
+            assert np.all(out[nan] == 0x7FC0)
+        assert ko[0, 0x00] == 0x0000 and ko[0, 0x80] == 0x8000
