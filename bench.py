@@ -70,6 +70,10 @@ def kv_write_bytes(t, e=KV_H * KV_D):
     return t * (2 * e * 2 + 2 * e + 8)
 
 
+def kv_read_bytes(t, e=KV_H * KV_D):
+    return t * (2 * e + 2 * e * 2 + 8)
+
+
 def kv_amax_bytes(t, e=KV_H * KV_D):
     return 2 * t * e * 2
 
@@ -372,21 +376,25 @@ def main():
     if "kv" in only:
         full = synth.kv_full_pool()
         t = len(full.slots)
-        per = kv_write_bytes(t) + KV_NB * KV_BS * e * 2
+        per = kv_write_bytes(t) + KV_NB * KV_BS * e * 2 + 2 * t * e * 2
         nset = rotation_sets(per)
         kd = bf16_dev(torch, full.k)
         vd = bf16_dev(torch, full.v)
         sd = torch.from_numpy(full.slots).cuda()
         bufs = [(kd.clone(), vd.clone(), sd.clone(), torch.zeros_like(kc), torch.zeros_like(vc),
-                 torch.zeros(2, dtype=torch.float32, device="cuda")) for _ in range(nset)]
+                 torch.zeros(2, dtype=torch.float32, device="cuda"), torch.empty_like(kd),
+                 torch.empty_like(vd)) for _ in range(nset)]
         ks_, vs_ = 3.0 * 20.0 / 448.0, 3.0 * 20.0 / 448.0
         wl = [(lambda b=b: fq.fp8_kv_write(b[0], b[1], b[3], b[4], b[2], KV_H, KV_D, KV_BS,
                                            ks_, vs_)) for b in bufs]
         al = [(lambda b=b: fq.fp8_kv_amax(b[0], b[1], b[5])) for b in bufs]
-        for f in wl + al:
+        rl = [(lambda b=b: fq.fp8_kv_read(b[3], b[4], b[2], KV_H, KV_D, KV_BS, ks_, vs_,
+                                          k_out=b[6], v_out=b[7])) for b in bufs]
+        for f in wl + al + rl:
             f()
         for name, launches, b in (("kv_write_full_pool", wl, kv_write_bytes(t)),
-                                  ("kv_amax_full_pool", al, kv_amax_bytes(t))):
+                                  ("kv_amax_full_pool", al, kv_amax_bytes(t)),
+                                  ("kv_read_full_pool", rl, kv_read_bytes(t))):
             mean_us, med_us = timer.kernel_us(launches, args.iters)
             kernels[f"{name}_t{t}"] = dict(
                 us=round(mean_us, 3), us_median=round(med_us, 3),

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     fp8_e4m3_encode,
     fp8_group_quant,
     fp8_kv_amax,
+    fp8_kv_read,
     fp8_kv_write,
     fp8_quant_w8a8_gemm_grouped,
     load,

@@ -21,7 +21,7 @@ FP8Q_CALIB_STAGE, FP8Q_CALIB_DECLINE, FP8Q_CALIB_FREEZE, FP8Q_CALIB_FROZEN = 0, 
 # Every symbol include/fp8q.h declares.
 EXPORTS = (
     "fp8q_strerror", "fp8q_version", "fp8q_time_next_launch", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
-    "w8a8_block_gemm", "w8a8_block_gemm_grouped", "fp8_quant_w8a8_gemm_grouped", "fp8_kv_write", "fp8_kv_amax", "fp8q_kv_calib_create",
+    "w8a8_block_gemm", "w8a8_block_gemm_grouped", "fp8_quant_w8a8_gemm_grouped", "fp8_kv_write", "fp8_kv_read", "fp8_kv_amax", "fp8q_kv_calib_create",
     "fp8q_kv_calib_observe", "fp8q_kv_calib_decide", "fp8q_kv_calib_scales",
     "fp8q_kv_calib_get_info", "fp8q_kv_calib_destroy",
 )
@@ -87,6 +87,8 @@ def load() -> ctypes.CDLL:
                                                        I32, I32, P]),
         "fp8_kv_write": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, I64, F32, F32,
                                         I32, I32, I64, P]),
+        "fp8_kv_read": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, I64, F32, F32, P, P,
+                                       I32, I32, I64, P]),
         "fp8_kv_amax": (ctypes.c_int, [P, P, I64, P, P]),
         "fp8q_kv_calib_create": (ctypes.c_int, [I32, F32, ctypes.POINTER(P)]),
         "fp8q_kv_calib_observe": (ctypes.c_int, [P, P, P, I32, I32, I32,
@@ -290,6 +292,40 @@ def fp8_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
                              value_stride, cache_stride,
                              current_stream(k.device) if stream is None else stream)
     check("fp8_kv_write", st)
+
+
+def fp8_kv_read(k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: torch.Tensor,
+                num_kv_heads: int, head_dim: int, block_size: int, k_scale: float,
+                v_scale: float, k_out: torch.Tensor | None = None,
+                v_out: torch.Tensor | None = None, out_key_stride: int | None = None,
+                out_value_stride: int | None = None, cache_stride: int | None = None,
+                num_tokens: int | None = None, stream: int | None = None):
+    """Dequantizing gather of paged E4M3 K/V back to bf16 rows (k_out, v_out); rows of
+    tokens whose slot is out of range are left as they were (zeros when allocated here)."""
+    e = num_kv_heads * head_dim
+    t = slot_mapping.numel() if num_tokens is None else num_tokens
+    out_key_stride = e if out_key_stride is None else out_key_stride
+    out_value_stride = e if out_value_stride is None else out_value_stride
+    cache_stride = block_size * e if cache_stride is None else cache_stride
+    if k_cache.numel() != v_cache.numel() or k_cache.numel() % cache_stride:
+        raise ValueError("pools must be equal and a whole number of blocks")
+    num_blocks = k_cache.numel() // cache_stride
+    if k_out is None:
+        k_out = torch.zeros((t, out_key_stride), dtype=torch.bfloat16, device=k_cache.device)
+    if v_out is None:
+        v_out = torch.zeros((t, out_value_stride), dtype=torch.bfloat16, device=k_cache.device)
+    for name, dst, stride in (("k_out", k_out, out_key_stride),
+                              ("v_out", v_out, out_value_stride)):
+        if t > 0 and dst.numel() < (t - 1) * stride + e:
+            raise ValueError(f"{name} is smaller than its rows")
+    st = load().fp8_kv_read(_dev(k_cache, "k_cache", _U8), _dev(v_cache, "v_cache", _U8),
+                            _dev(slot_mapping, "slot_mapping", torch.int64), t, num_kv_heads,
+                            head_dim, block_size, num_blocks, k_scale, v_scale,
+                            _dev(k_out, "k_out", _BF16, False), _dev(v_out, "v_out", _BF16, False),
+                            out_key_stride, out_value_stride, cache_stride,
+                            current_stream(k_cache.device) if stream is None else stream)
+    check("fp8_kv_read", st)
+    return k_out, v_out
 
 
 def fp8_kv_amax(k: torch.Tensor, v: torch.Tensor, amax2: torch.Tensor,

@@ -14,10 +14,13 @@
 // (lazy allocation at window capacity; decline when elements per token change or the
 // window would overflow), ::replay_and_release (packed strides), ::release, copy_rows.
 //
-// Difference from the pages: the pages synchronize the stream on every observe inside
+// Differences from the pages: the pages synchronize the stream on every observe inside
 // the window to read the batch's absmax back.  Here the running maximum is
 // max-accumulated on the device across the whole window and read once, at the freeze;
-// max is order-free, so the frozen scales are bit-identical.
+// max is order-free, so the frozen scales are bit-identical.  The pages replay one write
+// per staged batch, in order; here the replay is one write of all staged tokens after
+// dropping every token a later staged token overwrites (last writer wins either way, so
+// the pool bytes are the same).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -54,6 +57,7 @@ struct fp8q_kv_calib {
   uint16_t* sk = nullptr;
   uint16_t* sv = nullptr;
   int64_t* sslots = nullptr;
+  int64_t* rslots = nullptr;  // replay slots: sslots with overwritten tokens set to -1
   int64_t capacity = 0, elems = 0, used = 0;
   std::vector<std::pair<int64_t, int32_t>> batches;  // (offset tokens, tokens)
 };
@@ -72,8 +76,9 @@ void release_staging(fp8q_kv_calib* c) {
   if (c->sk) (void)hipFree(c->sk);
   if (c->sv) (void)hipFree(c->sv);
   if (c->sslots) (void)hipFree(c->sslots);
+  if (c->rslots) (void)hipFree(c->rslots);
   c->sk = c->sv = nullptr;
-  c->sslots = nullptr;
+  c->sslots = c->rslots = nullptr;
   c->capacity = c->elems = c->used = 0;
   c->batches.clear();
 }
@@ -151,7 +156,8 @@ extern "C" int fp8q_kv_calib_observe(fp8q_kv_calib* c, const uint16_t* k, const 
     const size_t rows = size_t(c->window);
     if (hipMalloc(&c->sk, rows * size_t(e) * 2) != hipSuccess ||
         hipMalloc(&c->sv, rows * size_t(e) * 2) != hipSuccess ||
-        hipMalloc(&c->sslots, rows * sizeof(int64_t)) != hipSuccess) {
+        hipMalloc(&c->sslots, rows * sizeof(int64_t)) != hipSuccess ||
+        hipMalloc(&c->rslots, rows * sizeof(int64_t)) != hipSuccess) {
       release_staging(c);
       return FP8Q_EHIP;
     }
@@ -192,12 +198,16 @@ extern "C" int fp8q_kv_calib_observe(fp8q_kv_calib* c, const uint16_t* k, const 
   c->k_scale = freeze_scale(c->k_amax, c->headroom);
   c->v_scale = freeze_scale(c->v_amax, c->headroom);
   c->frozen = true;
-  for (const auto& b : c->batches) {
-    // staged rows are packed: one row of `elems` per token, whatever the live strides
-    st = fp8q::kv_write(c->sk + b.first * c->elems, c->sv + b.first * c->elems, t->k_pool,
-                        t->v_pool, c->sslots + b.first, b.second, 1, int32_t(c->elems),
-                        t->block_size, t->num_blocks, c->k_scale, c->v_scale, c->elems,
-                        c->elems, t->cache_stride, stream);
+  if (c->used > 0) {
+    // One write of every staged token, in place of one write per staged batch in order:
+    // tokens that a later staged token overwrites are dropped first, so every slot gets
+    // the bytes of its last staged writer -- what the ordered replay leaves.  Staged rows
+    // are packed: one row of `elems` per token, whatever the live strides.
+    st = fp8q::kv_last_writer_slots(c->sslots, c->rslots, int32_t(c->used), stream);
+    if (st != FP8Q_OK) return st;
+    st = fp8q::kv_write(c->sk, c->sv, t->k_pool, t->v_pool, c->rslots, int32_t(c->used), 1,
+                        int32_t(c->elems), t->block_size, t->num_blocks, c->k_scale,
+                        c->v_scale, c->elems, c->elems, t->cache_stride, stream);
     if (st != FP8Q_OK) return st;
   }
   c->replayed = c->used;

@@ -42,6 +42,33 @@ __device__ __forceinline__ uint2 quant8(uint4 w, float s, float y) {
   return r;
 }
 
+// ----------------------------------------------------------------- E4M3 decoding
+// Two E4M3 codes (bytes 0,1 of w when kHigh is false, bytes 2,3 when true) -> binary32,
+// exact (every E4M3 value, subnormals included, is a normal binary32).
+template <bool kHigh>
+__device__ __forceinline__ float2 e4m3x2_to_f32(uint32_t w) {
+  const auto r = __builtin_amdgcn_cvt_pk_f32_fp8(int(w), kHigh);
+  return make_float2(r[0], r[1]);
+}
+
+// binary32 -> bf16 bits, round to nearest even by integer carry (exact for every finite
+// value whose rounding stays finite); any NaN becomes the quiet NaN 0x7FC0.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return f != f ? 0x7FC0u : r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Four E4M3 codes in w times a scale -> four bf16 packed in two 32-bit words.
+__device__ __forceinline__ uint2 dequant4(uint32_t w, float s) {
+  const float2 a = e4m3x2_to_f32<false>(w), b = e4m3x2_to_f32<true>(w);
+  return make_uint2(pack_bf16x2(a.x * s, a.y * s), pack_bf16x2(b.x * s, b.y * s));
+}
+
 // 16-byte load with the non-temporal (streaming) hint.
 __device__ __forceinline__ uint4 load16_nt(const uint4* p) {
   typedef unsigned v4u __attribute__((ext_vector_type(4)));

@@ -1,5 +1,5 @@
-// fp8q_kv.hip -- paged FP8 KV-cache write at a per-tensor scale, and the K/V absolute
-// maximum that feeds the online calibration.
+// fp8q_kv.hip -- paged FP8 KV-cache write at a per-tensor scale, the K/V absolute
+// maximum that feeds the online calibration, and the dequantizing read of a history.
 //
 // staging.rs page: Fp8KvWriteTarget (strides in elements, pool stride = block_size *
 // heads * head_dim per block) and replay_and_release (the write's argument list); module
@@ -203,6 +203,124 @@ __global__ __launch_bounds__(kKvBlock) void kv_write_scalar_kernel(
   }
 }
 
+// ------------------------------------------------------------------ dequantizing read
+// Gather of a paged history back to bf16 at one scale per tensor: every element is
+// bf16_rne(fp32(decode(code)) * scale).  Work item = one 16-code chunk of one token's K or
+// V row: item i -> token i / (2 * lpt), then K chunks, then V chunks, so consecutive lanes
+// read consecutive 16-byte pieces of one pool row and write consecutive 32-byte pieces of
+// one output row.  A lane takes kReadUnroll items a pass, all loads issued before any
+// conversion.  Tokens whose slot is out of range read pool row 0 (in bounds) and store
+// nothing.
+#ifndef FP8Q_KV_READ_UNROLL
+#define FP8Q_KV_READ_UNROLL 1
+#endif
+#ifndef FP8Q_KV_READ_NT_STORE
+#define FP8Q_KV_READ_NT_STORE 1  // bf16 rows written with the non-temporal hint
+#endif
+constexpr int kReadUnroll = FP8Q_KV_READ_UNROLL;
+
+__device__ __forceinline__ void store32_bf16(uint4 a, uint4 b, uint16_t* p) {
+#if FP8Q_KV_READ_NT_STORE
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(v4u{a.x, a.y, a.z, a.w}, reinterpret_cast<v4u*>(p));
+  __builtin_nontemporal_store(v4u{b.x, b.y, b.z, b.w}, reinterpret_cast<v4u*>(p) + 1);
+#else
+  reinterpret_cast<uint4*>(p)[0] = a;
+  reinterpret_cast<uint4*>(p)[1] = b;
+#endif
+}
+
+// Idx is uint32_t when every item index and slot fits in 31 bits, else uint64_t.
+template <typename Idx>
+__global__ __launch_bounds__(kKvBlock) void kv_read_vec_kernel(
+    const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+    const int64_t* __restrict__ slots, Idx items, uint32_t lpt, int64_t cs, uint32_t bs,
+    int64_t nslots, float k_scale, float v_scale, uint16_t* __restrict__ ko,
+    uint16_t* __restrict__ vo, int64_t kos, int64_t vos) {
+  const Idx nthreads = Idx(gridDim.x) * kKvBlock;
+  const Idx per_tok = Idx(2) * lpt;
+  const int64_t e = int64_t(16) * lpt;
+  for (Idx i0 = Idx(blockIdx.x) * kKvBlock + threadIdx.x; i0 < items;
+       i0 += nthreads * kReadUnroll) {
+    Idx tok[kReadUnroll], r[kReadUnroll];
+    int64_t slot[kReadUnroll];
+    // every slot load first (clamped items: in bounds), then every pool load
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) {
+      const Idx i = i0 + u * nthreads;
+      const Idx il = i < items ? i : items - 1;
+      tok[u] = il / per_tok;
+      r[u] = il - tok[u] * per_tok;
+      slot[u] = slots[tok[u]];
+    }
+    uint4 w[kReadUnroll];
+    bool ok[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) {
+      ok[u] = i0 + u * nthreads < items && slot[u] >= 0 && slot[u] < nslots;
+      const Idx su = ok[u] ? Idx(slot[u]) : Idx(0);  // invalid: row 0 of block 0
+      const Idx blk = su / bs;
+      const Idx off = su - blk * bs;
+      const bool is_v = r[u] >= lpt;
+      const int64_t chunk = int64_t(is_v ? r[u] - lpt : r[u]);
+      w[u] = *reinterpret_cast<const uint4*>((is_v ? vc : kc) + int64_t(blk) * cs +
+                                             int64_t(off) * e + chunk * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) {
+      const bool is_v = r[u] >= lpt;
+      const float s = is_v ? v_scale : k_scale;
+      const uint2 d0 = dequant4(w[u].x, s), d1 = dequant4(w[u].y, s);
+      const uint2 d2 = dequant4(w[u].z, s), d3 = dequant4(w[u].w, s);
+      const int64_t chunk = int64_t(is_v ? r[u] - lpt : r[u]);
+      uint16_t* dst = (is_v ? vo + int64_t(tok[u]) * vos : ko + int64_t(tok[u]) * kos) +
+                      chunk * 16;
+      if (ok[u])
+        store32_bf16(make_uint4(d0.x, d0.y, d1.x, d1.y), make_uint4(d2.x, d2.y, d3.x, d3.y),
+                     dst);
+    }
+  }
+}
+
+// Element-wise read for any geometry and alignment; one wave per token row.
+__global__ __launch_bounds__(kKvBlock) void kv_read_scalar_kernel(
+    const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+    const int64_t* __restrict__ slots, int64_t num_tokens, int e, int64_t cs, int bs,
+    int64_t nslots, float k_scale, float v_scale, uint16_t* __restrict__ ko,
+    uint16_t* __restrict__ vo, int64_t kos, int64_t vos) {
+  for (int64_t t = int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.y; t < num_tokens;
+       t += int64_t(gridDim.x) * kRowsPerBlock) {
+    int64_t blk, off;
+    if (!slot_to_block(uniform(slots[t]), nslots, bs, &blk, &off)) continue;
+    const int64_t src = blk * cs + off * e;
+    for (int c = threadIdx.x; c < e; c += 64) {
+      const float kd = e4m3x2_to_f32<false>(kc[src + c]).x;
+      const float vd = e4m3x2_to_f32<false>(vc[src + c]).x;
+      ko[t * kos + c] = uint16_t(f32_to_bf16_bits(kd * k_scale));
+      vo[t * vos + c] = uint16_t(f32_to_bf16_bits(vd * v_scale));
+    }
+  }
+}
+
+// ------------------------------------------------------------ last-writer replay mask
+// out[i] = -1 for every token i that a later token j > i of the same list writes over
+// (same slot); out must already hold a copy of slots.  Block (bi, bj) is one wave that
+// compares the 64 tokens of tile bi against the 64 of tile bj >= bi; every pair (i, j > i)
+// is seen by exactly one block.  Blocks only store -1 into out and never read it, so their
+// order does not matter.
+__global__ __launch_bounds__(64) void kv_mark_superseded_kernel(
+    const int64_t* __restrict__ slots, int64_t* __restrict__ out, int n) {
+  const int bi = blockIdx.x, bj = blockIdx.y;
+  if (bj < bi) return;
+  const int i = bi * 64 + int(threadIdx.x);
+  const int64_t si = slots[i < n ? i : n - 1];
+  const int j0 = bj * 64;
+  const int jn = n - j0 < 64 ? n - j0 : 64;
+  bool superseded = false;
+  for (int jj = 0; jj < jn; ++jj) superseded |= (j0 + jj > i) && (slots[j0 + jj] == si);
+  if (i < n && superseded) out[i] = -1;
+}
+
 // Folds a workgroup's maximum into amax2[which]: one LDS reduction, then a single atomic,
 // skipped when the value already there is at least as large (it only grows).
 __device__ __forceinline__ void fold_block_max(float m, float* amax2, int which) {
@@ -323,6 +441,55 @@ int kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t* v_
   return launch_status();
 }
 
+int kv_last_writer_slots(const int64_t* slots, int64_t* out, int32_t n, hipStream_t stream) {
+  if (n <= 0) return FP8Q_OK;
+  if (n > 65535 * 64) return FP8Q_EINVAL;
+  if (hipMemcpyAsync(out, slots, size_t(n) * sizeof(int64_t), hipMemcpyDeviceToDevice,
+                     stream) != hipSuccess)
+    return FP8Q_EHIP;
+  const unsigned tiles = unsigned((n + 63) / 64);
+  launch(kv_mark_superseded_kernel, dim3(tiles, tiles), dim3(64), 0, stream, slots, out, n);
+  return launch_status();
+}
+
+static int kv_read(const uint8_t* k_cache, const uint8_t* v_cache, const int64_t* slot_mapping,
+            int32_t num_tokens, int32_t heads, int32_t head_dim, int32_t block_size,
+            int64_t num_blocks, float k_scale, float v_scale, uint16_t* k_out,
+            uint16_t* v_out, int64_t out_key_stride, int64_t out_value_stride,
+            int64_t cache_stride, hipStream_t stream) {
+  const int64_t e = int64_t(heads) * head_dim;
+  const int64_t nslots = num_blocks * block_size;
+  const bool vec = e % 16 == 0 && out_key_stride % 8 == 0 && out_value_stride % 8 == 0 &&
+                   cache_stride % 16 == 0 && aligned(k_cache, 16) && aligned(v_cache, 16) &&
+                   aligned(k_out, 16) && aligned(v_out, 16) && e / 16 <= 0x7FFFFFFF;
+  if (vec) {
+    const int64_t items = int64_t(num_tokens) * 2 * (e / 16);
+    const int64_t per_block = int64_t(kKvBlock) * kReadUnroll;
+    const int64_t blocks = clamp_grid((items + per_block - 1) / per_block);
+    // 32-bit indices when no item index the loop forms (< 2 * items + per_block) and no
+    // slot can wrap
+    if (items < (int64_t(1) << 31) - per_block && nslots <= 0x7FFFFFFF)
+      launch(kv_read_vec_kernel<uint32_t>, dim3(unsigned(blocks)), dim3(kKvBlock), 0, stream,
+             k_cache, v_cache, slot_mapping, uint32_t(items), uint32_t(e / 16), cache_stride,
+             uint32_t(block_size), nslots, k_scale, v_scale, k_out, v_out, out_key_stride,
+             out_value_stride);
+    else
+      launch(kv_read_vec_kernel<uint64_t>, dim3(unsigned(blocks)), dim3(kKvBlock), 0, stream,
+             k_cache, v_cache, slot_mapping, uint64_t(items), uint32_t(e / 16), cache_stride,
+             uint32_t(block_size), nslots, k_scale, v_scale, k_out, v_out, out_key_stride,
+             out_value_stride);
+    return launch_status();
+  }
+  if (e > 0x7FFFFFFF) return FP8Q_EINVAL;
+  const int64_t blocks =
+      clamp_grid((int64_t(num_tokens) + kRowsPerBlock - 1) / kRowsPerBlock);
+  launch(kv_read_scalar_kernel, dim3(unsigned(blocks)), dim3(64, kRowsPerBlock), 0, stream,
+         k_cache, v_cache, slot_mapping, int64_t(num_tokens), int(e), cache_stride,
+         block_size, nslots, k_scale, v_scale, k_out, v_out, out_key_stride,
+         out_value_stride);
+  return launch_status();
+}
+
 }  // namespace fp8q
 
 using namespace fp8q;
@@ -351,4 +518,23 @@ extern "C" int fp8_kv_amax(const uint16_t* k, const uint16_t* v, int64_t n_elems
   if (!k || !v || !amax2) return FP8Q_ENULL;
   if (!aligned(amax2, 4)) return FP8Q_EALIGN;
   return kv_amax_rows(k, v, 1, n_elems, n_elems, n_elems, amax2, stream);
+}
+
+extern "C" int fp8_kv_read(const uint8_t* k_cache, const uint8_t* v_cache,
+                           const int64_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int64_t num_blocks, float k_scale, float v_scale, uint16_t* k_out,
+                           uint16_t* v_out, int32_t out_key_stride, int32_t out_value_stride,
+                           int64_t cache_stride, hipStream_t stream) {
+  const int rc = kv_write_check(num_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                                k_scale, v_scale, out_key_stride, out_value_stride,
+                                cache_stride);
+  if (rc != FP8Q_OK) return rc;
+  if (num_tokens == 0) return FP8Q_OK;
+  if (!k_cache || !v_cache || !slot_mapping || !k_out || !v_out) return FP8Q_ENULL;
+  if (!aligned(slot_mapping, 8) || !aligned(k_out, 2) || !aligned(v_out, 2))
+    return FP8Q_EALIGN;
+  return kv_read(k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                 block_size, num_blocks, k_scale, v_scale, k_out, v_out, out_key_stride,
+                 out_value_stride, cache_stride, stream);
 }

@@ -33,6 +33,11 @@ int kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t* v_
              int64_t key_stride, int64_t value_stride, int64_t cache_stride,
              hipStream_t stream);
 
+// out = slots with -1 in place of every token that a later token of the list overwrites
+// (the same slot); the survivors are distinct, so one kv_write of the whole list leaves the
+// pools exactly as writing the list's tokens one after another would.
+int kv_last_writer_slots(const int64_t* slots, int64_t* out, int32_t n, hipStream_t stream);
+
 int kv_amax_rows(const uint16_t* k, const uint16_t* v, int64_t rows, int64_t row_elems,
                  int64_t key_stride, int64_t value_stride, float* amax2, hipStream_t stream);
 

@@ -179,6 +179,35 @@ int fp8_kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t
                  float v_scale, int32_t key_stride, int32_t value_stride,
                  int64_t cache_stride, hipStream_t stream);
 
+/* ------------------------------------------------------ paged FP8 KV read (dequant)
+ * [staging] module doc: every token of a sequence's history is read back at the one
+ * per-tensor scale the layer holds (which is why early tokens written at the provisional
+ * scale must be rewritten at the frozen one); the write above defines the pool layout.
+ *
+ * For each token t < num_tokens with 0 <= slot < num_blocks * block_size (slot =
+ * slot_mapping[t]; output rows of other tokens are left untouched):
+ *   b = slot / block_size, o = slot % block_size, for all h < H, d < D:
+ *   k_out[t * out_key_stride + h*D + d] =
+ *       bf16_rne(fp32(E4M3 value of k_cache[b * cache_stride + (o * H + h) * D + d]) * k_scale)
+ *   v_out[... same ...] likewise with v_cache and v_scale
+ * The product is one binary32 multiplication (round to nearest even), then rounded to
+ * bf16 to nearest even; the NaN codes 0x7F / 0xFF read as the quiet NaN 0x7FC0.
+ *
+ *   k_cache, v_cache   device uint8 pools of num_blocks * cache_stride bytes each
+ *   slot_mapping       device int64 [num_tokens]
+ *   k_out, v_out       device bf16 rows of out_key_stride / out_value_stride elements
+ *   num_tokens >= 0 (0 is a no-op); num_kv_heads, head_dim, block_size, num_blocks > 0;
+ *   out strides >= H*D; cache_stride >= block_size*H*D; scales in [2^-64, 2^64].
+ * The vector path needs H*D a multiple of 16, 16-byte aligned pools and outputs, output
+ * strides multiples of 8 and cache_stride a multiple of 16; anything else takes an
+ * element-wise path with the same results.
+ * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EALIGN, FP8Q_ELAUNCH. */
+int fp8_kv_read(const uint8_t* k_cache, const uint8_t* v_cache, const int64_t* slot_mapping,
+                int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int64_t num_blocks, float k_scale, float v_scale, uint16_t* k_out,
+                uint16_t* v_out, int32_t out_key_stride, int32_t out_value_stride,
+                int64_t cache_stride, hipStream_t stream);
+
 /* ------------------------------------------------------------- KV absolute max
  * [calib] Fp8KvCalibration::absmax: max |K| and max |V| of a batch, max-accumulated into
  * a device float[2] that the caller zeroes once (so a window's running max can stay on
@@ -199,8 +228,9 @@ int fp8_kv_amax(const uint16_t* k, const uint16_t* v, int64_t n_elems, float* am
  * the batch (bf16 rows + slots) is copied into packed staging; the caller then writes
  * it at the provisional scale 2.0.  The observe whose token count reaches the window
  * freezes scale = (max(amax, 1e-10) * headroom) / 448 for K and V over every observed
- * token including its own batch, replays the staged batches in observation order at the
- * frozen scales into the target pools, and frees the staging; the caller then writes
+ * token including its own batch, replays the staged batches at the frozen scales into
+ * the target pools (one write of every staged token whose slot no later staged token
+ * writes, which leaves the bytes an in-order replay leaves), and frees the staging; the caller then writes
  * that batch at the frozen scales.  Later observes do nothing.  A batch whose heads x
  * head_dim differ from the first staged batch is not staged (it keeps the provisional
  * scale).  The window is clamped to 4096 tokens and headroom to >= 1.
@@ -251,7 +281,7 @@ int fp8q_kv_calib_create(int32_t window_tokens, float headroom, fp8q_kv_calib** 
 /* Fold one batch in (see above).  k, v: device bf16 [num_tokens] rows at the target's
  * key/value strides.  Enqueues work on `stream`; synchronizes `stream` only at the freeze
  * (to read the 8-byte running maximum, and again before freeing the staging).  The
- * first staged batch allocates the staging (window * H * D * 2 * 2 + window * 8 bytes).
+ * first staged batch allocates the staging (window * H * D * 2 * 2 + window * 16 bytes).
  * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EHIP, FP8Q_ELAUNCH, FP8Q_ESTATE. */
 int fp8q_kv_calib_observe(fp8q_kv_calib* c, const uint16_t* k, const uint16_t* v,
                           int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,

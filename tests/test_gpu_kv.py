@@ -177,3 +177,123 @@ def test_calibration_reuse_inside_window_equals_single_pass():
         oracle.kv_write(b.k, b.v, kc2, vc2, b.slots, len(b.slots), H, D, BS, info["k_scale"],
                         info["v_scale"], E, E, CS)
     assert np.array_equal(kc, kc2) and np.array_equal(vc, vc2)
+
+
+def test_calibration_replay_with_heavy_slot_reuse_matches_oracle():
+    """Staged batches that keep rewriting a few dozen slots (plus padding and out-of-range
+    slots), over several 64-token tiles: the one-launch replay keeps each slot's last staged
+    writer, exactly as the oracle's in-order replay."""
+    rng = np.random.default_rng(5020)
+    batches = []
+    for i in range(40):
+        n = int(rng.integers(1, 65))
+        slots = rng.permutation(96)[:n].astype(np.int64) * 7 % (NB * BS)
+        if i % 5 == 0:
+            slots[0] = -1
+        if i % 7 == 3:
+            slots[-1] = NB * BS + 11
+        k = synth.to_bf16_bits(rng.normal(0, 3, size=(n, E)))
+        v = synth.to_bf16_bits(rng.normal(0, 3, size=(n, E)))
+        batches.append(synth.KvBatch(k=k, v=v, slots=slots))
+    window = sum(len(b.slots) for b in batches[:-1]) + 1  # the last batch crosses
+    kc, vc, info = _calibrate_on_gpu(batches, window)
+    kc_ref, vc_ref, ref = _calibrate_oracle(batches, window)
+    assert info["frozen"] == 1 and info["replayed_tokens"] == ref["replayed_tokens"] > 64
+    assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+
+
+# ------------------------------------------------------------------ dequantizing read
+
+
+def _read_both(kc, vc, slots, h, d, bs, nblk, ks, vs, kos, vos, cs, t, fill=0x1234,
+               offset=0):
+    """GPU read (through the C ABI) and oracle read of the same pools; the output rows start
+    as `fill` so rows of skipped tokens can be checked."""
+    ko = np.full(t * kos, fill, dtype=np.uint16)
+    vo = np.full(t * vos, fill, dtype=np.uint16)
+    kod = bf16_dev(np.concatenate([np.zeros(offset, np.uint16), ko]))[offset:]
+    vod = bf16_dev(np.concatenate([np.zeros(offset, np.uint16), vo]))[offset:]
+    fq.fp8_kv_read(torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV), i64_dev(slots),
+                   h, d, bs, ks, vs, k_out=kod, v_out=vod, out_key_stride=kos,
+                   out_value_stride=vos, cache_stride=cs, num_tokens=t)
+    oracle.kv_read(kc, vc, slots, h, d, bs, nblk, ks, vs, ko, vo, kos, vos, cs)
+    return host(kod), host(vod), ko, vo
+
+
+def test_read_full_pool_every_code_matches_oracle():
+    """The whole 2048-block pool (every byte value, NaN codes included) read back through a
+    permuted slot map with padding and out-of-range slots."""
+    rng = np.random.default_rng(77)
+    kc = rng.integers(0, 256, size=NB * CS, dtype=np.uint8)
+    vc = rng.integers(0, 256, size=NB * CS, dtype=np.uint8)
+    slots = rng.permutation(NB * BS).astype(np.int64)
+    slots[5] = -1
+    slots[-3] = NB * BS + 7
+    t = len(slots)
+    kg, vg, ko, vo = _read_both(kc, vc, slots, H, D, BS, NB, 0.0234375, 3.0e-3, E, E, CS, t)
+    assert np.array_equal(kg, ko) and np.array_equal(vg, vo)
+    assert np.all(kg[5 * E:6 * E] == 0x1234) and np.all(vg[(t - 3) * E:(t - 2) * E] == 0x1234)
+
+
+@pytest.mark.parametrize("t", [1, 2, 37, 129])
+def test_read_ragged_token_counts(t):
+    rng = np.random.default_rng(t)
+    nblk = 16
+    kc = rng.integers(0, 256, size=nblk * CS, dtype=np.uint8)
+    vc = rng.integers(0, 256, size=nblk * CS, dtype=np.uint8)
+    slots = rng.permutation(nblk * BS)[:t].astype(np.int64)
+    kg, vg, ko, vo = _read_both(kc, vc, slots, H, D, BS, nblk, 1.7e9, 2.0 ** -64, E, E, CS, t)
+    assert np.array_equal(kg, ko) and np.array_equal(vg, vo)
+
+
+def test_read_strided_outputs_and_padded_pool_stride():
+    rng = np.random.default_rng(4)
+    t, kos, vos, cs, nblk = 50, E + 64, E + 8, CS + 128, 64
+    kc = rng.integers(0, 256, size=nblk * cs, dtype=np.uint8)
+    vc = rng.integers(0, 256, size=nblk * cs, dtype=np.uint8)
+    slots = rng.permutation(nblk * BS)[:t].astype(np.int64)
+    kg, vg, ko, vo = _read_both(kc, vc, slots, H, D, BS, nblk, 0.3, 0.7, kos, vos, cs, t)
+    assert np.array_equal(kg, ko) and np.array_equal(vg, vo)
+
+
+@pytest.mark.parametrize("h,d,offset", [(3, 5, 0), (2, 64, 1), (1, 8, 3), (8, 128, 0)])
+def test_read_elementwise_and_wide_rows(h, d, offset):
+    """Odd geometry and misaligned outputs take the element-wise path; 8 x 128 rows take the
+    vector path with a token spanning several waves."""
+    rng = np.random.default_rng(h * d + offset)
+    e, t, bs, nblk = h * d, 37, 4, 16
+    cs = bs * e
+    kc = rng.integers(0, 256, size=nblk * cs, dtype=np.uint8)
+    vc = rng.integers(0, 256, size=nblk * cs, dtype=np.uint8)
+    slots = rng.permutation(nblk * bs)[:t].astype(np.int64)
+    slots[0] = -1
+    kg, vg, ko, vo = _read_both(kc, vc, slots, h, d, bs, nblk, 0.5, 3.0, e + 3 * (offset > 0),
+                                e + 3 * (offset > 0), cs, t, offset=offset)
+    assert np.array_equal(kg, ko) and np.array_equal(vg, vo)
+
+
+def test_write_then_read_round_trip_on_device():
+    """GPU write then GPU read at the same scales reproduces the oracle's write + read."""
+    b = synth.kv_full_pool()
+    t = len(b.slots)
+    kc, vc, kcd, vcd = _pools()
+    ks = float(np.float32(oracle.amax(b.k)) / np.float32(448))
+    vs = float(np.float32(oracle.amax(b.v)) / np.float32(448))
+    fq.fp8_kv_write(bf16_dev(b.k), bf16_dev(b.v), kcd, vcd, i64_dev(b.slots), H, D, BS, ks, vs)
+    kod, vod = fq.fp8_kv_read(kcd, vcd, i64_dev(b.slots), H, D, BS, ks, vs)
+    oracle.kv_write(b.k, b.v, kc, vc, b.slots, t, H, D, BS, ks, vs, E, E, CS)
+    ko = np.zeros((t, E), dtype=np.uint16)
+    vo = np.zeros((t, E), dtype=np.uint16)
+    oracle.kv_read(kc, vc, b.slots, H, D, BS, NB, ks, vs, ko, vo, E, E, CS)
+    assert np.array_equal(host(kod), ko) and np.array_equal(host(vod), vo)
+
+
+def test_read_argument_errors():
+    kcd = torch.zeros(NB * CS, dtype=torch.uint8, device=DEV)
+    s = i64_dev(np.zeros(4, dtype=np.int64))
+    with pytest.raises(fq.Fp8qError):
+        fq.fp8_kv_read(kcd, kcd, s, H, D, BS, 0.0, 1.0)
+    with pytest.raises(fq.Fp8qError):
+        fq.fp8_kv_read(kcd, kcd, s, H, D, BS, 1.0, float("nan"))
+    ko, vo = fq.fp8_kv_read(kcd, kcd, s, H, D, BS, 1.0, 1.0, num_tokens=0)
+    assert ko.shape == (0, E)
