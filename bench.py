@@ -451,15 +451,15 @@ def main():
 
 def profiled_traffic(name):
     """HBM bytes per launch from the committed rocprofv3 counter summary
-    (profiles/traffic.txt: '<kernel key> <bytes per launch> <source file> <sha256>'), if
-    it was taken on the current kernel source; else None."""
+    (profiles/traffic.txt: '<kernel key> <bytes per launch> <source files, comma-separated>
+    <sha256 of their contents>'), if it was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.txt")
     try:
         with open(path) as f:
             for line in f:
                 parts = line.split()
                 if len(parts) == 4 and parts[0] == name:
-                    if source_sha(parts[2]) == parts[3]:
+                    if sources_sha(parts[2].split(",")) == parts[3]:
                         return int(parts[1])
                     return None
     except OSError:
@@ -467,12 +467,15 @@ def profiled_traffic(name):
     return None
 
 
-def source_sha(rel):
-    try:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            return hashlib.sha256(f.read()).hexdigest()
-    except OSError:
-        return None
+def sources_sha(rels):
+    h = hashlib.sha256()
+    for rel in rels:
+        try:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        except OSError:
+            return None
+    return h.hexdigest()
 
 
 def cpu_baseline(synth, log):

@@ -205,55 +205,59 @@ __global__ __launch_bounds__(kKvBlock) void kv_write_scalar_kernel(
 
 // ------------------------------------------------------------------ dequantizing read
 // Gather of a paged history back to bf16 at one scale per tensor: every element is
-// bf16_rne(fp32(decode(code)) * scale).  Work item = one 16-code chunk of one token's K or
-// V row: item i -> token i / (2 * lpt), then K chunks, then V chunks, so consecutive lanes
-// read consecutive 16-byte pieces of one pool row and write consecutive 32-byte pieces of
-// one output row.  A lane takes kReadUnroll items a pass, all loads issued before any
-// conversion.  Tokens whose slot is out of range read pool row 0 (in bounds) and store
-// nothing.
+// bf16_rne(fp32(decode(code)) * scale).  Work item = the same 8 elements of one token's K
+// and V rows: item i -> token i / ipt (ipt = H*D/8 items per token), chunk i % ipt.  A lane
+// loads 8 K codes and 8 V codes and stores 16 bf16 bytes of each output row; consecutive
+// lanes take consecutive chunks, so every load instruction of a wave reads 512 contiguous
+// bytes of a pool row and every store writes 1 KB of an output row in whole 16-byte lanes
+// (no instruction leaves holes in a cache line).  A lane takes kReadUnroll items a pass,
+// all loads issued before any conversion.  Tokens whose slot is out of range read pool
+// row 0 (in bounds) and store nothing.
 #ifndef FP8Q_KV_READ_UNROLL
-#define FP8Q_KV_READ_UNROLL 1
+#define FP8Q_KV_READ_UNROLL 4
 #endif
 #ifndef FP8Q_KV_READ_NT_STORE
 #define FP8Q_KV_READ_NT_STORE 1  // bf16 rows written with the non-temporal hint
 #endif
 constexpr int kReadUnroll = FP8Q_KV_READ_UNROLL;
 
-__device__ __forceinline__ void store32_bf16(uint4 a, uint4 b, uint16_t* p) {
+__device__ __forceinline__ void store16_bf16(uint4 a, uint16_t* p) {
 #if FP8Q_KV_READ_NT_STORE
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
   __builtin_nontemporal_store(v4u{a.x, a.y, a.z, a.w}, reinterpret_cast<v4u*>(p));
-  __builtin_nontemporal_store(v4u{b.x, b.y, b.z, b.w}, reinterpret_cast<v4u*>(p) + 1);
 #else
-  reinterpret_cast<uint4*>(p)[0] = a;
-  reinterpret_cast<uint4*>(p)[1] = b;
+  *reinterpret_cast<uint4*>(p) = a;
 #endif
+}
+
+__device__ __forceinline__ uint4 dequant8(uint2 w, float s) {
+  const uint2 a = dequant4(w.x, s), b = dequant4(w.y, s);
+  return make_uint4(a.x, a.y, b.x, b.y);
 }
 
 // Idx is uint32_t when every item index and slot fits in 31 bits, else uint64_t.
 template <typename Idx>
 __global__ __launch_bounds__(kKvBlock) void kv_read_vec_kernel(
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
-    const int64_t* __restrict__ slots, Idx items, uint32_t lpt, int64_t cs, uint32_t bs,
+    const int64_t* __restrict__ slots, Idx items, uint32_t ipt, int64_t cs, uint32_t bs,
     int64_t nslots, float k_scale, float v_scale, uint16_t* __restrict__ ko,
     uint16_t* __restrict__ vo, int64_t kos, int64_t vos) {
   const Idx nthreads = Idx(gridDim.x) * kKvBlock;
-  const Idx per_tok = Idx(2) * lpt;
-  const int64_t e = int64_t(16) * lpt;
+  const int64_t e = int64_t(8) * ipt;
   for (Idx i0 = Idx(blockIdx.x) * kKvBlock + threadIdx.x; i0 < items;
        i0 += nthreads * kReadUnroll) {
-    Idx tok[kReadUnroll], r[kReadUnroll];
+    Idx tok[kReadUnroll], c[kReadUnroll];
     int64_t slot[kReadUnroll];
     // every slot load first (clamped items: in bounds), then every pool load
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u) {
       const Idx i = i0 + u * nthreads;
       const Idx il = i < items ? i : items - 1;
-      tok[u] = il / per_tok;
-      r[u] = il - tok[u] * per_tok;
+      tok[u] = il / ipt;
+      c[u] = il - tok[u] * ipt;
       slot[u] = slots[tok[u]];
     }
-    uint4 w[kReadUnroll];
+    uint2 kw[kReadUnroll], vw[kReadUnroll];
     bool ok[kReadUnroll];
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u) {
@@ -261,23 +265,17 @@ __global__ __launch_bounds__(kKvBlock) void kv_read_vec_kernel(
       const Idx su = ok[u] ? Idx(slot[u]) : Idx(0);  // invalid: row 0 of block 0
       const Idx blk = su / bs;
       const Idx off = su - blk * bs;
-      const bool is_v = r[u] >= lpt;
-      const int64_t chunk = int64_t(is_v ? r[u] - lpt : r[u]);
-      w[u] = *reinterpret_cast<const uint4*>((is_v ? vc : kc) + int64_t(blk) * cs +
-                                             int64_t(off) * e + chunk * 16);
+      const int64_t src = int64_t(blk) * cs + int64_t(off) * e + int64_t(c[u]) * 8;
+      kw[u] = *reinterpret_cast<const uint2*>(kc + src);
+      vw[u] = *reinterpret_cast<const uint2*>(vc + src);
     }
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u) {
-      const bool is_v = r[u] >= lpt;
-      const float s = is_v ? v_scale : k_scale;
-      const uint2 d0 = dequant4(w[u].x, s), d1 = dequant4(w[u].y, s);
-      const uint2 d2 = dequant4(w[u].z, s), d3 = dequant4(w[u].w, s);
-      const int64_t chunk = int64_t(is_v ? r[u] - lpt : r[u]);
-      uint16_t* dst = (is_v ? vo + int64_t(tok[u]) * vos : ko + int64_t(tok[u]) * kos) +
-                      chunk * 16;
-      if (ok[u])
-        store32_bf16(make_uint4(d0.x, d0.y, d1.x, d1.y), make_uint4(d2.x, d2.y, d3.x, d3.y),
-                     dst);
+      const uint4 kd = dequant8(kw[u], k_scale), vd = dequant8(vw[u], v_scale);
+      if (ok[u]) {
+        store16_bf16(kd, ko + int64_t(tok[u]) * kos + int64_t(c[u]) * 8);
+        store16_bf16(vd, vo + int64_t(tok[u]) * vos + int64_t(c[u]) * 8);
+      }
     }
   }
 }
@@ -459,23 +457,23 @@ static int kv_read(const uint8_t* k_cache, const uint8_t* v_cache, const int64_t
             int64_t cache_stride, hipStream_t stream) {
   const int64_t e = int64_t(heads) * head_dim;
   const int64_t nslots = num_blocks * block_size;
-  const bool vec = e % 16 == 0 && out_key_stride % 8 == 0 && out_value_stride % 8 == 0 &&
-                   cache_stride % 16 == 0 && aligned(k_cache, 16) && aligned(v_cache, 16) &&
-                   aligned(k_out, 16) && aligned(v_out, 16) && e / 16 <= 0x7FFFFFFF;
+  const bool vec = e % 8 == 0 && out_key_stride % 8 == 0 && out_value_stride % 8 == 0 &&
+                   cache_stride % 8 == 0 && aligned(k_cache, 8) && aligned(v_cache, 8) &&
+                   aligned(k_out, 16) && aligned(v_out, 16) && e / 8 <= 0x7FFFFFFF;
   if (vec) {
-    const int64_t items = int64_t(num_tokens) * 2 * (e / 16);
+    const int64_t items = int64_t(num_tokens) * (e / 8);
     const int64_t per_block = int64_t(kKvBlock) * kReadUnroll;
     const int64_t blocks = clamp_grid((items + per_block - 1) / per_block);
     // 32-bit indices when no item index the loop forms (< 2 * items + per_block) and no
     // slot can wrap
     if (items < (int64_t(1) << 31) - per_block && nslots <= 0x7FFFFFFF)
       launch(kv_read_vec_kernel<uint32_t>, dim3(unsigned(blocks)), dim3(kKvBlock), 0, stream,
-             k_cache, v_cache, slot_mapping, uint32_t(items), uint32_t(e / 16), cache_stride,
+             k_cache, v_cache, slot_mapping, uint32_t(items), uint32_t(e / 8), cache_stride,
              uint32_t(block_size), nslots, k_scale, v_scale, k_out, v_out, out_key_stride,
              out_value_stride);
     else
       launch(kv_read_vec_kernel<uint64_t>, dim3(unsigned(blocks)), dim3(kKvBlock), 0, stream,
-             k_cache, v_cache, slot_mapping, uint64_t(items), uint32_t(e / 16), cache_stride,
+             k_cache, v_cache, slot_mapping, uint64_t(items), uint32_t(e / 8), cache_stride,
              uint32_t(block_size), nslots, k_scale, v_scale, k_out, v_out, out_key_stride,
              out_value_stride);
     return launch_status();

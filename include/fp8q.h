@@ -198,9 +198,9 @@ int fp8_kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t
  *   k_out, v_out       device bf16 rows of out_key_stride / out_value_stride elements
  *   num_tokens >= 0 (0 is a no-op); num_kv_heads, head_dim, block_size, num_blocks > 0;
  *   out strides >= H*D; cache_stride >= block_size*H*D; scales in [2^-64, 2^64].
- * The vector path needs H*D a multiple of 16, 16-byte aligned pools and outputs, output
- * strides multiples of 8 and cache_stride a multiple of 16; anything else takes an
- * element-wise path with the same results.
+ * The vector path needs H*D, the output strides and cache_stride multiples of 8, 8-byte
+ * aligned pools and 16-byte aligned outputs; anything else takes an element-wise path
+ * with the same results.
  * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EALIGN, FP8Q_ELAUNCH. */
 int fp8_kv_read(const uint8_t* k_cache, const uint8_t* v_cache, const int64_t* slot_mapping,
                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,

@@ -182,9 +182,17 @@ def kv_write(k_bf16, v_bf16, k_cache, v_cache, slots, num_tokens, num_kv_heads, 
     vx = _u16(v_bf16)
     sl = np.ascontiguousarray(slots, dtype=np.int64)
     assert k_cache.flags["C_CONTIGUOUS"] and v_cache.flags["C_CONTIGUOUS"]
+    _check_slots(sl[:num_tokens], k_cache, v_cache, block_size, cache_stride)
     lib.oracle_kv_write(_ptr(kx), _ptr(vx), _ptr(k_cache), _ptr(v_cache), _ptr(sl),
                         num_tokens, num_kv_heads, head_dim, block_size, k_scale, v_scale,
                         key_stride, value_stride, cache_stride)
+
+
+def _check_slots(sl, k_cache, v_cache, block_size, cache_stride):
+    """The writer indexes the pools with every non-negative slot: refuse slots past the end
+    (the C code has no pool size to check against)."""
+    nslots = min(k_cache.size, v_cache.size) // cache_stride * block_size
+    assert np.all(sl < nslots), "slot past the end of the pools"
 
 
 def kv_read(k_cache, v_cache, slots, num_kv_heads, head_dim, block_size, num_blocks, k_scale,
@@ -214,6 +222,7 @@ class Calibrator:
         kx = _u16(k_bf16)
         vx = _u16(v_bf16)
         sl = np.ascontiguousarray(slots, dtype=np.int64)
+        _check_slots(sl, k_cache, v_cache, block_size, cache_stride)
         return self._lib.oracle_calib_observe_and_write(
             self._c, _ptr(kx), _ptr(vx), _ptr(sl), sl.size, num_kv_heads, head_dim,
             block_size, cache_stride, _ptr(k_cache), _ptr(v_cache))

@@ -180,9 +180,9 @@ def test_calibration_reuse_inside_window_equals_single_pass():
 
 
 def test_calibration_replay_with_heavy_slot_reuse_matches_oracle():
-    """Staged batches that keep rewriting a few dozen slots (plus padding and out-of-range
-    slots), over several 64-token tiles: the one-launch replay keeps each slot's last staged
-    writer, exactly as the oracle's in-order replay."""
+    """Staged batches that keep rewriting a few dozen slots (plus padding slots), over several
+    64-token tiles: the one-launch replay keeps each slot's last staged writer, exactly as
+    the oracle's in-order replay."""
     rng = np.random.default_rng(5020)
     batches = []
     for i in range(40):
@@ -190,8 +190,6 @@ def test_calibration_replay_with_heavy_slot_reuse_matches_oracle():
         slots = rng.permutation(96)[:n].astype(np.int64) * 7 % (NB * BS)
         if i % 5 == 0:
             slots[0] = -1
-        if i % 7 == 3:
-            slots[-1] = NB * BS + 11
         k = synth.to_bf16_bits(rng.normal(0, 3, size=(n, E)))
         v = synth.to_bf16_bits(rng.normal(0, 3, size=(n, E)))
         batches.append(synth.KvBatch(k=k, v=v, slots=slots))
@@ -256,7 +254,8 @@ def test_read_strided_outputs_and_padded_pool_stride():
     assert np.array_equal(kg, ko) and np.array_equal(vg, vo)
 
 
-@pytest.mark.parametrize("h,d,offset", [(3, 5, 0), (2, 64, 1), (1, 8, 3), (8, 128, 0)])
+@pytest.mark.parametrize("h,d,offset", [(3, 5, 0), (2, 64, 1), (1, 8, 3), (8, 128, 0), (1, 8, 0),
+                                          (3, 8, 0)])
 def test_read_elementwise_and_wide_rows(h, d, offset):
     """Odd geometry and misaligned outputs take the element-wise path; 8 x 128 rows take the
     vector path with a token spanning several waves."""
