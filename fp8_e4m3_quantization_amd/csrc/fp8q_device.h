@@ -63,10 +63,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
-// Four E4M3 codes in w times a scale -> four bf16 packed in two 32-bit words.
+// Four E4M3 codes in w times a scale -> four bf16 packed in two 32-bit words (integer
+// rounding; exact for NaN codes too).
 __device__ __forceinline__ uint2 dequant4(uint32_t w, float s) {
   const float2 a = e4m3x2_to_f32<false>(w), b = e4m3x2_to_f32<true>(w);
   return make_uint2(pack_bf16x2(a.x * s, a.y * s), pack_bf16x2(b.x * s, b.y * s));
+}
+
+// Two binary32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32; used only on
+// finite values (a NaN's bits are whatever the converter makes of it).
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// As dequant4, through the hardware converter: valid when no code of w is a NaN code.
+__device__ __forceinline__ uint2 dequant4_finite(uint32_t w, float s) {
+  const float2 a = e4m3x2_to_f32<false>(w), b = e4m3x2_to_f32<true>(w);
+  return make_uint2(cvt_bf16x2(a.x * s, a.y * s), cvt_bf16x2(b.x * s, b.y * s));
+}
+
+// Non-zero iff one of the four codes in w is a NaN code (S.1111.111): adding 1 to the low
+// seven bits of a byte carries into its top bit exactly when they are all ones.
+__device__ __forceinline__ uint32_t e4m3_nan_bytes(uint32_t w) {
+  return ((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
 }
 
 // 16-byte load with the non-temporal (streaming) hint.

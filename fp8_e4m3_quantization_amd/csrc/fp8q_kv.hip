@@ -28,6 +28,10 @@ namespace fp8q {
 namespace {
 
 constexpr int kKvBlock = 256;
+#ifndef FP8Q_KV_WIDE_BLOCK
+#define FP8Q_KV_WIDE_BLOCK 256
+#endif
+constexpr int kWideBlock = FP8Q_KV_WIDE_BLOCK;  // threads per block of the wide write
 
 __device__ __forceinline__ bool slot_to_block(int64_t slot, int64_t nslots, int bs,
                                               int64_t* blk, int64_t* off) {
@@ -135,23 +139,26 @@ __device__ __forceinline__ void store16_nt(uint4 v, uint8_t* p) {
 #endif
 }
 
-__global__ __launch_bounds__(kKvBlock) void kv_write_wide_kernel(
+// lpt = 1 << lpt_log2 (2 * lpt divides 64, so lpt is a power of two: lane arithmetic is
+// shifts and masks).
+__global__ __launch_bounds__(kWideBlock) void kv_write_wide_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint8_t* __restrict__ kc,
-    uint8_t* __restrict__ vc, const int64_t* __restrict__ slots, int64_t num_tokens, int lpt,
-    int64_t ks, int64_t vs, int64_t cs, int bs, int64_t nslots, float k_scale, float k_inv,
-    float v_scale, float v_inv) {
+    uint8_t* __restrict__ vc, const int64_t* __restrict__ slots, int64_t num_tokens,
+    int lpt_log2, int64_t ks, int64_t vs, int64_t cs, int bs, int64_t nslots, float k_scale,
+    float k_inv, float v_scale, float v_inv) {
   const int lane = threadIdx.x & 63;
-  const int tpw = 64 / (2 * lpt);               // tokens per wave per step
-  const int slot_in_wave = lane / (2 * lpt);    // which of those tokens
-  const int half = (lane / lpt) & 1;            // 0: K, 1: V
-  const int chunk = lane % lpt;                 // 16-element chunk within the row
+  const int lpt = 1 << lpt_log2;
+  const int tpw = 64 >> (lpt_log2 + 1);             // tokens per wave per step
+  const int slot_in_wave = lane >> (lpt_log2 + 1);  // which of those tokens
+  const int half = (lane >> lpt_log2) & 1;          // 0: K, 1: V
+  const int chunk = lane & (lpt - 1);               // 16-element chunk within the row
   const int e = 16 * lpt;
   const uint16_t* src = half ? v : k;
   const int64_t sstride = half ? vs : ks;
   uint8_t* dpool = half ? vc : kc;
   const float sc = half ? v_scale : k_scale, inv = half ? v_inv : k_inv;
-  const int64_t wave = (int64_t(blockIdx.x) * kKvBlock + threadIdx.x) >> 6;
-  const int64_t nwaves = (int64_t(gridDim.x) * kKvBlock) >> 6;
+  const int64_t wave = (int64_t(blockIdx.x) * kWideBlock + threadIdx.x) >> 6;
+  const int64_t nwaves = (int64_t(gridDim.x) * kWideBlock) >> 6;
   const int64_t per_iter = int64_t(tpw) * kWideSteps;
   for (int64_t t0 = wave * per_iter; t0 < num_tokens; t0 += nwaves * per_iter) {
     uint4 x0[kWideSteps], x1[kWideSteps];
@@ -235,12 +242,18 @@ __device__ __forceinline__ uint4 dequant8(uint2 w, float s) {
   return make_uint4(a.x, a.y, b.x, b.y);
 }
 
-// Idx is uint32_t when every item index and slot fits in 31 bits, else uint64_t.
-template <typename Idx>
+__device__ __forceinline__ uint4 dequant8_finite(uint2 w, float s) {
+  const uint2 a = dequant4_finite(w.x, s), b = dequant4_finite(w.y, s);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// Idx is uint32_t when every item index and slot fits in 31 bits, else uint64_t; kPow2:
+// ipt is a power of two (ipt_log2 its exponent), so token and chunk are a shift and a mask.
+template <typename Idx, bool kPow2>
 __global__ __launch_bounds__(kKvBlock) void kv_read_vec_kernel(
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
-    const int64_t* __restrict__ slots, Idx items, uint32_t ipt, int64_t cs, uint32_t bs,
-    int64_t nslots, float k_scale, float v_scale, uint16_t* __restrict__ ko,
+    const int64_t* __restrict__ slots, Idx items, uint32_t ipt, uint32_t ipt_log2, int64_t cs,
+    uint32_t bs, int64_t nslots, float k_scale, float v_scale, uint16_t* __restrict__ ko,
     uint16_t* __restrict__ vo, int64_t kos, int64_t vos) {
   const Idx nthreads = Idx(gridDim.x) * kKvBlock;
   const int64_t e = int64_t(8) * ipt;
@@ -253,7 +266,7 @@ __global__ __launch_bounds__(kKvBlock) void kv_read_vec_kernel(
     for (int u = 0; u < kReadUnroll; ++u) {
       const Idx i = i0 + u * nthreads;
       const Idx il = i < items ? i : items - 1;
-      tok[u] = il / ipt;
+      tok[u] = kPow2 ? il >> ipt_log2 : il / ipt;
       c[u] = il - tok[u] * ipt;
       slot[u] = slots[tok[u]];
     }
@@ -271,7 +284,17 @@ __global__ __launch_bounds__(kKvBlock) void kv_read_vec_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u) {
-      const uint4 kd = dequant8(kw[u], k_scale), vd = dequant8(vw[u], v_scale);
+      // hardware bf16 conversion unless a NaN code is present (then the exact integer path)
+      const uint32_t nan = e4m3_nan_bytes(kw[u].x) | e4m3_nan_bytes(kw[u].y) |
+                           e4m3_nan_bytes(vw[u].x) | e4m3_nan_bytes(vw[u].y);
+      uint4 kd, vd;
+      if (__builtin_expect(nan == 0, 1)) {
+        kd = dequant8_finite(kw[u], k_scale);
+        vd = dequant8_finite(vw[u], v_scale);
+      } else {
+        kd = dequant8(kw[u], k_scale);
+        vd = dequant8(vw[u], v_scale);
+      }
       if (ok[u]) {
         store16_bf16(kd, ko + int64_t(tok[u]) * kos + int64_t(c[u]) * 8);
         store16_bf16(vd, vo + int64_t(tok[u]) * vos + int64_t(c[u]) * 8);
@@ -410,10 +433,11 @@ int kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t* v_
                     aligned(v_cache, 16);
   if (wide) {
     const int lpt = int(e / 16);
-    const int64_t per_block = int64_t(kKvBlock / 64) * (64 / (2 * lpt)) * kWideSteps;
+    const int lpt_log2 = __builtin_ctz(unsigned(lpt));
+    const int64_t per_block = int64_t(kWideBlock / 64) * (64 / (2 * lpt)) * kWideSteps;
     const int64_t blocks = clamp_grid((int64_t(num_tokens) + per_block - 1) / per_block);
-    launch(kv_write_wide_kernel, dim3(unsigned(blocks)), dim3(kKvBlock), 0, stream, k, v,
-           k_cache, v_cache, slot_mapping, int64_t(num_tokens), lpt, key_stride, value_stride,
+    launch(kv_write_wide_kernel, dim3(unsigned(blocks)), dim3(kWideBlock), 0, stream, k, v,
+           k_cache, v_cache, slot_mapping, int64_t(num_tokens), lpt_log2, key_stride, value_stride,
            cache_stride, block_size, nslots, k_scale, k_inv, v_scale, v_inv);
     return launch_status();
   }
@@ -466,16 +490,20 @@ static int kv_read(const uint8_t* k_cache, const uint8_t* v_cache, const int64_t
     const int64_t blocks = clamp_grid((items + per_block - 1) / per_block);
     // 32-bit indices when no item index the loop forms (< 2 * items + per_block) and no
     // slot can wrap
-    if (items < (int64_t(1) << 31) - per_block && nslots <= 0x7FFFFFFF)
-      launch(kv_read_vec_kernel<uint32_t>, dim3(unsigned(blocks)), dim3(kKvBlock), 0, stream,
-             k_cache, v_cache, slot_mapping, uint32_t(items), uint32_t(e / 8), cache_stride,
-             uint32_t(block_size), nslots, k_scale, v_scale, k_out, v_out, out_key_stride,
-             out_value_stride);
-    else
-      launch(kv_read_vec_kernel<uint64_t>, dim3(unsigned(blocks)), dim3(kKvBlock), 0, stream,
-             k_cache, v_cache, slot_mapping, uint64_t(items), uint32_t(e / 8), cache_stride,
-             uint32_t(block_size), nslots, k_scale, v_scale, k_out, v_out, out_key_stride,
-             out_value_stride);
+    const uint32_t ipt = uint32_t(e / 8);
+    const bool pow2 = (ipt & (ipt - 1)) == 0;
+    const uint32_t ipt_log2 = uint32_t(__builtin_ctz(ipt));
+    if (items < (int64_t(1) << 31) - per_block && nslots <= 0x7FFFFFFF) {
+      auto kern = pow2 ? kv_read_vec_kernel<uint32_t, true> : kv_read_vec_kernel<uint32_t, false>;
+      launch(kern, dim3(unsigned(blocks)), dim3(kKvBlock), 0, stream, k_cache, v_cache,
+             slot_mapping, uint32_t(items), ipt, ipt_log2, cache_stride, uint32_t(block_size),
+             nslots, k_scale, v_scale, k_out, v_out, out_key_stride, out_value_stride);
+    } else {
+      auto kern = pow2 ? kv_read_vec_kernel<uint64_t, true> : kv_read_vec_kernel<uint64_t, false>;
+      launch(kern, dim3(unsigned(blocks)), dim3(kKvBlock), 0, stream, k_cache, v_cache,
+             slot_mapping, uint64_t(items), ipt, ipt_log2, cache_stride, uint32_t(block_size),
+             nslots, k_scale, v_scale, k_out, v_out, out_key_stride, out_value_stride);
+    }
     return launch_status();
   }
   if (e > 0x7FFFFFFF) return FP8Q_EINVAL;

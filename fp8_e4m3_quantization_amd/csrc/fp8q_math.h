@@ -58,7 +58,11 @@ FP8Q_HD inline float div_by_scale(float x, float s, float y) {
 // E4M3 range can never produce inf - inf; the result then still lies beyond +-448.
 FP8Q_HD inline float div_by_scale_clipped(float x, float s, float y) {
   float q = x * y;
+#if defined(__HIP_DEVICE_COMPILE__)
+  q = __builtin_amdgcn_fmed3f(q, -1024.0f, 1024.0f);  // one v_med3_f32; same for non-NaN q
+#else
   q = q > 1024.0f ? 1024.0f : (q < -1024.0f ? -1024.0f : q);
+#endif
   float rn = __builtin_fmaf(q, s, -x);
   return __builtin_fmaf(-rn, y, q);
 }

@@ -27,7 +27,10 @@
 namespace fp8q {
 namespace {
 
-constexpr int kQuantBlock = 256;           // 4 waves
+#ifndef FP8Q_QUANT_BLOCK
+#define FP8Q_QUANT_BLOCK 256
+#endif
+constexpr int kQuantBlock = FP8Q_QUANT_BLOCK;  // threads per block
 constexpr int kGroupsPerWave = 8;
 #ifndef FP8Q_QUANT_UNROLL
 #define FP8Q_QUANT_UNROLL 1  // wave tiles whose loads are issued together per iteration
