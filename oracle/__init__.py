@@ -11,6 +11,7 @@ Functions (all single-threaded, in the order the pages define them):
   group_quant(x_bf16[m,k])           -> (q uint8[m,k], scales f32[m,k/128])
   block_quant(w_bf16[n,k])           -> (wq uint8[n,k], ws f32[ceil(n/128),ceil(k/128)])
   gemm(a_q, a_s, w_q, w_s)           -> float64[m,n] reference
+  gemm_w8a16(a_bf16, w_q, w_s)       -> (float64[m,n] reference, float64[m,n] sum of |terms|)
   amax(x_bf16)                       -> float32
   kv_write(...)                      in-place on the uint8 pools
   kv_read(...)                       dequantizing gather of a paged history to bf16
@@ -53,6 +54,7 @@ def _load():
     lib.oracle_group_quant.argtypes = [_p, _i64, _i64, _p, _p]
     lib.oracle_block_quant.argtypes = [_p, _i64, _i64, _p, _p]
     lib.oracle_gemm.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p]
+    lib.oracle_gemm_w8a16.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p]
     lib.oracle_amax.argtypes = [_p, _i64, _p]
     lib.oracle_kv_write.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, _f32, _f32,
                                     _i64, _i64, _i64]
@@ -160,6 +162,21 @@ def gemm(a_q, a_s, w_q, w_s) -> np.ndarray:
     ref = np.empty((m, n), dtype=np.float64)
     lib.oracle_gemm(_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), m, n, k, _ptr(ref))
     return ref
+
+
+def gemm_w8a16(a_bf16, w_q, w_s):
+    """bf16 activation x block-scaled E4M3 weight, in double: (ref, sum of |terms|)."""
+    lib = _load()
+    a = _u16(a_bf16)
+    w_q = np.ascontiguousarray(w_q, dtype=np.uint8)
+    w_s = np.ascontiguousarray(w_s, dtype=np.float32)
+    m, k = a.shape
+    n = w_q.shape[0]
+    assert w_q.shape[1] == k and w_s.shape == ((n + 127) // 128, k // 128)
+    ref = np.empty((m, n), dtype=np.float64)
+    mag = np.empty((m, n), dtype=np.float64)
+    lib.oracle_gemm_w8a16(_ptr(a), _ptr(w_q), _ptr(w_s), m, n, k, _ptr(ref), _ptr(mag))
+    return ref, mag
 
 
 # ------------------------------------------------------------------------------- KV

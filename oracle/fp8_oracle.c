@@ -267,6 +267,34 @@ void oracle_gemm(const uint8_t* a_q, const float* a_s, const uint8_t* w_q, const
   }
 }
 
+/* -------------------------------------------- W8A16: bf16 activation x E4M3 weight */
+
+/* The decode page's small-batch tier (module doc, NUMERICS; DECODE_W8A8_ROWS): the
+ * activation stays bf16 and multiplies E4M3 weights carrying the same 128x128 FP32 block
+ * scales.  ref[m, n] = sum_k bf16(a[m,k]) * dec(w_q[n,k]) * w_s[n/128, k/128] and
+ * absref[m, n] = sum_k |same term|, every product and sum in double, K order (each term is
+ * exact in double: 8 + 4 + 24 significant bits). */
+void oracle_gemm_w8a16(const uint16_t* a, const uint8_t* w_q, const float* w_s, int64_t m,
+                       int64_t n, int64_t k, double* ref, double* absref) {
+  int64_t i, j, kk, groups = k / 128;
+  double dec[256];
+  for (i = 0; i < 256; ++i) dec[i] = oracle_e4m3_decode((uint8_t)i);
+  assert(k % 128 == 0);
+  for (i = 0; i < m; ++i) {
+    for (j = 0; j < n; ++j) {
+      double acc = 0.0, mag = 0.0;
+      for (kk = 0; kk < k; ++kk) {
+        double t = (double)oracle_bf16_to_f32(a[i * k + kk]) * dec[w_q[j * k + kk]] *
+                   (double)w_s[(j / 128) * groups + kk / 128];
+        acc += t;
+        mag += fabs(t);
+      }
+      ref[i * n + j] = acc;
+      absref[i * n + j] = mag;
+    }
+  }
+}
+
 /* -------------------------------------------------------------- C7: absolute max */
 
 /* max |x| over n bf16 values, max-accumulated into *acc (the caller zeroes it). */

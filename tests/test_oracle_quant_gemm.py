@@ -153,3 +153,52 @@ def test_w8a8_error_band_on_decode_shape(orc):
     ref = synth.bf16_bits_to_f32(a).astype(np.float64) @ wd.T
     rel = np.sqrt(np.mean((got - ref) ** 2) / np.mean(ref ** 2))
     assert 0.005 < rel < 0.06, rel
+
+
+# ------------------------------------------------------------------------ W8A16 tier
+
+
+def test_w8a16_matches_numpy_on_decoded_weights(orc):
+    """bf16 activation x E4M3 weight: numpy's float64 matmul over torch-decoded weights with
+    the block scales expanded; the sum of |terms| likewise; a rolled scale grid fails."""
+    rng = np.random.default_rng(21)
+    m, n, k = 3, 384, 640
+    a = synth.to_bf16_bits(rng.normal(0, 1, size=(m, k)))
+    w = synth.to_bf16_bits(rng.normal(0, 0.02, size=(n, k)))
+    w_q, w_s = orc.block_quant(w)
+    ad = synth.bf16_bits_to_f32(a).astype(np.float64)
+    wd = _torch_dec(w_q) * np.repeat(np.repeat(w_s.astype(np.float64), 128, axis=0), 128, axis=1)
+    ref, mag = orc.gemm_w8a16(a, w_q, w_s)
+    assert np.allclose(ref, ad @ wd.T, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    assert np.allclose(mag, np.abs(ad) @ np.abs(wd).T, rtol=1e-12)
+    bad = np.ascontiguousarray(np.roll(w_s, 1, axis=1))
+    assert not np.allclose(orc.gemm_w8a16(a, w_q, bad)[0], ref, rtol=1e-3)
+
+
+def test_w8a16_identity_weight_returns_the_activation(orc):
+    rng = np.random.default_rng(4)
+    k = 256
+    a = synth.to_bf16_bits(rng.normal(0, 5, size=(4, k)))
+    w_q = np.zeros((k, k), dtype=np.uint8)
+    np.fill_diagonal(w_q, 0x38)  # 1.0
+    ref, mag = orc.gemm_w8a16(a, w_q, np.ones((2, 2), dtype=np.float32))
+    x = synth.bf16_bits_to_f32(a).astype(np.float64)
+    assert np.array_equal(ref, x) and np.array_equal(mag, np.abs(x))
+
+
+def test_w8a16_integer_exact_case_by_brute_force(orc):
+    """Small integers and power-of-two scales: every sum is an exact integer; a pure-Python
+    loop over the decoded codes (2.0 = 0x40, 1.0 = 0x38, sign bit 0x80) gives it."""
+    rng = np.random.default_rng(5)
+    m, n, k = 2, 256, 256
+    av = rng.integers(-3, 4, size=(m, k)).astype(np.float64)
+    a = synth.to_bf16_bits(av)
+    wv = rng.integers(-2, 3, size=(n, k))
+    code = {0: 0x00, 1: 0x38, 2: 0x40, -1: 0xB8, -2: 0xC0}
+    w_q = np.vectorize(code.get)(wv).astype(np.uint8)
+    w_s = np.array([[2.0, 0.5], [0.25, 4.0]], dtype=np.float32)
+    ref, _ = orc.gemm_w8a16(a, w_q, w_s)
+    for i in range(m):
+        for j in range(0, n, 37):
+            want = sum(av[i, kk] * wv[j, kk] * float(w_s[j // 128, kk // 128]) for kk in range(k))
+            assert ref[i, j] == want
