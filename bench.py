@@ -42,7 +42,8 @@ def parse():
     p.add_argument("--iters", type=int, default=100, help="launches per kernel measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="",
-                   help="comma list of sections: step,gemm,grouped,sweep,quant,kv (default all)")
+                   help="comma list of sections: step,gemm,grouped,sweep,gemv,quant,kv "
+                        "(default all)")
     return p.parse_args()
 
 
@@ -60,6 +61,11 @@ def quant_bytes(m, k):
 def gemm_bytes(m, n, k):
     g = k // 128
     return n * k + (n // 128) * g * 4 + m * k + m * g * 4 + m * n * 2
+
+
+def gemv_bytes(m, n, k):
+    """W8A16 tier: weight codes + block scales, bf16 activation, bf16 output."""
+    return n * k + (n // 128) * (k // 128) * 4 + m * k * 2 + m * n * 2
 
 
 def gemm_weight_bytes(n, k):
@@ -208,7 +214,7 @@ def main():
     fq.load()
     timer = Timer(torch, fq.load())
     only = (set(args.only.split(",")) if args.only
-            else {"step", "gemm", "grouped", "sweep", "quant", "kv"})
+            else {"step", "gemm", "grouped", "sweep", "gemv", "quant", "kv"})
     kernels = {}
 
     def log(msg):
@@ -319,6 +325,26 @@ def main():
             frac_hbm=round(b / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), bytes=b)
         log(f"fused quant + grouped gemm: {mean_us:.2f} us "
             f"{kernels['quant_w8a8_gemm_fused_m16_k5120_4proj']['gbs']} GB/s")
+
+    # ------------------------------------------------------ W8A16 tier (1..4 rows)
+    if "gemv" in only:
+        n = 16384
+        for m in (1, 2, 4):
+            acts = [bf16_dev(torch, synth.decode_activation(m, seed=4500 + m + 10 * i))
+                    for i in range(len(sets))]
+            outs = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for _ in sets]
+            launches = [(lambda i=i: fq.w8a16_block_gemv(acts[i], sets[i]["w"][n][0],
+                                                         sets[i]["w"][n][1], outs[i]))
+                        for i in range(len(sets))]
+            mean_us, med_us = timer.kernel_us(launches, args.iters)
+            b = gemv_bytes(m, n, K_DECODE)
+            kernels[f"w8a16_gemv_m{m}_n{n}_k5120"] = dict(
+                us=round(mean_us, 3), us_median=round(med_us, 3),
+                gbs=round(b / (mean_us * 1e-6) / 1e9, 1),
+                frac_hbm=round(b / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), bytes=b)
+            log(f"w8a16 gemv m={m} n={n}: {mean_us:.2f} us "
+                f"{kernels[f'w8a16_gemv_m{m}_n{n}_k5120']['gbs']} GB/s")
+            del acts, outs
 
     # ----------------------------------------------------------- width sweep
     if "sweep" in only:

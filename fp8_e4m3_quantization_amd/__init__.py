@@ -23,4 +23,6 @@ from ._lib import (  # noqa: F401
     strerror,
     w8a8_block_gemm,
     w8a8_block_gemm_grouped,
+    w8a16_block_gemv,
+    w8a16_block_gemv_grouped,
 )

@@ -21,7 +21,8 @@ FP8Q_CALIB_STAGE, FP8Q_CALIB_DECLINE, FP8Q_CALIB_FREEZE, FP8Q_CALIB_FROZEN = 0, 
 # Every symbol include/fp8q.h declares.
 EXPORTS = (
     "fp8q_strerror", "fp8q_version", "fp8q_time_next_launch", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
-    "w8a8_block_gemm", "w8a8_block_gemm_grouped", "fp8_quant_w8a8_gemm_grouped", "fp8_kv_write", "fp8_kv_read", "fp8_kv_amax", "fp8q_kv_calib_create",
+    "w8a8_block_gemm", "w8a8_block_gemm_grouped", "fp8_quant_w8a8_gemm_grouped",
+    "w8a16_block_gemv", "w8a16_block_gemv_grouped", "fp8_kv_write", "fp8_kv_read", "fp8_kv_amax", "fp8q_kv_calib_create",
     "fp8q_kv_calib_observe", "fp8q_kv_calib_decide", "fp8q_kv_calib_scales",
     "fp8q_kv_calib_get_info", "fp8q_kv_calib_destroy",
 )
@@ -85,6 +86,9 @@ def load() -> ctypes.CDLL:
                                                    I32, P]),
         "fp8_quant_w8a8_gemm_grouped": (ctypes.c_int, [P, P, P, ctypes.POINTER(GemmProj), I32,
                                                        I32, I32, P]),
+        "w8a16_block_gemv": (ctypes.c_int, [P, P, P, P, I32, I32, I32, I32, P]),
+        "w8a16_block_gemv_grouped": (ctypes.c_int, [P, ctypes.POINTER(GemmProj), I32, I32, I32,
+                                                    P]),
         "fp8_kv_write": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, I64, F32, F32,
                                         I32, I32, I64, P]),
         "fp8_kv_read": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, I64, F32, F32, P, P,
@@ -214,6 +218,8 @@ def w8a8_block_gemm(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tensor,
 
 
 def _proj_array(m, k, projections, device):
+    """projections: (w_q [n, k], w_scale, out) with out None, a contiguous [m, ldc] tensor,
+    or a 2-D column view [m, n] of a wider row-major buffer (its row stride is the ldc)."""
     arr = (GemmProj * len(projections))()
     outs = []
     for i, (w_q, w_scale, out) in enumerate(projections):
@@ -222,11 +228,18 @@ def _proj_array(m, k, projections, device):
             raise ValueError(f"projection {i} does not match the activation")
         if out is None:
             out = torch.empty((m, n), dtype=torch.bfloat16, device=device)
-        ldc = out.shape[-1]
-        if out.numel() < (m - 1) * ldc + n:
+        if out.is_contiguous():
+            ldc = out.shape[-1]
+            room = out.numel()
+        elif out.dim() == 2 and out.stride(1) == 1 and out.shape[1] >= n:
+            ldc = out.stride(0)
+            room = out.untyped_storage().nbytes() // out.element_size() - out.storage_offset()
+        else:
+            raise ValueError(f"projection {i}: out must be contiguous or a row-major column view")
+        if ldc < n or room < (m - 1) * ldc + n:
             raise ValueError(f"projection {i}: out is smaller than (m - 1) * ldc + n")
         arr[i] = GemmProj(_dev(w_q, "w_q", _U8), _dev(w_scale, "w_scale", torch.float32),
-                          _dev(out, "out", _BF16), n, ldc)
+                          _dev(out, "out", _BF16, False), n, ldc)
         outs.append(out)
     return arr, outs
 
@@ -244,6 +257,40 @@ def w8a8_block_gemm_grouped(a_q: torch.Tensor, a_scale: torch.Tensor, projection
                                         len(projections), m, k,
                                         current_stream(a_q.device) if stream is None else stream)
     check("w8a8_block_gemm_grouped", st)
+    return outs
+
+
+def w8a16_block_gemv(a: torch.Tensor, w_q: torch.Tensor, w_scale: torch.Tensor,
+                     out: torch.Tensor | None = None, ldc: int | None = None,
+                     stream: int | None = None) -> torch.Tensor:
+    """bf16 a [m <= 4, k] x E4M3 w_q [n, k]^T with block scales -> bf16 out [m, ldc]."""
+    m, k = a.shape
+    n = w_q.shape[0]
+    if w_q.shape[1] != k:
+        raise ValueError("a and w_q disagree on k")
+    if w_scale.numel() != (n // 128) * (k // 128):
+        raise ValueError("w_scale does not match w_q")
+    if out is None:
+        ldc = n if ldc is None else ldc
+        out = torch.empty((m, ldc), dtype=torch.bfloat16, device=a.device)
+    else:
+        ldc = out.shape[-1] if ldc is None else ldc
+        if out.numel() < (m - 1) * ldc + n:
+            raise ValueError("out is smaller than (m - 1) * ldc + n elements")
+    st = load().w8a16_block_gemv(_dev(a, "a", _BF16), _dev(w_q, "w_q", _U8),
+                                 _dev(w_scale, "w_scale", torch.float32), _dev(out, "out", _BF16),
+                                 m, n, k, ldc, current_stream(a.device) if stream is None else stream)
+    check("w8a16_block_gemv", st)
+    return out
+
+
+def w8a16_block_gemv_grouped(a: torch.Tensor, projections, stream: int | None = None):
+    """One launch of the W8A16 tier over several projections of the same bf16 activation."""
+    m, k = a.shape
+    arr, outs = _proj_array(m, k, projections, a.device)
+    st = load().w8a16_block_gemv_grouped(_dev(a, "a", _BF16), arr, len(projections), m, k,
+                                         current_stream(a.device) if stream is None else stream)
+    check("w8a16_block_gemv_grouped", st)
     return outs
 
 

@@ -21,15 +21,13 @@
 
 #include "fp8q.h"
 #include "fp8q_device.h"
+#include "fp8q_gemm_common.h"
 #include "fp8q_launch.h"
 
 #pragma clang fp contract(off)
 
 namespace fp8q {
 namespace {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxGemmK = 131072;  // LDS holds the [k/128][16] activation scales
 
@@ -137,58 +135,20 @@ __global__ __launch_bounds__(64 * kWaves) void w8a8_gemm_kernel(
 // meet in LDS (double-buffered, one barrier per strip) and one pass writes bf16.
 // Several projections that read the same activation can share one launch: strips are
 // numbered across them.
-constexpr int kMaxProj = 8;
-constexpr int kPWaves = 8;
-
-struct ProjSet {
-  const uint8_t* w[kMaxProj];
-  const float* ws[kMaxProj];
-  uint16_t* out[kMaxProj];
-  int ldc[kMaxProj];
-  int strip_end[kMaxProj];  // cumulative strip count after projection p
-  int count;
-};
-
-// s_waitcnt lgkmcnt(0) + s_barrier: orders the LDS partials without waiting on the
-// weight prefetches that are still in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
-  __builtin_amdgcn_s_barrier();
-}
-
-// Weight loads go through a buffer descriptor per strip (base = the strip's first row,
-// 16*k bytes).  A strip past the end gets a zero-size descriptor: its loads return zeros
-// without touching memory, so every prefetch is issued unconditionally and the compiler
-// tracks the in-order load counter exactly (no branch around any load).
+// Weight loads go through a buffer descriptor per strip (make_strip_rsrc); the cache
+// policy bits of those loads:
 #ifndef FP8Q_GEMM_AUX
-#define FP8Q_GEMM_AUX 0  // cache-policy bits of the weight loads
+#define FP8Q_GEMM_AUX 0
 #endif
 #ifndef FP8Q_GEMM_NT_OUT
 #define FP8Q_GEMM_NT_OUT 1  // bf16 outputs written with the non-temporal hint
 #endif
-constexpr uint32_t kBufferDword3 = 0x00020000;  // raw 32-bit buffer format (gfx9 family)
-
-// Weight block scales are read-only for the whole launch and uniform per wave: reading
-// them through the constant address space makes them scalar loads (counted apart from
-// the vector weight loads, so waiting for a scale never drains the weight prefetch).
-typedef const __attribute__((address_space(4))) float const_float;
 
 template <int kGpw>
 struct Slice {
   v8i b[kGpw];
   float ws[kGpw];
 };
-
-template <int kAux>
-__device__ __forceinline__ v8i buffer_load32(__amdgpu_buffer_rsrc_t r, int off) {
-  typedef unsigned v4u __attribute__((ext_vector_type(4)));
-  const v4u x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAux);
-  const v4u y = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kAux);
-  v8i o;
-  o[0] = int(x[0]); o[1] = int(x[1]); o[2] = int(x[2]); o[3] = int(x[3]);
-  o[4] = int(y[0]); o[5] = int(y[1]); o[6] = int(y[2]); o[7] = int(y[3]);
-  return o;
-}
 
 // Strips are processed in rounds of kRound: a wave multiplies its K-slice of kRound strips
 // back to back (its partial tiles stay in registers), then all waves meet once -- partials
@@ -225,19 +185,11 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
 #pragma unroll
   for (int u = 0; u < kGpw; ++u) goff[u] = (g0 + max(0, min(u, cnt - 1))) * 128;
 
-  // strip s -> (projection, first column); uniform across the workgroup
-  auto locate = [&](int s, int* p_out, int* n0) {
-    int p = 0;
-    while (p + 1 < ps.count && s >= ps.strip_end[p]) ++p;
-    *p_out = p;
-    *n0 = (s - (p ? ps.strip_end[p - 1] : 0)) * 16;
-  };
   auto fetch = [&](int s, Slice<kGpw>& sl) {
     const bool valid = s < total_strips;
     int p, n0;
-    locate(valid ? s : total_strips - 1, &p, &n0);
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(ps.w[p] + int64_t(n0) * k), 0, valid ? 16 * k : 0, kBufferDword3);
+    locate_strip(ps, valid ? s : total_strips - 1, &p, &n0);
+    const __amdgpu_buffer_rsrc_t r = make_strip_rsrc(ps.w[p] + int64_t(n0) * k, k, valid);
     const_float* wsp = (const_float*)(ps.ws[p] + int64_t(n0 >> 7) * groups);
 #pragma unroll
     for (int u = 0; u < kGpw; ++u) sl.b[u] = buffer_load32<kAux>(r, row * k + koff + goff[u]);
@@ -368,7 +320,7 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
         for (int w = 0; w < kPWaves; ++w) sum[x] += part[((j * kPWaves + w) * 4 + q0 + x) * 64 + lane];
       if (i + j < nit) {
         int p, n0;
-        locate(first + (i + j) * stride, &p, &n0);
+        locate_strip(ps, first + (i + j) * stride, &p, &n0);
         uint16_t* o = ps.out[p] + n0 + (lane & 15);
         const int ldc = ps.ldc[p];
 #pragma unroll

@@ -1,0 +1,227 @@
+// fp8q_gemv.hip -- the W8A16 decode tier for 1..4 activation rows: bf16 activation times
+// E4M3 weight with 128x128 FP32 block scales, FP32 accumulation, bf16 out.
+//
+// dispatch_proj_decode.rs page: module doc NUMERICS (the W8A16 arithmetic: bf16 activation
+// x E4M3 weight with the checkpoint's 128x128 FP32 block scales, which the W8A8 rows
+// replace above four rows), DECODE_W8A8_ROWS (four rows or fewer stay on the batch-4 GEMV
+// tier, one row on the scalar GEMV: at those widths a GEMV that streams each weight byte
+// once is the right shape).
+//
+// The pages' GEMV tiers are CUDA FFMA loops.  Here the same persistent layout as the W8A8
+// decode kernel streams the weights: one 8-wave workgroup per CU walks 16-column output
+// strips, wave w owns a fixed 1/8 of the K-groups with its activation fragments held in
+// registers for the whole launch, weight slices are prefetched one strip ahead through a
+// buffer descriptor, and the 8 partials of each strip meet in LDS once per 4 strips.  Per
+// 128-wide group a lane widens its 32 weight codes to bf16 (exact: every E4M3 value is a
+// bf16 value) with 16 v_cvt_pk_f32_fp8 and 16 v_perm_b32, and four v_mfma_f32_16x16x32_bf16
+// accumulate the group's partial, which the block scale then multiplies in FP32.  The MFMA
+// computes 16 activation rows; rows >= m repeat row m-1 and are never stored.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8q.h"
+#include "fp8q_device.h"
+#include "fp8q_gemm_common.h"
+#include "fp8q_launch.h"
+
+#pragma clang fp contract(off)
+
+namespace fp8q {
+namespace {
+
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+
+constexpr int kGemvMaxRows = 4;
+constexpr int kGemvRound = 4;  // strips per LDS reduction
+constexpr int kGemvMaxK = kPWaves * 8 * 128;
+
+// Two E4M3 codes (bytes 0,1 or 2,3 of w) -> two bf16 in one word: the binary32 decode is
+// exact and its top half is the bf16 value (no rounding: three mantissa bits).
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  const float2 f = e4m3x2_to_f32<kHigh>(w);
+  return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+}
+
+// Eight codes (two dwords) -> the eight bf16 of one MFMA operand, in k order.
+__device__ __forceinline__ v8bf16 widen8(uint32_t lo, uint32_t hi) {
+  const uint4 r = make_uint4(e4m3x2_to_bf16x2<false>(lo), e4m3x2_to_bf16x2<true>(lo),
+                             e4m3x2_to_bf16x2<false>(hi), e4m3x2_to_bf16x2<true>(hi));
+  return __builtin_bit_cast(v8bf16, r);
+}
+
+template <int kGpw>
+struct GemvSlice {
+  v8i b[kGpw];
+  float ws[kGpw];
+};
+
+// Operand layout (v_mfma_f32_16x16x32_bf16): lane l supplies row (l & 15) and 8 values of
+// k.  For group g the lane holds k = 128g + 32*(l>>4) + [0, 32) of its row (activation
+// row for A, weight row = output column for B); MFMA i of the group uses the 8 values at
+// +8i.  A and B use the same assignment, so the four MFMAs sum every k of the group once.
+// Accumulator: lane l, register j holds activation row 4*(l>>4) + j, column l & 15; with
+// m <= 4 only lanes 0..15 carry stored rows.
+template <int kGpw>
+__global__ __launch_bounds__(64 * kPWaves) void w8a16_persistent_kernel(
+    const uint16_t* __restrict__ a, ProjSet ps, int m, int k, int total_strips) {
+  __shared__ float s_part[2][kGemvRound * kPWaves * 64];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int groups = k >> 7;
+  const int g0 = (groups * wv) / kPWaves;
+  const int cnt = (groups * (wv + 1)) / kPWaves - g0;  // 0 <= cnt <= kGpw
+  const int row = lane & 15, koff = (lane >> 4) * 32;
+  const int arow = row < m ? row : m - 1;  // rows >= m repeat row m-1 (in bounds, unused)
+  int goff[kGpw];  // first k of slice group u (a short slice repeats its last group; the
+                   // repeat is skipped in the multiply)
+#pragma unroll
+  for (int u = 0; u < kGpw; ++u) goff[u] = (g0 + max(0, min(u, cnt - 1))) * 128;
+
+  auto fetch = [&](int s, GemvSlice<kGpw>& sl) {
+    const bool valid = s < total_strips;
+    int p, n0;
+    locate_strip(ps, valid ? s : total_strips - 1, &p, &n0);
+    const __amdgpu_buffer_rsrc_t r = make_strip_rsrc(ps.w[p] + int64_t(n0) * k, k, valid);
+    const_float* wsp = (const_float*)(ps.ws[p] + int64_t(n0 >> 7) * groups);
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u) sl.b[u] = buffer_load32<0>(r, row * k + koff + goff[u]);
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u) sl.ws[u] = wsp[goff[u] >> 7];
+  };
+
+  const int stride = int(gridDim.x);
+  const int first = int(blockIdx.x);
+  const int nit = (total_strips - first + stride - 1) / stride;
+  if (nit <= 0) return;
+
+  // activation fragments first (they stay in registers), then the first weight prefetch
+  uint4 af[kGpw][4];
+  const uint4* ap = reinterpret_cast<const uint4*>(a + int64_t(arow) * k + koff);
+#pragma unroll
+  for (int u = 0; u < kGpw; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[u][i] = ap[(goff[u] >> 3) + i];
+  GemvSlice<kGpw> buf[2];
+  fetch(first, buf[0]);
+
+  auto multiply = [&](const GemvSlice<kGpw>& cur) {
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u) {
+      if (u < cnt) {  // wave-uniform
+        v4f c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(v8bf16, af[u][i]),
+              widen8(uint32_t(cur.b[u][2 * i]), uint32_t(cur.b[u][2 * i + 1])), c, 0, 0, 0);
+        const float w = cur.ws[u];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(c[q], w, acc[q]);
+      }
+    }
+    return acc;
+  };
+
+  int par = 0;
+  for (int i = 0; i < nit; i += kGemvRound) {
+    float* part = s_part[par];  // [round strip][wave][register][16 columns]
+#pragma unroll
+    for (int j = 0; j < kGemvRound; ++j) {
+      fetch(first + (i + j + 1) * stride, buf[(j + 1) & 1]);
+      if (i + j < nit) {
+        const v4f acc = multiply(buf[j & 1]);
+        if (lane < 16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) part[((j * kPWaves + wv) * 4 + q) * 16 + lane] = acc[q];
+        }
+      }
+    }
+    lds_barrier();
+    // Reduce: thread t < 256 owns output (round strip t/64, register (t/16)%4, column t%16).
+    // Every LDS read of the round comes before its one store.
+    const int t = int(threadIdx.x);
+    if (t < kGemvRound * 64) {
+      const int j = t >> 6, q = (t >> 4) & 3, c = t & 15;
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kPWaves; ++w) sum += part[((j * kPWaves + w) * 4 + q) * 16 + c];
+      if (i + j < nit && q < m) {
+        int p, n0;
+        locate_strip(ps, first + (i + j) * stride, &p, &n0);
+        ps.out[p][int64_t(q) * ps.ldc[p] + n0 + c] = f32_to_bf16_rne(sum);
+      }
+    }
+    par ^= 1;
+  }
+}
+
+template <int kGpw>
+int launch_gemv(const uint16_t* a, const ProjSet& ps, int m, int k, int total,
+                hipStream_t stream) {
+  const int grid = total < num_cus() ? total : num_cus();
+  launch(w8a16_persistent_kernel<kGpw>, dim3(grid), dim3(64 * kPWaves), 0, stream, a, ps, m,
+         k, total);
+  return launch_status();
+}
+
+int run_gemv(const uint16_t* a, const ProjSet& ps, int m, int k, hipStream_t stream) {
+  const int total = ps.strip_end[ps.count - 1];
+  switch ((k / 128 + kPWaves - 1) / kPWaves) {
+    case 1: return launch_gemv<1>(a, ps, m, k, total, stream);
+    case 2: return launch_gemv<2>(a, ps, m, k, total, stream);
+    case 3: return launch_gemv<3>(a, ps, m, k, total, stream);
+    case 4: return launch_gemv<4>(a, ps, m, k, total, stream);
+    case 5: return launch_gemv<5>(a, ps, m, k, total, stream);
+    case 6: return launch_gemv<6>(a, ps, m, k, total, stream);
+    case 7: return launch_gemv<7>(a, ps, m, k, total, stream);
+    case 8: return launch_gemv<8>(a, ps, m, k, total, stream);
+    default: return FP8Q_EINVAL;
+  }
+}
+
+int check_gemv_proj(const uint8_t* w_q, const float* w_scale, const uint16_t* out, int32_t n,
+                    int32_t ldc) {
+  if (n <= 0 || n % 128 != 0 || ldc < n) return FP8Q_EINVAL;
+  if (!w_q || !w_scale || !out) return FP8Q_ENULL;
+  if (!aligned(w_q, 16) || !aligned(w_scale, 4) || !aligned(out, 2)) return FP8Q_EALIGN;
+  return FP8Q_OK;
+}
+
+}  // namespace
+}  // namespace fp8q
+
+using namespace fp8q;
+
+extern "C" int w8a16_block_gemv_grouped(const uint16_t* a, const fp8q_gemm_proj* projs,
+                                        int32_t count, int32_t m, int32_t k,
+                                        hipStream_t stream) {
+  if (count < 1 || count > kMaxProj) return FP8Q_EINVAL;
+  if (m < 1 || m > kGemvMaxRows || k <= 0 || k % 128 != 0 || k > kGemvMaxK) return FP8Q_EINVAL;
+  if (!a || !projs) return FP8Q_ENULL;
+  if (!aligned(a, 16)) return FP8Q_EALIGN;
+  ProjSet ps = {};
+  int64_t end = 0;
+  for (int p = 0; p < count; ++p) {
+    const int rc = check_gemv_proj(projs[p].w_q, projs[p].w_scale, projs[p].out, projs[p].n,
+                                   projs[p].ldc);
+    if (rc != FP8Q_OK) return rc;
+    end += projs[p].n / 16;
+    if (end > 0x7FFFFFFF) return FP8Q_EINVAL;
+    ps.w[p] = projs[p].w_q;
+    ps.ws[p] = projs[p].w_scale;
+    ps.out[p] = projs[p].out;
+    ps.ldc[p] = projs[p].ldc;
+    ps.strip_end[p] = int(end);
+  }
+  ps.count = count;
+  return run_gemv(a, ps, m, k, stream);
+}
+
+extern "C" int w8a16_block_gemv(const uint16_t* a, const uint8_t* w_q, const float* w_scale,
+                                uint16_t* out, int32_t m, int32_t n, int32_t k, int32_t ldc,
+                                hipStream_t stream) {
+  const fp8q_gemm_proj p = {w_q, w_scale, out, n, ldc};
+  return w8a16_block_gemv_grouped(a, &p, 1, m, k, stream);
+}

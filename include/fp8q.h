@@ -152,6 +152,27 @@ int fp8_quant_w8a8_gemm_grouped(const uint16_t* a, uint8_t* a_q, float* a_scale,
                                 const fp8q_gemm_proj* projs, int32_t count, int32_t m,
                                 int32_t k, hipStream_t stream);
 
+/* --------------------------------------------- W8A16 decode tier (1..4 rows)
+ * [decode] module doc NUMERICS (the W8A16 arithmetic: bf16 activation times E4M3 weight
+ * with the same 128x128 FP32 block scales) and DECODE_W8A8_ROWS (up to four rows stay on
+ * this tier).  The activation is not quantized:
+ *   out[r, c] = bf16_rne( sum_g w_scale[c/128, g] * sum_{j<128} a[r, 128g+j] * dec(w_q[c, 128g+j]) )
+ * with exact products and FP32 accumulation (the group's partial, then times its scale).
+ * A row's result does not depend on m (the same row gives the same bits at m = 1..4).
+ * Only rows 0..m-1 are written ((m - 1) * ldc + n elements).
+ *   a        device, bf16 [m, k] row-major, 16-byte aligned
+ *   w_q, w_scale, out, n, ldc  as w8a8_block_gemm
+ *   1 <= m <= 4; n % 128 == 0; k > 0, k % 128 == 0, k <= 8192; ldc >= n.
+ * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EALIGN, FP8Q_ELAUNCH. */
+int w8a16_block_gemv(const uint16_t* a, const uint8_t* w_q, const float* w_scale,
+                     uint16_t* out, int32_t m, int32_t n, int32_t k, int32_t ldc,
+                     hipStream_t stream);
+
+/* Several projections of one bf16 activation in one launch (as w8a8_block_gemm_grouped):
+ * each projs[p] gets exactly what w8a16_block_gemv computes for it. 1 <= count <= 8. */
+int w8a16_block_gemv_grouped(const uint16_t* a, const fp8q_gemm_proj* projs, int32_t count,
+                             int32_t m, int32_t k, hipStream_t stream);
+
 /* --------------------------------------------------------- paged FP8 KV write
  * [staging] Fp8KvWriteTarget and replay_and_release (the write's arguments: strides in
  * elements, pool stride = block_size * heads * head_dim); [staging] module doc: one scale
