@@ -42,8 +42,8 @@ def parse():
     p.add_argument("--iters", type=int, default=100, help="launches per kernel measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="",
-                   help="comma list of sections: step,gemm,grouped,sweep,gemv,quant,kv "
-                        "(default all)")
+                   help="comma list of sections: step,gemm,grouped,sweep,gemv,prefill,quant,"
+                        "kv (default all)")
     return p.parse_args()
 
 
@@ -214,7 +214,7 @@ def main():
     fq.load()
     timer = Timer(torch, fq.load())
     only = (set(args.only.split(",")) if args.only
-            else {"step", "gemm", "grouped", "sweep", "gemv", "quant", "kv"})
+            else {"step", "gemm", "grouped", "sweep", "gemv", "prefill", "quant", "kv"})
     kernels = {}
 
     def log(msg):
@@ -345,6 +345,28 @@ def main():
             log(f"w8a16 gemv m={m} n={n}: {mean_us:.2f} us "
                 f"{kernels[f'w8a16_gemv_m{m}_n{n}_k5120']['gbs']} GB/s")
             del acts, outs
+
+    # --------------------------------------- W8A8 GEMM at the 4593-token prefill width
+    if "prefill" in only:
+        m = synth.PREFILL_TOKENS
+        a = bf16_dev(torch, synth.prefill_activation(K_DECODE, seed=3100))
+        q, s = fq.fp8_group_quant(a)
+        del a
+        for n in (16384, 5120):
+            wq, ws = sets[0]["w"][n]
+            outs = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+            launches = [(lambda o=o: fq.w8a8_block_gemm_prefill(q, s, wq, ws, o)) for o in outs]
+            launches[0]()
+            mean_us, med_us = timer.kernel_us(launches, min(args.iters, 50))
+            fl = 2.0 * m * n * K_DECODE
+            key = f"w8a8_gemm_prefill_m{m}_n{n}_k5120"
+            kernels[key] = dict(us=round(mean_us, 3), us_median=round(med_us, 3),
+                                tflops=round(fl / (mean_us * 1e-6) / 1e12, 1),
+                                frac_mfma_fp8=round(fl / (mean_us * 1e-6) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4))
+            log(f"prefill gemm m={m} n={n}: {mean_us:.1f} us {kernels[key]['tflops']} TFLOP/s "
+                f"({kernels[key]['frac_mfma_fp8']:.3f} of fp8 MFMA peak)")
+            del outs
+        del q, s
 
     # ----------------------------------------------------------- width sweep
     if "sweep" in only:

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     load,
     strerror,
     w8a8_block_gemm,
+    w8a8_block_gemm_prefill,
     w8a8_block_gemm_grouped,
     w8a16_block_gemv,
     w8a16_block_gemv_grouped,

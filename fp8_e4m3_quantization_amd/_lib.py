@@ -21,8 +21,8 @@ FP8Q_CALIB_STAGE, FP8Q_CALIB_DECLINE, FP8Q_CALIB_FREEZE, FP8Q_CALIB_FROZEN = 0, 
 # Every symbol include/fp8q.h declares.
 EXPORTS = (
     "fp8q_strerror", "fp8q_version", "fp8q_time_next_launch", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
-    "w8a8_block_gemm", "w8a8_block_gemm_grouped", "fp8_quant_w8a8_gemm_grouped",
-    "w8a16_block_gemv", "w8a16_block_gemv_grouped", "fp8_kv_write", "fp8_kv_read", "fp8_kv_amax", "fp8q_kv_calib_create",
+    "w8a8_block_gemm", "w8a8_block_gemm_prefill", "w8a8_block_gemm_grouped",
+    "fp8_quant_w8a8_gemm_grouped", "w8a16_block_gemv", "w8a16_block_gemv_grouped", "fp8_kv_write", "fp8_kv_read", "fp8_kv_amax", "fp8q_kv_calib_create",
     "fp8q_kv_calib_observe", "fp8q_kv_calib_decide", "fp8q_kv_calib_scales",
     "fp8q_kv_calib_get_info", "fp8q_kv_calib_destroy",
 )
@@ -86,6 +86,7 @@ def load() -> ctypes.CDLL:
                                                    I32, P]),
         "fp8_quant_w8a8_gemm_grouped": (ctypes.c_int, [P, P, P, ctypes.POINTER(GemmProj), I32,
                                                        I32, I32, P]),
+        "w8a8_block_gemm_prefill": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, P]),
         "w8a16_block_gemv": (ctypes.c_int, [P, P, P, P, I32, I32, I32, I32, P]),
         "w8a16_block_gemv_grouped": (ctypes.c_int, [P, ctypes.POINTER(GemmProj), I32, I32, I32,
                                                     P]),
@@ -192,10 +193,7 @@ def fp8_e4m3_encode(x: torch.Tensor, q: torch.Tensor | None = None,
     return q
 
 
-def w8a8_block_gemm(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tensor,
-                    w_scale: torch.Tensor, out: torch.Tensor | None = None,
-                    ldc: int | None = None, stream: int | None = None) -> torch.Tensor:
-    """E4M3 a_q [m, k] x E4M3 w_q [n, k]^T with block scales -> bf16 out [m, ldc]."""
+def _w8a8(fn, a_q, a_scale, w_q, w_scale, out, ldc, stream):
     m, k = a_q.shape
     n = w_q.shape[0]
     if w_q.shape[1] != k:
@@ -209,12 +207,26 @@ def w8a8_block_gemm(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tensor,
         ldc = out.shape[-1] if ldc is None else ldc
         if out.numel() < (m - 1) * ldc + n:
             raise ValueError("out is smaller than (m - 1) * ldc + n elements")
-    st = load().w8a8_block_gemm(_dev(a_q, "a_q", _U8), _dev(a_scale, "a_scale", torch.float32),
-                                _dev(w_q, "w_q", _U8), _dev(w_scale, "w_scale", torch.float32),
-                                _dev(out, "out", _BF16), m, n, k, ldc,
-                                current_stream(a_q.device) if stream is None else stream)
-    check("w8a8_block_gemm", st)
+    st = getattr(load(), fn)(_dev(a_q, "a_q", _U8), _dev(a_scale, "a_scale", torch.float32),
+                             _dev(w_q, "w_q", _U8), _dev(w_scale, "w_scale", torch.float32),
+                             _dev(out, "out", _BF16), m, n, k, ldc,
+                             current_stream(a_q.device) if stream is None else stream)
+    check(fn, st)
     return out
+
+
+def w8a8_block_gemm(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tensor,
+                    w_scale: torch.Tensor, out: torch.Tensor | None = None,
+                    ldc: int | None = None, stream: int | None = None) -> torch.Tensor:
+    """E4M3 a_q [m <= 16, k] x E4M3 w_q [n, k]^T with block scales -> bf16 out [m, ldc]."""
+    return _w8a8("w8a8_block_gemm", a_q, a_scale, w_q, w_scale, out, ldc, stream)
+
+
+def w8a8_block_gemm_prefill(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tensor,
+                            w_scale: torch.Tensor, out: torch.Tensor | None = None,
+                            ldc: int | None = None, stream: int | None = None) -> torch.Tensor:
+    """The same block-scaled W8A8 GEMM for any row count (tiled for prefill widths)."""
+    return _w8a8("w8a8_block_gemm_prefill", a_q, a_scale, w_q, w_scale, out, ldc, stream)
 
 
 def _proj_array(m, k, projections, device):

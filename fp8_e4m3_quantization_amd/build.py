@@ -13,8 +13,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfp8q.so")
-SOURCES = ["fp8q_api.hip", "fp8q_quant.hip", "fp8q_gemm.hip", "fp8q_gemv.hip", "fp8q_kv.hip",
-           "fp8q_calib.hip"]
+SOURCES = ["fp8q_api.hip", "fp8q_quant.hip", "fp8q_gemm.hip", "fp8q_gemm_prefill.hip",
+           "fp8q_gemv.hip", "fp8q_kv.hip", "fp8q_calib.hip"]
 ARCH = "gfx950"
 
 

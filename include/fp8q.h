@@ -117,6 +117,23 @@ int w8a8_block_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q
                     const float* w_scale, uint16_t* out, int32_t m, int32_t n, int32_t k,
                     int32_t ldc, hipStream_t stream);
 
+/* ------------------------------------------------ W8A8 GEMM at prefill widths
+ * [resid] DenseFp8Inputs::w8a8_kernels (the W8A8 prefill arm: per-token group quant, then
+ * a block-scaled FP8 GEMM); [actq] module doc (a 4593-token prefill).  The arithmetic and
+ * operand layouts are w8a8_block_gemm's; only the row range differs: any m >= 1 (the
+ * kernel is tiled 128 x 128 and fills the chip from a few hundred rows up).
+ *   out[r, c] = bf16_rne( sum_g a_scale[r, g] * w_scale[c/128, g]
+ *                                * sum_{j<128} dec(a_q[r, 128g+j]) * dec(w_q[c, 128g+j]) )
+ * FP32 products and accumulation, one scaled FMA per group.  Only rows 0..m-1 are written
+ * ((m - 1) * ldc + n elements).
+ *   a_q, a_scale, w_q, w_scale, out  as w8a8_block_gemm
+ *   m >= 1; n % 128 == 0; k % 128 == 0, 128 * k < 2^31; ldc >= n (16-byte row stores when
+ *   ldc % 8 == 0 and out is 16-byte aligned, element stores otherwise).
+ * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EALIGN, FP8Q_ELAUNCH. */
+int w8a8_block_gemm_prefill(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
+                            const float* w_scale, uint16_t* out, int32_t m, int32_t n,
+                            int32_t k, int32_t ldc, hipStream_t stream);
+
 /* ---------------------------------------------- grouped W8A8 decode GEMM
  * [decode] decode_w8a8_quant_act: several projections that read the same activation
  * (attention Q/K/V, a layer's projections) share one quantization; DecodeW8a8Plan::strided:

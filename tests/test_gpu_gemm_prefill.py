@@ -1,0 +1,119 @@
+"""GPU parity: the block-scaled W8A8 GEMM at prefill widths against the FP64 oracle.
+
+Bar as for the decode GEMM: |gpu - ref| <= 1e-2 |ref| + 1e-3 rms(ref) per bf16 output (rms
+over the outputs compared); bit-exact where the sums are exact.  Small and ragged shapes
+are compared in full; the 4593-token prefill shape on sampled rows (first, middle, last
+row tiles, the ragged tail) and sampled 128-column blocks, which the oracle computes from
+the same codes and scales."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_e4m3_quantization_amd as fq
+from fp8_e4m3_quantization_amd import synth
+from tests.gpu_util import (DEV, bf16_dev, bf16_host_to_f64, f32_dev, gemm_tolerance_ok,
+                            host, need_gpu, u8_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(_):
+    need_gpu()
+
+
+def _quant(a_bits):
+    q, s = fq.fp8_group_quant(bf16_dev(a_bits))
+    return q, s
+
+
+@pytest.mark.parametrize("m,n,k", [(17, 128, 128), (130, 384, 384), (300, 256, 1152),
+                                   (1, 128, 256), (128, 640, 512), (257, 1024, 256)])
+def test_ragged_shapes_in_full(m, n, k):
+    a = synth.prefill_activation(k, m=m, seed=m * 7 + k)
+    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=n + k))
+    q, s = _quant(a)
+    out = host(fq.w8a8_block_gemm_prefill(q, s, u8_dev(wq), f32_dev(ws)))
+    ref = oracle.gemm(host(q), host(s), wq, ws)
+    ok, worst = gemm_tolerance_ok(out, ref)
+    assert ok, f"worst error / bound = {worst:.3f}"
+
+
+def test_small_integer_sums_are_exact():
+    rng = np.random.default_rng(41)
+    m, n, k = 200, 256, 256
+    codes = np.array([0x00, 0x38, 0x40, 0xB8, 0xC0], dtype=np.uint8)  # 0, 1, 2, -1, -2
+    aq = codes[rng.integers(0, 5, size=(m, k))]
+    wq = codes[rng.integers(0, 5, size=(n, k))]
+    as_ = (2.0 ** rng.integers(-2, 1, size=(m, k // 128))).astype(np.float32)
+    ws = (2.0 ** rng.integers(-2, 1, size=(n // 128, k // 128))).astype(np.float32)
+    out = host(fq.w8a8_block_gemm_prefill(u8_dev(aq), f32_dev(as_), u8_dev(wq), f32_dev(ws)))
+    ref = oracle.gemm(aq, as_, wq, ws)
+    rep = bf16_host_to_f64(synth.to_bf16_bits(ref)) == ref
+    assert rep.mean() > 0.95
+    assert np.array_equal(bf16_host_to_f64(out)[rep], ref[rep])
+
+
+@pytest.mark.parametrize("n", [5120, 16384])
+def test_prefill_shape_on_sampled_outputs(n):
+    k, m = 5120, synth.PREFILL_TOKENS
+    a = synth.prefill_activation(k, seed=3100)
+    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=2100 + n))
+    q, s = _quant(a)
+    out = fq.w8a8_block_gemm_prefill(q, s, u8_dev(wq), f32_dev(ws))
+    got = host(out)
+    qh, sh = host(q), host(s)
+    rows = np.r_[0:8, 125:133, 2300:2308, m - 17:m]
+    blocks = [0, n // 256, n // 128 - 1]
+    for b in blocks:
+        ref = oracle.gemm(np.ascontiguousarray(qh[rows]), np.ascontiguousarray(sh[rows]),
+                          np.ascontiguousarray(wq[b * 128:(b + 1) * 128]),
+                          np.ascontiguousarray(ws[b:b + 1]))
+        ok, worst = gemm_tolerance_ok(got[rows, b * 128:(b + 1) * 128], ref)
+        assert ok, f"block {b}: worst error / bound = {worst:.3f}"
+
+
+def test_agrees_with_the_decode_kernel_on_sixteen_rows():
+    k, n = 5120, 1024
+    a = synth.decode_activation(16, seed=2000)
+    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=2100 + n))
+    q, s = _quant(a)
+    w, sw = u8_dev(wq), f32_dev(ws)
+    pre = host(fq.w8a8_block_gemm_prefill(q, s, w, sw))
+    dec = host(fq.w8a8_block_gemm(q, s, w, sw))
+    ref = oracle.gemm(host(q), host(s), wq, ws)
+    assert gemm_tolerance_ok(pre, ref)[0] and gemm_tolerance_ok(dec, ref)[0]
+    # both are FP32 sums of the same scaled group partials, in different orders
+    assert np.max(np.abs(bf16_host_to_f64(pre) - bf16_host_to_f64(dec))) <= \
+        2.0 ** -7 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("ldc,offset", [(640, 0), (517, 0), (640, 1)])
+def test_strided_and_unaligned_output_writes_exactly_its_extent(ldc, offset):
+    m, n, k = 140, 512, 256
+    a = synth.prefill_activation(k, m=m, seed=9)
+    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=10))
+    q, s = _quant(a)
+    total = offset + m * ldc + 64
+    buf = torch.full((total,), 5.0, dtype=torch.bfloat16, device=DEV)
+    view = buf[offset:]
+    fq.w8a8_block_gemm_prefill(q, s, u8_dev(wq), f32_dev(ws), out=view, ldc=ldc)
+    got = host(buf)
+    mask = np.zeros(total, dtype=bool)
+    for r in range(m):
+        mask[offset + r * ldc: offset + r * ldc + n] = True
+    assert np.all(bf16_host_to_f64(got[~mask]) == 5.0)
+    vals = np.stack([got[offset + r * ldc: offset + r * ldc + n] for r in range(m)])
+    ok, worst = gemm_tolerance_ok(vals, oracle.gemm(host(q), host(s), wq, ws))
+    assert ok, worst
+
+
+@pytest.mark.parametrize("m,n,k,ldc,code", [
+    (0, 128, 128, 128, -1), (4, 100, 128, 128, -1), (4, 128, 100, 128, -1),
+    (4, 256, 128, 128, -1), (4, 128, 1 << 24, 128, -1)])
+def test_invalid_shapes_rejected_before_launch(m, n, k, ldc, code):
+    import ctypes
+    lib = fq.load()
+    p = ctypes.c_void_p(16)
+    assert lib.w8a8_block_gemm_prefill(p, p, p, p, p, m, n, k, ldc, None) == code
+    assert lib.w8a8_block_gemm_prefill(None, p, p, p, p, 4, 128, 128, 128, None) == -2
