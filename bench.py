@@ -97,8 +97,9 @@ def fused_step_gemm_bytes(m, ns, k):
 
 
 def step_bytes():
-    return (fused_step_gemm_bytes(M_DECODE, N_DECODE, K_DECODE)
-            + kv_amax_bytes(M_DECODE) + kv_write_bytes(M_DECODE))
+    """One decode step: the fused quant + GEMM launch, then the KV batch's rows read once for
+    both its absmax and its write (+ the 8-byte running max)."""
+    return fused_step_gemm_bytes(M_DECODE, N_DECODE, K_DECODE) + kv_write_bytes(M_DECODE) + 8
 
 
 # ------------------------------------------------------------------------- timing
@@ -243,8 +244,9 @@ def main():
         fq.fp8_quant_w8a8_gemm_grouped(s["a"], [(s["w"][n][0], s["w"][n][1], s["out"][n])
                                                 for n in N_DECODE], q=s["q"], scales=s["s"])
         cal.observe(s["k"], s["v"], KV_H, KV_D, kc, vc, s["slots"], KV_BS)  # frozen: no-op
-        fq.fp8_kv_amax(s["k"], s["v"], s["amax"])
-        fq.fp8_kv_write(s["k"], s["v"], kc, vc, s["slots"], KV_H, KV_D, KV_BS, k_scale, v_scale)
+        # the batch's K/V absmax and its paged write, one pass over the rows
+        fq.fp8_kv_write_amax(s["k"], s["v"], kc, vc, s["slots"], KV_H, KV_D, KV_BS, k_scale,
+                             v_scale, s["amax"])
 
     result = {}
     if "step" in only:

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     fp8_kv_amax,
     fp8_kv_read,
     fp8_kv_write,
+    fp8_kv_write_amax,
     fp8_quant_w8a8_gemm_grouped,
     load,
     strerror,

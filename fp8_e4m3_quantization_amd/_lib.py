@@ -22,7 +22,7 @@ FP8Q_CALIB_STAGE, FP8Q_CALIB_DECLINE, FP8Q_CALIB_FREEZE, FP8Q_CALIB_FROZEN = 0, 
 EXPORTS = (
     "fp8q_strerror", "fp8q_version", "fp8q_time_next_launch", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
     "w8a8_block_gemm", "w8a8_block_gemm_prefill", "w8a8_block_gemm_grouped",
-    "fp8_quant_w8a8_gemm_grouped", "w8a16_block_gemv", "w8a16_block_gemv_grouped", "fp8_kv_write", "fp8_kv_read", "fp8_kv_amax", "fp8q_kv_calib_create",
+    "fp8_quant_w8a8_gemm_grouped", "w8a16_block_gemv", "w8a16_block_gemv_grouped", "fp8_kv_write", "fp8_kv_write_amax", "fp8_kv_read", "fp8_kv_amax", "fp8q_kv_calib_create",
     "fp8q_kv_calib_observe", "fp8q_kv_calib_decide", "fp8q_kv_calib_scales",
     "fp8q_kv_calib_get_info", "fp8q_kv_calib_destroy",
 )
@@ -92,6 +92,8 @@ def load() -> ctypes.CDLL:
                                                     P]),
         "fp8_kv_write": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, I64, F32, F32,
                                         I32, I32, I64, P]),
+        "fp8_kv_write_amax": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, I64, F32, F32,
+                                             I32, I32, I64, P, P]),
         "fp8_kv_read": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, I64, F32, F32, P, P,
                                        I32, I32, I64, P]),
         "fp8_kv_amax": (ctypes.c_int, [P, P, I64, P, P]),
@@ -326,13 +328,9 @@ def fp8_quant_w8a8_gemm_grouped(a: torch.Tensor, projections, q: torch.Tensor | 
     return outs
 
 
-def fp8_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
-                 v_cache: torch.Tensor, slot_mapping: torch.Tensor, num_kv_heads: int,
-                 head_dim: int, block_size: int, k_scale: float, v_scale: float,
-                 key_stride: int | None = None, value_stride: int | None = None,
-                 cache_stride: int | None = None, num_tokens: int | None = None,
-                 stream: int | None = None) -> None:
-    """Slot-mapped E4M3 scatter of bf16 K/V rows into paged pools [blocks, bs*H*D]."""
+def _kv_write(fn, k, v, k_cache, v_cache, slot_mapping, num_kv_heads, head_dim, block_size,
+              k_scale, v_scale, key_stride, value_stride, cache_stride, num_tokens, stream,
+              extra=()):
     e = num_kv_heads * head_dim
     t = slot_mapping.numel() if num_tokens is None else num_tokens
     key_stride = e if key_stride is None else key_stride
@@ -344,13 +342,40 @@ def fp8_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
     for name, src, stride in (("k", k, key_stride), ("v", v, value_stride)):
         if t > 0 and src.numel() < (t - 1) * stride + e:
             raise ValueError(f"{name} is smaller than its rows")
-    st = load().fp8_kv_write(_dev(k, "k", _BF16, False), _dev(v, "v", _BF16, False),
+    st = getattr(load(), fn)(_dev(k, "k", _BF16, False), _dev(v, "v", _BF16, False),
                              _dev(k_cache, "k_cache", _U8), _dev(v_cache, "v_cache", _U8),
                              _dev(slot_mapping, "slot_mapping", torch.int64), t, num_kv_heads,
                              head_dim, block_size, num_blocks, k_scale, v_scale, key_stride,
-                             value_stride, cache_stride,
+                             value_stride, cache_stride, *extra,
                              current_stream(k.device) if stream is None else stream)
-    check("fp8_kv_write", st)
+    check(fn, st)
+
+
+def fp8_kv_write(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                 v_cache: torch.Tensor, slot_mapping: torch.Tensor, num_kv_heads: int,
+                 head_dim: int, block_size: int, k_scale: float, v_scale: float,
+                 key_stride: int | None = None, value_stride: int | None = None,
+                 cache_stride: int | None = None, num_tokens: int | None = None,
+                 stream: int | None = None) -> None:
+    """Slot-mapped E4M3 scatter of bf16 K/V rows into paged pools [blocks, bs*H*D]."""
+    _kv_write("fp8_kv_write", k, v, k_cache, v_cache, slot_mapping, num_kv_heads, head_dim,
+              block_size, k_scale, v_scale, key_stride, value_stride, cache_stride,
+              num_tokens, stream)
+
+
+def fp8_kv_write_amax(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, slot_mapping: torch.Tensor, num_kv_heads: int,
+                      head_dim: int, block_size: int, k_scale: float, v_scale: float,
+                      amax2: torch.Tensor, key_stride: int | None = None,
+                      value_stride: int | None = None, cache_stride: int | None = None,
+                      num_tokens: int | None = None, stream: int | None = None) -> torch.Tensor:
+    """fp8_kv_write plus the batch's max|K|, max|V| folded into amax2, in one pass."""
+    if amax2.numel() < 2:
+        raise ValueError("amax2 holds two floats")
+    _kv_write("fp8_kv_write_amax", k, v, k_cache, v_cache, slot_mapping, num_kv_heads,
+              head_dim, block_size, k_scale, v_scale, key_stride, value_stride, cache_stride,
+              num_tokens, stream, extra=(_dev(amax2, "amax2", torch.float32),))
+    return amax2
 
 
 def fp8_kv_read(k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: torch.Tensor,

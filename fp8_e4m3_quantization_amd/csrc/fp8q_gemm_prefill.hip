@@ -9,8 +9,9 @@
 //
 // Tiling for gfx950: a 256-thread workgroup owns a 128 x 128 output tile and walks K one
 // 128-wide group at a time, two workgroups per CU.  Each step stages the group's 128 x 128
-// activation and weight codes in LDS (double-buffered, rows padded to 144 bytes so that
-// the MFMA operand reads of 16 rows x 32 bytes hit distinct banks), with the next group's
+// activation and weight codes in LDS (double-buffered; 16-byte chunk c of row r sits at
+// slot c ^ (r & 7) of its 128-byte row, so the MFMA operand reads of 16 rows x 32 bytes and
+// the staging writes spread over all banks), with the next group's
 // buffer loads in flight in registers (rows past the matrix read as zeros).  Wave (wm, wn)
 // of the 2 x 2 grid owns 64 x 64 of the tile: 4 x 4 tiles of v_mfma_f32_16x16x128_f8f6f4,
 // one instruction per tile per group, so every instruction's result is one group's
@@ -34,7 +35,18 @@ namespace fp8q {
 namespace {
 
 constexpr int kBM = 128, kBN = 128, kThreads = 256;
-constexpr int kPitch = 144;               // LDS bytes per staged 128-byte row
+#ifndef FP8Q_PREFILL_SWIZZLE
+#define FP8Q_PREFILL_SWIZZLE 1  // 1: 128-byte rows, 16-byte chunk c of row r at slot c ^ (r & 7)
+#endif
+#ifndef FP8Q_PREFILL_PITCH
+#define FP8Q_PREFILL_PITCH 144
+#endif
+constexpr int kPitch = FP8Q_PREFILL_SWIZZLE ? 128 : FP8Q_PREFILL_PITCH;  // LDS bytes per row
+
+// LDS byte offset of 16-byte chunk c (0..7) of staged row r.
+__device__ __forceinline__ int lds_chunk(int r, int c) {
+  return FP8Q_PREFILL_SWIZZLE ? r * 128 + ((c ^ (r & 7)) << 4) : r * kPitch + (c << 4);
+}
 constexpr int kAStage = kBM * kPitch;     // one group of the activation tile
 constexpr int kBStage = kBN * kPitch;     // one group of the weight tile
 constexpr int kStage = kAStage + kBStage;
@@ -47,9 +59,10 @@ static_assert(kBM * kCPitch * 2 <= 2 * kStage, "output staging reuses the operan
 
 typedef unsigned v4u __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
 
-__device__ __forceinline__ v8i lds_load32(const uint8_t* p) {
-  const v4u x = *reinterpret_cast<const v4u*>(p);
-  const v4u y = *reinterpret_cast<const v4u*>(p + 16);
+// 32 operand bytes of row r: chunks 2h and 2h + 1.
+__device__ __forceinline__ v8i lds_load32(const uint8_t* base, int row, int h) {
+  const v4u x = *reinterpret_cast<const v4u*>(base + lds_chunk(row, 2 * h));
+  const v4u y = *reinterpret_cast<const v4u*>(base + lds_chunk(row, 2 * h + 1));
   v8i r;
   r[0] = int(x[0]); r[1] = int(x[1]); r[2] = int(x[2]); r[3] = int(x[3]);
   r[4] = int(y[0]); r[5] = int(y[1]); r[6] = int(y[2]); r[7] = int(y[3]);
@@ -101,7 +114,7 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_kernel(
   const __amdgpu_buffer_rsrc_t rb_rsrc = tile_rsrc(w_q, n0, n, k);
   const int srow = t >> 3, schunk = (t & 7) * 16;
   const int goff = srow * k + schunk;               // + 32q rows, + 128g bytes
-  const int loff = srow * kPitch + schunk;          // + 32q rows
+  const int loff = lds_chunk(srow, t & 7);          // + 32q rows (same row & 7)
   const float* gs = a_scale + int64_t(min(m0 + (t & (kBM - 1)), m - 1)) * groups;
   const_float* wsp = (const_float*)(w_scale + int64_t(n0 >> 7) * groups);
 
@@ -133,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_kernel(
 
   // operand rows: lane l supplies row (l & 15) and bytes [32*(l>>4), +32) of the group;
   // the accumulator of a 16 x 16 tile holds rows 4*(l>>4) + j, column l & 15
-  const int orow = lane & 15, okoff = (lane >> 4) * 32;
+  const int orow = lane & 15, oh = lane >> 4;
   FP8Q_PREFILL_GLOAD(0);
   FP8Q_PREFILL_LSTORE(0);
   __syncthreads();
@@ -147,14 +160,14 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_kernel(
     float f[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      af[i] = lds_load32(sa + (wm * 64 + i * 16 + orow) * kPitch + okoff);
+      af[i] = lds_load32(sa, wm * 64 + i * 16 + orow, oh);
       const float4 as =
           *reinterpret_cast<const float4*>(&s_as[buf][wm * 64 + i * 16 + (lane >> 4) * 4]);
       f[i][0] = as.x * ws; f[i][1] = as.y * ws; f[i][2] = as.z * ws; f[i][3] = as.w * ws;
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const v8i bf = lds_load32(sb + (wn * 64 + c * 16 + orow) * kPitch + okoff);
+      const v8i bf = lds_load32(sb, wn * 64 + c * 16 + orow, oh);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const v4f p = mfma_group(af[i], bf);

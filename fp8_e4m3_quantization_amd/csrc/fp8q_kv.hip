@@ -139,13 +139,38 @@ __device__ __forceinline__ void store16_nt(uint4 v, uint8_t* p) {
 #endif
 }
 
+// Folds a workgroup's two maxima (K, V) into amax2[0..1]: wave DPP max, one LDS round, one
+// atomic each (skipped when the value there is already at least as large: it only grows).
+template <int kBlock>
+__device__ __forceinline__ void fold_block_max2(float mk, float mv, float* amax2) {
+  __shared__ float red[2][kBlock / 64];
+  const int tid = threadIdx.x;
+  mk = max_over_wave(mk);
+  mv = max_over_wave(mv);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = mk;
+    red[1][tid >> 6] = mv;
+  }
+  __syncthreads();
+  if (tid < 2) {
+    float b = red[tid][0];
+    for (int w = 1; w < kBlock / 64; ++w) b = fmaxf(b, red[tid][w]);
+    unsigned int* dst = reinterpret_cast<unsigned int*>(amax2 + tid);
+    if (b > 0.0f && __float_as_uint(b) > __hip_atomic_load(dst, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(dst, __float_as_uint(b));
+  }
+}
+
 // lpt = 1 << lpt_log2 (2 * lpt divides 64, so lpt is a power of two: lane arithmetic is
-// shifts and masks).
+// shifts and masks).  kAmax: also max-accumulate max|K| and max|V| of every row
+// t < num_tokens (whatever its slot) into amax2, from the same loads.
+template <bool kAmax>
 __global__ __launch_bounds__(kWideBlock) void kv_write_wide_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, uint8_t* __restrict__ kc,
     uint8_t* __restrict__ vc, const int64_t* __restrict__ slots, int64_t num_tokens,
     int lpt_log2, int64_t ks, int64_t vs, int64_t cs, int bs, int64_t nslots, float k_scale,
-    float k_inv, float v_scale, float v_inv) {
+    float k_inv, float v_scale, float v_inv, float* __restrict__ amax2) {
   const int lane = threadIdx.x & 63;
   const int lpt = 1 << lpt_log2;
   const int tpw = 64 >> (lpt_log2 + 1);             // tokens per wave per step
@@ -160,6 +185,7 @@ __global__ __launch_bounds__(kWideBlock) void kv_write_wide_kernel(
   const int64_t wave = (int64_t(blockIdx.x) * kWideBlock + threadIdx.x) >> 6;
   const int64_t nwaves = (int64_t(gridDim.x) * kWideBlock) >> 6;
   const int64_t per_iter = int64_t(tpw) * kWideSteps;
+  float mx = 0.0f;  // kAmax: this lane's running max |x|
   for (int64_t t0 = wave * per_iter; t0 < num_tokens; t0 += nwaves * per_iter) {
     uint4 x0[kWideSteps], x1[kWideSteps];
     int64_t tok[kWideSteps];
@@ -184,8 +210,10 @@ __global__ __launch_bounds__(kWideBlock) void kv_write_wide_kernel(
       const uint2 a = quant8<true>(x0[st], sc, inv);
       const uint2 b = quant8<true>(x1[st], sc, inv);
       if (ok) store16_nt(make_uint4(a.x, a.y, b.x, b.y), dpool + blk * cs + off * e + chunk * 16);
+      if (kAmax && tok[st] < num_tokens) mx = fmaxf(mx, fmaxf(absmax8(x0[st]), absmax8(x1[st])));
     }
   }
+  if constexpr (kAmax) fold_block_max2<kWideBlock>(half ? 0.0f : mx, half ? mx : 0.0f, amax2);
 }
 
 __device__ __forceinline__ uint8_t e4m3_one(float v) {
@@ -422,7 +450,7 @@ int kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t* v_
              const int64_t* slot_mapping, int32_t num_tokens, int32_t heads, int32_t head_dim,
              int32_t block_size, int64_t num_blocks, float k_scale, float v_scale,
              int64_t key_stride, int64_t value_stride, int64_t cache_stride,
-             hipStream_t stream) {
+             hipStream_t stream, float* amax2) {
   const int64_t e = int64_t(heads) * head_dim;
   const int64_t nslots = num_blocks * block_size;
   // reciprocals on the host: IEEE binary32 division, RN(1/scale)
@@ -436,10 +464,21 @@ int kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t* v_
     const int lpt_log2 = __builtin_ctz(unsigned(lpt));
     const int64_t per_block = int64_t(kWideBlock / 64) * (64 / (2 * lpt)) * kWideSteps;
     const int64_t blocks = clamp_grid((int64_t(num_tokens) + per_block - 1) / per_block);
-    launch(kv_write_wide_kernel, dim3(unsigned(blocks)), dim3(kWideBlock), 0, stream, k, v,
-           k_cache, v_cache, slot_mapping, int64_t(num_tokens), lpt_log2, key_stride, value_stride,
-           cache_stride, block_size, nslots, k_scale, k_inv, v_scale, v_inv);
+    if (amax2)
+      launch(kv_write_wide_kernel<true>, dim3(unsigned(blocks)), dim3(kWideBlock), 0, stream,
+             k, v, k_cache, v_cache, slot_mapping, int64_t(num_tokens), lpt_log2, key_stride,
+             value_stride, cache_stride, block_size, nslots, k_scale, k_inv, v_scale, v_inv,
+             amax2);
+    else
+      launch(kv_write_wide_kernel<false>, dim3(unsigned(blocks)), dim3(kWideBlock), 0, stream,
+             k, v, k_cache, v_cache, slot_mapping, int64_t(num_tokens), lpt_log2, key_stride,
+             value_stride, cache_stride, block_size, nslots, k_scale, k_inv, v_scale, v_inv,
+             amax2);
     return launch_status();
+  }
+  if (amax2) {  // other geometries: the absmax pass, then the write
+    const int rc = kv_amax_rows(k, v, num_tokens, e, key_stride, value_stride, amax2, stream);
+    if (rc != FP8Q_OK) return rc;
   }
   const bool vec = e % 8 == 0 && key_stride % 8 == 0 && value_stride % 8 == 0 &&
                    cache_stride % 8 == 0 && aligned(k, 16) && aligned(v, 16) &&
@@ -535,6 +574,23 @@ extern "C" int fp8_kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cac
   return kv_write(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
                   block_size, num_blocks, k_scale, v_scale, key_stride, value_stride,
                   cache_stride, stream);
+}
+
+extern "C" int fp8_kv_write_amax(const uint16_t* k, const uint16_t* v, uint8_t* k_cache,
+                                 uint8_t* v_cache, const int64_t* slot_mapping,
+                                 int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int64_t num_blocks, float k_scale,
+                                 float v_scale, int32_t key_stride, int32_t value_stride,
+                                 int64_t cache_stride, float* amax2, hipStream_t stream) {
+  const int rc = kv_write_check(num_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                                k_scale, v_scale, key_stride, value_stride, cache_stride);
+  if (rc != FP8Q_OK) return rc;
+  if (num_tokens == 0) return FP8Q_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping || !amax2) return FP8Q_ENULL;
+  if (!aligned(slot_mapping, 8) || !aligned(amax2, 4)) return FP8Q_EALIGN;
+  return kv_write(k, v, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                  block_size, num_blocks, k_scale, v_scale, key_stride, value_stride,
+                  cache_stride, stream, amax2);
 }
 
 extern "C" int fp8_kv_amax(const uint16_t* k, const uint16_t* v, int64_t n_elems,

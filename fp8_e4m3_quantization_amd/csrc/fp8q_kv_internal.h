@@ -31,7 +31,7 @@ int kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t* v_
              const int64_t* slot_mapping, int32_t num_tokens, int32_t heads, int32_t head_dim,
              int32_t block_size, int64_t num_blocks, float k_scale, float v_scale,
              int64_t key_stride, int64_t value_stride, int64_t cache_stride,
-             hipStream_t stream);
+             hipStream_t stream, float* amax2 = nullptr);
 
 // out = slots with -1 in place of every token that a later token of the list overwrites
 // (the same slot); the survivors are distinct, so one kv_write of the whole list leaves the

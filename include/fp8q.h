@@ -217,6 +217,22 @@ int fp8_kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t
                  float v_scale, int32_t key_stride, int32_t value_stride,
                  int64_t cache_stride, hipStream_t stream);
 
+/* [calib] Fp8KvCalibration::observe + [staging] module doc, in one pass: inside the
+ * calibration window every batch is both measured (absmax) and written (at the provisional
+ * scale).  Exactly fp8_kv_write(...) followed by fp8_kv_amax over the same batch's rows:
+ *   amax2[0] = max(amax2[0], max |k[t * key_stride + i]|), amax2[1] likewise for v, over
+ *   every t < num_tokens and i < H*D (padding tokens included: the batch's data, as the
+ *   pages' absmax), with the pools written as fp8_kv_write writes them.
+ * One kernel when H*D is a multiple of 16 up to 512 and the rows are 16-byte aligned; else
+ * the absmax pass and the write run back to back.  amax2: device fp32[2], 4-byte aligned.
+ * Errors as fp8_kv_write, and FP8Q_ENULL for a NULL amax2. */
+int fp8_kv_write_amax(const uint16_t* k, const uint16_t* v, uint8_t* k_cache,
+                      uint8_t* v_cache, const int64_t* slot_mapping, int32_t num_tokens,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int64_t num_blocks, float k_scale, float v_scale, int32_t key_stride,
+                      int32_t value_stride, int64_t cache_stride, float* amax2,
+                      hipStream_t stream);
+
 /* ------------------------------------------------------ paged FP8 KV read (dequant)
  * [staging] module doc: every token of a sequence's history is read back at the one
  * per-tensor scale the layer holds (which is why early tokens written at the provisional

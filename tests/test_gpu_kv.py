@@ -296,3 +296,49 @@ def test_read_argument_errors():
         fq.fp8_kv_read(kcd, kcd, s, H, D, BS, 1.0, float("nan"))
     ko, vo = fq.fp8_kv_read(kcd, kcd, s, H, D, BS, 1.0, 1.0, num_tokens=0)
     assert ko.shape == (0, E)
+
+
+# ------------------------------------------------------ write + absmax in one pass
+
+
+@pytest.mark.parametrize("h,d", [(H, D), (2, 64), (3, 5)])
+def test_write_amax_equals_write_then_amax(h, d):
+    """Per batch: pools as fp8_kv_write leaves them, amax2 the running max over every row of
+    the batch -- a padding token's data included (its slot is -1 and it is not written)."""
+    batches, _ = synth.kv_batches(num_tokens_total=300, seed=5030)
+    e = h * d
+    nblk, bs = 64, BS
+    cs = bs * e
+    kc = np.full(nblk * cs, 0x11, dtype=np.uint8)
+    vc = np.full(nblk * cs, 0x22, dtype=np.uint8)
+    kcd, vcd = torch.from_numpy(kc.copy()).to(DEV), torch.from_numpy(vc.copy()).to(DEV)
+    amax2 = torch.zeros(2, dtype=torch.float32, device=DEV)
+    km = vm = np.float32(0.0)
+    for i, b in enumerate(batches):
+        kk = np.ascontiguousarray(b.k[:, :e])
+        vv = np.ascontiguousarray(b.v[:, :e])
+        slots = b.slots % (nblk * bs)
+        if i == 2:
+            slots = slots.copy()
+            slots[0] = -1
+            kk = kk.copy()
+            kk[0, 0] = synth.to_bf16_bits(np.array([-5000.0]))[0]
+        fq.fp8_kv_write_amax(bf16_dev(kk), bf16_dev(vv), kcd, vcd, i64_dev(slots), h, d, bs,
+                             0.375, 0.5, amax2)
+        oracle.kv_write(kk, vv, kc, vc, slots, len(slots), h, d, bs, 0.375, 0.5, e, e, cs)
+        km = max(km, oracle.amax(kk))
+        vm = max(vm, oracle.amax(vv))
+        assert host(amax2).tolist() == [float(km), float(vm)]
+    assert km == synth.bf16_bits_to_f32(synth.to_bf16_bits(np.array([5000.0])))[0]  # 4992
+    assert np.array_equal(host(kcd), kc) and np.array_equal(host(vcd), vc)
+
+
+def test_write_amax_full_pool():
+    b = synth.kv_full_pool()
+    kc, vc, kcd, vcd = _pools()
+    amax2 = torch.zeros(2, dtype=torch.float32, device=DEV)
+    fq.fp8_kv_write_amax(bf16_dev(b.k), bf16_dev(b.v), kcd, vcd, i64_dev(b.slots), H, D, BS,
+                         0.1, 0.2, amax2)
+    oracle.kv_write(b.k, b.v, kc, vc, b.slots, len(b.slots), H, D, BS, 0.1, 0.2, E, E, CS)
+    assert np.array_equal(host(kcd), kc) and np.array_equal(host(vcd), vc)
+    assert host(amax2).tolist() == [float(oracle.amax(b.k)), float(oracle.amax(b.v))]
