@@ -8,19 +8,15 @@
 // block scales, FP32 epilogue).
 //
 // Tiling for gfx950: a 256-thread workgroup owns a 128 x 128 output tile and walks K one
-// 128-wide group at a time, two workgroups per CU.  Each step stages the group's 128 x 128
-// activation and weight codes in LDS (double-buffered; 16-byte chunk c of row r sits at
-// slot c ^ (r & 7) of its 128-byte row, so the MFMA operand reads of 16 rows x 32 bytes and
-// the staging writes spread over all banks), with the next group's
-// buffer loads in flight in registers (rows past the matrix read as zeros).  Wave (wm, wn)
-// of the 2 x 2 grid owns 64 x 64 of the tile: 4 x 4 tiles of v_mfma_f32_16x16x128_f8f6f4,
-// one instruction per tile per group, so every instruction's result is one group's
-// partial and takes its scale product a_scale[row, g] * w_scale[col/128, g] in one FMA
-// per element.  The epilogue stages the bf16 tile through LDS and writes it with 16-byte
-// row-contiguous stores.
-// Workgroups are ordered so that concurrently running ones share operand tiles: 8
-// consecutive row tiles per column tile, and each XCD (workgroup ids are dealt to the 8
-// XCDs round-robin) takes a contiguous stretch of that order for its own L2.
+// 128-wide group at a time, two workgroups per CU.  Each step holds the group's 128 x 128
+// activation and weight codes in LDS (double-buffered).  Wave (wm, wn) of the 2 x 2 grid
+// owns 64 x 64 of the tile: 4 x 4 tiles of v_mfma_f32_16x16x128_f8f6f4, one instruction per
+// tile per group, so every instruction's result is one group's partial and takes its scale
+// a_scale[row, g] * w_scale[col/128, g] in one FMA per element.  The epilogue stages the bf16
+// tile through LDS and writes it with 16-byte row-contiguous stores.  Workgroups are
+// ordered so that concurrently running ones share operand tiles: 8 consecutive row tiles
+// per column tile, and each XCD (workgroup ids are dealt to the 8 XCDs round-robin) takes a
+// contiguous stretch of that order for its own L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,29 +31,26 @@ namespace fp8q {
 namespace {
 
 constexpr int kBM = 128, kBN = 128, kThreads = 256;
-#ifndef FP8Q_PREFILL_SWIZZLE
-#define FP8Q_PREFILL_SWIZZLE 1  // 1: 128-byte rows, 16-byte chunk c of row r at slot c ^ (r & 7)
-#endif
-#ifndef FP8Q_PREFILL_PITCH
-#define FP8Q_PREFILL_PITCH 144
-#endif
-constexpr int kPitch = FP8Q_PREFILL_SWIZZLE ? 128 : FP8Q_PREFILL_PITCH;  // LDS bytes per row
-
-// LDS byte offset of 16-byte chunk c (0..7) of staged row r.
-__device__ __forceinline__ int lds_chunk(int r, int c) {
-  return FP8Q_PREFILL_SWIZZLE ? r * 128 + ((c ^ (r & 7)) << 4) : r * kPitch + (c << 4);
-}
-constexpr int kAStage = kBM * kPitch;     // one group of the activation tile
-constexpr int kBStage = kBN * kPitch;     // one group of the weight tile
+constexpr int kAStage = kBM * 128;        // one group of the activation tile (bytes)
+constexpr int kBStage = kBN * 128;        // one group of the weight tile
 constexpr int kStage = kAStage + kBStage;
 constexpr int kCPitch = kBN + 8;          // bf16 elements per staged output row
-constexpr int kGroupM = 8;                // row tiles per column tile in the walk order
+#ifndef FP8Q_PREFILL_GROUPM
+#define FP8Q_PREFILL_GROUPM 8
+#endif
+constexpr int kGroupM = FP8Q_PREFILL_GROUPM;  // row tiles per column tile in the walk order
 constexpr int kXcds = 8;
-constexpr int kChunksA = kBM * 8 / kThreads;  // 16-byte chunks per thread per group
-constexpr int kChunksB = kBN * 8 / kThreads;
 static_assert(kBM * kCPitch * 2 <= 2 * kStage, "output staging reuses the operand stages");
 
-typedef unsigned v4u __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// LDS byte offset of 16-byte chunk c (0..7) of staged 128-byte row r: the chunk sits at
+// slot c ^ (r & 7) ^ (bit 3 of r).  An MFMA operand read takes one chunk index from 16
+// consecutive rows per 16 lanes: those 16 rows land on 16 distinct 16-byte bank groups of
+// the 256-byte bank row, so the read is conflict-free.
+__device__ __forceinline__ int lds_chunk(int r, int c) {
+  return r * 128 + ((c ^ (r & 7) ^ ((r >> 3) & 1)) << 4);
+}
 
 // 32 operand bytes of row r: chunks 2h and 2h + 1.
 __device__ __forceinline__ v8i lds_load32(const uint8_t* base, int row, int h) {
@@ -84,6 +77,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base,
                                            valid > 0 ? valid * k : 0, kBufferDword3);
 }
 
+// Operand tiles are copied global -> LDS by the buffer unit itself (buffer_load ... lds):
+// no staging registers and no LDS store instructions.  A wave's copy instruction fills one
+// contiguous 1 KB block of LDS, lane L writing bytes [16L, 16L + 16); so lane L of block b
+// loads the global chunk that the swizzle puts at row 8b + L/8, slot L % 8.  Per group: wait
+// for this wave's copies, one barrier, read every operand fragment of the group, start the
+// copies of the next group into the other buffer, then multiply -- the copies run under
+// the MFMAs.  (The copies are issued only after the group's LDS reads: the compiler orders
+// every LDS read after all outstanding copies, so a copy issued earlier would stall them.)
 __global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_kernel(
     const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale,
     const uint8_t* __restrict__ w_q, const float* __restrict__ w_scale,
@@ -92,7 +93,6 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
   __shared__ __attribute__((aligned(16))) float s_as[2][kBM];
 
-  // workgroup -> tile: XCD-contiguous stretches of a row-tile-grouped order
   const int nblk = tiles_m * tiles_n;
   int bid = int(blockIdx.x);
   const int even = nblk - nblk % kXcds;
@@ -106,37 +106,39 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_kernel(
 
   const int t = int(threadIdx.x), lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave >> 1, wn = wave & 1;  // this wave's 64 x 64 quarter of the tile
+  const int wm = wave >> 1, wn = wave & 1;
   const int groups = k >> 7;
 
-  // global -> register staging: thread t moves 16-byte chunk (t & 7) of rows t/8 + 32q
   const __amdgpu_buffer_rsrc_t ra_rsrc = tile_rsrc(a_q, m0, m, k);
   const __amdgpu_buffer_rsrc_t rb_rsrc = tile_rsrc(w_q, n0, n, k);
-  const int srow = t >> 3, schunk = (t & 7) * 16;
-  const int goff = srow * k + schunk;               // + 32q rows, + 128g bytes
-  const int loff = lds_chunk(srow, t & 7);          // + 32q rows (same row & 7)
-  const float* gs = a_scale + int64_t(min(m0 + (t & (kBM - 1)), m - 1)) * groups;
+  // wave w fills blocks b = w + 4q (q < 4) of each operand stage: rows 8b .. 8b + 7
+  int voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int b = wave + 4 * q, r = 8 * b + (lane >> 3);
+    const int c = (lane & 7) ^ (lane >> 3) ^ (b & 1);  // lds_chunk(r, c) == b*1024 + 16*lane
+    voff[q] = r * k + c * 16;
+  }
+  // activation scales: wave w copies rows 32w .. 32w + 31 of column g (lanes 0..31)
+  const float* gsp = a_scale + int64_t(min(m0 + 32 * wave + (lane & 31), m - 1)) * groups;
   const_float* wsp = (const_float*)(w_scale + int64_t(n0 >> 7) * groups);
 
-  v4u ra[kChunksA], rb[kChunksB];
-  float rs = 0.0f;
-#define FP8Q_PREFILL_GLOAD(g)                                                              \
-  do {                                                                                     \
-    _Pragma("unroll") for (int q = 0; q < kChunksA; ++q) ra[q] =                           \
-        __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, goff + q * 32 * k + (g) * 128, 0, 0); \
-    _Pragma("unroll") for (int q = 0; q < kChunksB; ++q) rb[q] =                           \
-        __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, goff + q * 32 * k + (g) * 128, 0, 0); \
-    if (t < kBM) rs = gs[g];                                                               \
-  } while (0)
-#define FP8Q_PREFILL_LSTORE(buf)                                                           \
-  do {                                                                                     \
-    uint8_t* base_ = lds + (buf) * kStage;                                                 \
-    _Pragma("unroll") for (int q = 0; q < kChunksA; ++q)                                   \
-        *reinterpret_cast<v4u*>(base_ + loff + q * 32 * kPitch) = ra[q];                   \
-    _Pragma("unroll") for (int q = 0; q < kChunksB; ++q)                                   \
-        *reinterpret_cast<v4u*>(base_ + kAStage + loff + q * 32 * kPitch) = rb[q];         \
-    if (t < kBM) s_as[buf][t] = rs;                                                        \
-  } while (0)
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto copy_group = [&](int buf, int g) {
+    uint8_t* base = lds + buf * kStage;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra_rsrc, (lds_void*)(base + (wave + 4 * q) * 1024),
+                                               16, voff[q], g * 128, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb_rsrc, (lds_void*)(base + kAStage + (wave + 4 * q) * 1024), 16, voff[q], g * 128,
+          0, 0);
+    if (lane < 32)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(gsp + g),
+                                       (lds_void*)(&s_as[buf][32 * wave]), 4, 0, 0);
+  };
 
   v4f acc[4][4];
 #pragma unroll
@@ -144,44 +146,40 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[i][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // operand rows: lane l supplies row (l & 15) and bytes [32*(l>>4), +32) of the group;
-  // the accumulator of a 16 x 16 tile holds rows 4*(l>>4) + j, column l & 15
   const int orow = lane & 15, oh = lane >> 4;
-  FP8Q_PREFILL_GLOAD(0);
-  FP8Q_PREFILL_LSTORE(0);
-  __syncthreads();
+  copy_group(0, 0);
   for (int g = 0; g < groups; ++g) {
     const int buf = g & 1;
-    if (g + 1 < groups) FP8Q_PREFILL_GLOAD(g + 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of group g landed
+    __syncthreads();                     // ... and everyone's; buffer buf^1 is free again
     const uint8_t* sa = lds + buf * kStage;
     const uint8_t* sb = sa + kAStage;
     const float ws = wsp[g];
-    v8i af[4];
-    float f[4][4];
+    v8i af[4], bf[4];
+    float4 as[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       af[i] = lds_load32(sa, wm * 64 + i * 16 + orow, oh);
-      const float4 as =
-          *reinterpret_cast<const float4*>(&s_as[buf][wm * 64 + i * 16 + (lane >> 4) * 4]);
-      f[i][0] = as.x * ws; f[i][1] = as.y * ws; f[i][2] = as.z * ws; f[i][3] = as.w * ws;
+      as[i] = *reinterpret_cast<const float4*>(&s_as[buf][wm * 64 + i * 16 + oh * 4]);
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const v8i bf = lds_load32(sb, wn * 64 + c * 16 + orow, oh);
+    for (int c = 0; c < 4; ++c) bf[c] = lds_load32(sb, wn * 64 + c * 16 + orow, oh);
+    if (g + 1 < groups) copy_group(buf ^ 1, g + 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v4f p = mfma_group(af[i], bf);
+    for (int i = 0; i < 4; ++i) {
+      const float f0 = as[i].x * ws, f1 = as[i].y * ws, f2 = as[i].z * ws, f3 = as[i].w * ws;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][c][j] = __builtin_fmaf(p[j], f[i][j], acc[i][c][j]);
+      for (int c = 0; c < 4; ++c) {
+        const v4f p = mfma_group(af[i], bf[c]);
+        acc[i][c][0] = __builtin_fmaf(p[0], f0, acc[i][c][0]);
+        acc[i][c][1] = __builtin_fmaf(p[1], f1, acc[i][c][1]);
+        acc[i][c][2] = __builtin_fmaf(p[2], f2, acc[i][c][2]);
+        acc[i][c][3] = __builtin_fmaf(p[3], f3, acc[i][c][3]);
       }
     }
-    if (g + 1 < groups) FP8Q_PREFILL_LSTORE(buf ^ 1);
-    __syncthreads();
   }
-#undef FP8Q_PREFILL_GLOAD
-#undef FP8Q_PREFILL_LSTORE
+  __syncthreads();  // every wave is done reading the last stage before it is reused
 
-  // epilogue: bf16 tile staged in LDS, then 16-byte row-contiguous stores
   uint16_t* sc = reinterpret_cast<uint16_t*>(lds);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -189,7 +187,7 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_kernel(
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = wm * 64 + i * 16 + (lane >> 4) * 4 + j;
+        const int r = wm * 64 + i * 16 + oh * 4 + j;
         const int col = wn * 64 + c * 16 + (lane & 15);
         sc[r * kCPitch + col] = f32_to_bf16_rne(acc[i][c][j]);
       }
