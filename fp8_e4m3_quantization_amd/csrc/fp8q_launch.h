@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+
 #include "fp8q.h"
 
 namespace fp8q {
@@ -26,16 +28,31 @@ struct LaunchEvents {
 };
 inline thread_local LaunchEvents g_next_launch_events;
 
-// Every kernel of the library is enqueued through here.
-template <typename Kernel, typename... Args>
-inline void launch(Kernel kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
-                   Args... args) {
+// Status of the last launch this host thread enqueued through launch().
+inline thread_local hipError_t g_last_launch = hipSuccess;
+
+// Every kernel of the library is enqueued through here.  The arguments are converted to the
+// kernel's own parameter types and handed to hipLaunchKernel / hipExtLaunchKernel, whose
+// return value is this launch's status (an error left by an earlier, unrelated HIP call on
+// the thread is neither reported nor cleared).
+template <typename... KArgs, typename... Args>
+inline void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds,
+                   hipStream_t stream, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+  std::tuple<KArgs...> packed(static_cast<KArgs>(args)...);
+  void* argv[sizeof...(KArgs) + 1];
+  std::apply([&](auto&... a) {
+    int i = 0;
+    ((argv[i++] = static_cast<void*>(&a)), ...);
+  }, packed);
   const LaunchEvents ev = g_next_launch_events;
   if (ev.start || ev.stop) {
     g_next_launch_events = LaunchEvents();
-    hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, ev.start, ev.stop, 0, args...);
+    g_last_launch = hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv,
+                                       lds, stream, ev.start, ev.stop, 0);
   } else {
-    hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+    g_last_launch =
+        hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds, stream);
   }
 }
 
@@ -55,8 +72,6 @@ inline int num_cus() {
 }
 
 // Status of the launch just enqueued on this thread.
-inline int launch_status() {
-  return hipGetLastError() == hipSuccess ? FP8Q_OK : FP8Q_ELAUNCH;
-}
+inline int launch_status() { return g_last_launch == hipSuccess ? FP8Q_OK : FP8Q_ELAUNCH; }
 
 }  // namespace fp8q
