@@ -33,7 +33,7 @@ typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 
 constexpr int kGemvMaxRows = 4;
 constexpr int kGemvRound = 4;  // strips per LDS reduction
-constexpr int kGemvMaxK = kPWaves * 8 * 128;
+constexpr int kGemvMaxK = kPWaves * 8 * 128;  // the persistent form holds <= 8 groups per wave
 
 // Two E4M3 codes (bytes 0,1 or 2,3 of w) -> two bf16 in one word: the binary32 decode is
 // exact and its top half is the bf16 value (no rounding: three mantissa bits).
@@ -157,6 +157,71 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a16_persistent_kernel(
   }
 }
 
+// Long-K form (k > 8192): one 8-wave workgroup per 16-column strip; wave w walks a
+// contiguous 1/8 of the K-groups kChunk at a time (weights through the strip's buffer
+// descriptor, activation fragments from L2), then the 8 partials meet in LDS.  Same
+// operand layout and per-group arithmetic as the persistent kernel.
+constexpr int kGemvLongChunk = 4;
+constexpr int kGemvLongMaxK = 131072;
+
+__global__ __launch_bounds__(64 * kPWaves) void w8a16_long_kernel(const uint16_t* __restrict__ a,
+                                                                  ProjSet ps, int m, int k) {
+  __shared__ float s_part[kPWaves * 64];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int groups = k >> 7;
+  int p, n0;
+  locate_strip(ps, int(blockIdx.x), &p, &n0);
+  const __amdgpu_buffer_rsrc_t r = make_strip_rsrc(ps.w[p] + int64_t(n0) * k, k, true);
+  const_float* wsp = (const_float*)(ps.ws[p] + int64_t(n0 >> 7) * groups);
+  const int row = lane & 15, koff = (lane >> 4) * 32;
+  const int arow = row < m ? row : m - 1;
+  const uint4* ap = reinterpret_cast<const uint4*>(a + int64_t(arow) * k + koff);
+  const int g_begin = (groups * wv) / kPWaves, g_end = (groups * (wv + 1)) / kPWaves;
+
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int g = g_begin; g < g_end; g += kGemvLongChunk) {
+    v8i wb[kGemvLongChunk];
+    uint4 af[kGemvLongChunk][4];
+    float ws[kGemvLongChunk];
+#pragma unroll
+    for (int u = 0; u < kGemvLongChunk; ++u) {
+      const int gu = min(g + u, g_end - 1);  // a short chunk re-reads its last group
+      wb[u] = buffer_load32<0>(r, row * k + koff + gu * 128);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[u][i] = ap[gu * 16 + i];
+      ws[u] = wsp[gu];
+    }
+#pragma unroll
+    for (int u = 0; u < kGemvLongChunk; ++u) {
+      if (g + u < g_end) {  // wave-uniform
+        v4f c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(v8bf16, af[u][i]),
+              widen8(uint32_t(wb[u][2 * i]), uint32_t(wb[u][2 * i + 1])), c, 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(c[q], ws[u], acc[q]);
+      }
+    }
+  }
+  // partials of lanes 0..15 (the stored rows) meet in LDS; fixed summation order
+  if (lane < 16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_part[(wv * 4 + q) * 16 + lane] = acc[q];
+  }
+  __syncthreads();
+  const int t = int(threadIdx.x);
+  if (t < 64) {
+    const int q = t >> 4, c = t & 15;
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kPWaves; ++w) sum += s_part[(w * 4 + q) * 16 + c];
+    if (q < m) ps.out[p][int64_t(q) * ps.ldc[p] + n0 + c] = f32_to_bf16_rne(sum);
+  }
+}
+
 template <int kGpw>
 int launch_gemv(const uint16_t* a, const ProjSet& ps, int m, int k, int total,
                 hipStream_t stream) {
@@ -168,6 +233,10 @@ int launch_gemv(const uint16_t* a, const ProjSet& ps, int m, int k, int total,
 
 int run_gemv(const uint16_t* a, const ProjSet& ps, int m, int k, hipStream_t stream) {
   const int total = ps.strip_end[ps.count - 1];
+  if (k > kGemvMaxK) {
+    launch(w8a16_long_kernel, dim3(unsigned(total)), dim3(64 * kPWaves), 0, stream, a, ps, m, k);
+    return launch_status();
+  }
   switch ((k / 128 + kPWaves - 1) / kPWaves) {
     case 1: return launch_gemv<1>(a, ps, m, k, total, stream);
     case 2: return launch_gemv<2>(a, ps, m, k, total, stream);
@@ -198,7 +267,8 @@ extern "C" int w8a16_block_gemv_grouped(const uint16_t* a, const fp8q_gemm_proj*
                                         int32_t count, int32_t m, int32_t k,
                                         hipStream_t stream) {
   if (count < 1 || count > kMaxProj) return FP8Q_EINVAL;
-  if (m < 1 || m > kGemvMaxRows || k <= 0 || k % 128 != 0 || k > kGemvMaxK) return FP8Q_EINVAL;
+  if (m < 1 || m > kGemvMaxRows || k <= 0 || k % 128 != 0 || k > kGemvLongMaxK)
+    return FP8Q_EINVAL;
   if (!a || !projs) return FP8Q_ENULL;
   if (!aligned(a, 16)) return FP8Q_EALIGN;
   ProjSet ps = {};

@@ -179,7 +179,9 @@ int fp8_quant_w8a8_gemm_grouped(const uint16_t* a, uint8_t* a_q, float* a_scale,
  * Only rows 0..m-1 are written ((m - 1) * ldc + n elements).
  *   a        device, bf16 [m, k] row-major, 16-byte aligned
  *   w_q, w_scale, out, n, ldc  as w8a8_block_gemm
- *   1 <= m <= 4; n % 128 == 0; k > 0, k % 128 == 0, k <= 8192; ldc >= n.
+ *   1 <= m <= 4; n % 128 == 0; k > 0, k % 128 == 0, k <= 131072; ldc >= n.
+ *   (k <= 8192 runs a persistent kernel that keeps the activation in registers; longer k
+ *   a per-strip kernel that reads it from L2.  Both sum in a fixed order per k.)
  * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EALIGN, FP8Q_ELAUNCH. */
 int w8a16_block_gemv(const uint16_t* a, const uint8_t* w_q, const float* w_scale,
                      uint16_t* out, int32_t m, int32_t n, int32_t k, int32_t ldc,

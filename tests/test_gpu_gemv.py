@@ -53,11 +53,23 @@ def test_decode_projections_within_bound(n, m):
 
 
 @pytest.mark.parametrize("m", [2, 3])
-@pytest.mark.parametrize("k", [128, 384, 1152, 8192])
+@pytest.mark.parametrize("k", [128, 384, 1152, 8192, 8320, 16384, 20608])
 def test_row_counts_and_ragged_k(m, k):
+    """k <= 8192 runs the persistent kernel, longer k the per-strip long-K kernel (20608 =
+    161 groups: the 8 waves' slices and their last 4-group chunks are uneven)."""
     n = 384
     wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=k + m))
     a = synth.decode_activation(m, k=k, seed=k * 3 + m)
+    out = host(fq.w8a16_block_gemv(bf16_dev(a), u8_dev(wq), f32_dev(ws)))
+    ref, mag = oracle.gemm_w8a16(a, wq, ws)
+    ok, worst = _within(out, ref, mag, k)
+    assert ok, f"worst error / bound = {worst:.3f}"
+
+
+def test_longest_k_within_bound():
+    k, n, m = 131072, 128, 4
+    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=41))
+    a = synth.decode_activation(m, k=k, seed=42)
     out = host(fq.w8a16_block_gemv(bf16_dev(a), u8_dev(wq), f32_dev(ws)))
     ref, mag = oracle.gemm_w8a16(a, wq, ws)
     ok, worst = _within(out, ref, mag, k)
@@ -143,7 +155,7 @@ def test_strided_output_writes_exactly_its_extent():
 
 @pytest.mark.parametrize("m,n,k,ldc,code", [
     (0, 128, 128, 128, -1), (5, 128, 128, 128, -1), (1, 100, 128, 128, -1),
-    (1, 128, 100, 128, -1), (1, 128, 8320, 128, -1), (1, 256, 128, 128, -1)])
+    (1, 128, 100, 128, -1), (1, 128, 131200, 128, -1), (1, 256, 128, 128, -1)])
 def test_invalid_shapes_rejected_before_launch(m, n, k, ldc, code):
     import ctypes
     lib = fq.load()
