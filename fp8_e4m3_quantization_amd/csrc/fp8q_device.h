@@ -22,23 +22,34 @@ __device__ __forceinline__ float clip448(float v) {
   return __builtin_amdgcn_fmed3f(v, -kE4M3Max, kE4M3Max);
 }
 
-// Four finite binary32 values -> four E4M3 codes, a in byte 0 ... d in byte 3.
+// Four finite binary32 values -> four E4M3 codes, a in byte 0 ... d in byte 3.  With
+// kSaturate the values are clipped to +-448 first; without it the caller guarantees
+// |v| < 464: gfx950's v_cvt_pk_fp8_f32 rounds such magnitudes to at most 448 (464 is the
+// midpoint between 448 and the NaN code's slot; farther out it produces the NaN code).
+template <bool kSaturate>
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clip448(a), clip448(b), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(clip448(c), clip448(d), w, true);
+  if constexpr (kSaturate) {
+    a = clip448(a); b = clip448(b); c = clip448(c); d = clip448(d);
+  }
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return uint32_t(w);
 }
 
 // Eight bf16 (one 16-byte load) divided by a scale and packed into eight E4M3 codes.
-// `clipped` selects the estimate clip needed when the scale may be far below |x|/448.
-template <bool kClipped>
+//   kBounded: group quantization, every |x| <= amax and s = RN(max(amax, 1e-10) / 448).
+//     Then |x / s| <= 448 / (1 - 2^-24), so RN(x / s) <= 448 + ulp(448): the estimate needs
+//     no clip and the converter rounds the quotient to at most 448 (no saturation step).
+//   otherwise: any scale (the KV cache's per-tensor scale may be far below |x| / 448): the
+//     estimate is clipped so that inf - inf cannot occur and the result saturates at +-448.
+template <bool kBounded>
 __device__ __forceinline__ uint2 quant8(uint4 w, float s, float y) {
   auto dq = [&](float x) {
-    return kClipped ? div_by_scale_clipped(x, s, y) : div_by_scale(x, s, y);
+    return kBounded ? div_by_scale(x, s, y) : div_by_scale_clipped(x, s, y);
   };
   uint2 r;
-  r.x = e4m3x4(dq(bf16_lo(w.x)), dq(bf16_hi(w.x)), dq(bf16_lo(w.y)), dq(bf16_hi(w.y)));
-  r.y = e4m3x4(dq(bf16_lo(w.z)), dq(bf16_hi(w.z)), dq(bf16_lo(w.w)), dq(bf16_hi(w.w)));
+  r.x = e4m3x4<!kBounded>(dq(bf16_lo(w.x)), dq(bf16_hi(w.x)), dq(bf16_lo(w.y)), dq(bf16_hi(w.y)));
+  r.y = e4m3x4<!kBounded>(dq(bf16_lo(w.z)), dq(bf16_hi(w.z)), dq(bf16_lo(w.w)), dq(bf16_hi(w.w)));
   return r;
 }
 

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(64 * kWaves) void w8a8_gemm_kernel(
 #define FP8Q_GEMM_AUX 0
 #endif
 #ifndef FP8Q_GEMM_NT_OUT
-#define FP8Q_GEMM_NT_OUT 1  // bf16 outputs written with the non-temporal hint
+#define FP8Q_GEMM_NT_OUT 0  // 1: bf16 outputs written with the non-temporal hint
 #endif
 
 template <int kGpw>
@@ -173,14 +173,14 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
   static_assert(kRound % (kDepth + 1) == 0, "buffer index must be static within a round");
   static_assert(kRound * 256 == kPWaves * 64 * 2, "reduce: two outputs per lane");
   __shared__ float s_part[2][kRound * kPWaves * 4 * 64];
+  __shared__ uint4 s_tile[kPWaves * ActTile<kQuant ? 16 : 8>::kUints];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int groups = k >> 7;
   const int g0 = (groups * wv) / kPWaves;
   const int cnt = (groups * (wv + 1)) / kPWaves - g0;  // 0 <= cnt <= kGpw
   const int row = lane & 15, koff = (lane >> 4) * 32;
-  const int arow = row < m ? row : m - 1;  // activation loads stay in bounds
-  int goff[kGpw];  // byte offset of slice group u (a short slice re-reads its last group,
+  int goff[kGpw];  // first k of slice group u (a short slice re-reads its last group,
                    // whose activation fragment below is zero)
 #pragma unroll
   for (int u = 0; u < kGpw; ++u) goff[u] = (g0 + max(0, min(u, cnt - 1))) * 128;
@@ -198,25 +198,27 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
   };
 
   const int stride = int(gridDim.x);
-  const int first = int(blockIdx.x);
+  const int first = first_strip(int(blockIdx.x), stride);
   const int nit = (total_strips - first + stride - 1) / stride;
   if (nit <= 0) return;
 
   // 1) raw activation loads, 2) the first weight prefetch, 3) activation fragments: the
   // fragments wait only for the loads issued before the prefetch, so the weight stream
-  // starts without waiting for the activation (load counters retire in order).
+  // starts without waiting for the activation (load counters retire in order).  The
+  // activation tiles reach the fragments through LDS (ActTile).
+  using Tile = ActTile<kQuant ? 16 : 8>;
+  uint4* tile = s_tile + wv * Tile::kUints;
   v8i a[kGpw];
   float4 as[kGpw];
   Slice<kGpw> buf[kDepth + 1];
   const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
   const int r0 = 4 * (lane >> 4);
   if constexpr (!kQuant) {
-    v8i raw[kGpw];
+    v4u raw[kGpw][Tile::kLoads];
     float4 rs[kGpw];
-    const uint8_t* ap = act.a_q + int64_t(arow) * k + koff;
 #pragma unroll
     for (int u = 0; u < kGpw; ++u) {
-      raw[u] = load32(ap + goff[u]);
+      Tile::load(act.a_q + goff[u], k, m, lane, raw[u]);
       const int g = goff[u] >> 7;
       rs[u].x = act.a_scale[int64_t(min(r0 + 0, m - 1)) * groups + g];
       rs[u].y = act.a_scale[int64_t(min(r0 + 1, m - 1)) * groups + g];
@@ -229,21 +231,23 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
 #pragma unroll
     for (int u = 0; u < kGpw; ++u) {
       const bool live = u < cnt;
-      a[u] = (live && row < m) ? raw[u] : zero8;
+      uint4 f[2];
+      Tile::exchange(tile, raw[u], lane, koff >> 4, f);
+      const v8i fr = {int(f[0].x), int(f[0].y), int(f[0].z), int(f[0].w),
+                      int(f[1].x), int(f[1].y), int(f[1].z), int(f[1].w)};
+      a[u] = (live && row < m) ? fr : zero8;
       as[u].x = (live && r0 + 0 < m) ? rs[u].x : 0.0f;
       as[u].y = (live && r0 + 1 < m) ? rs[u].y : 0.0f;
       as[u].z = (live && r0 + 2 < m) ? rs[u].z : 0.0f;
       as[u].w = (live && r0 + 3 < m) ? rs[u].w : 0.0f;
     }
   } else {
-    // lane l holds elements [32*(l>>4), +32) of row (l & 15) in each slice group: the four
+    // lane l gets elements [32*(l>>4), +32) of row (l & 15) in each slice group: the four
     // lanes l, l^16, l^32, l^48 together hold the row's 128-element group
-    uint4 raw[kGpw][4];
-    const uint4* xp = reinterpret_cast<const uint4*>(act.a_bf16 + int64_t(arow) * k + koff);
+    v4u stage[kGpw][Tile::kLoads];
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(act.a_bf16);
 #pragma unroll
-    for (int u = 0; u < kGpw; ++u)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) raw[u][c] = xp[(goff[u] >> 3) + c];
+    for (int u = 0; u < kGpw; ++u) Tile::load(xb + 2 * goff[u], 2 * int64_t(k), m, lane, stage[u]);
 #pragma unroll
     for (int j = 0; j < kDepth; ++j) fetch(first + j * stride, buf[j]);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the activation math
@@ -251,14 +255,16 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
 #pragma unroll
     for (int u = 0; u < kGpw; ++u) {
       const bool live = u < cnt;
-      float amax = fmaxf(fmaxf(absmax8(raw[u][0]), absmax8(raw[u][1])),
-                         fmaxf(absmax8(raw[u][2]), absmax8(raw[u][3])));
+      uint4 raw[4];
+      Tile::exchange(tile, stage[u], lane, koff >> 3, raw);
+      float amax = fmaxf(fmaxf(absmax8(raw[0]), absmax8(raw[1])),
+                         fmaxf(absmax8(raw[2]), absmax8(raw[3])));
       amax = fmaxf(amax, __shfl_xor(amax, 16));
       amax = fmaxf(amax, __shfl_xor(amax, 32));
       const float sc = group_scale_from_amax(amax);
       const float y = 1.0f / sc;  // IEEE division: RN(1/s)
-      const uint2 c0 = quant8<false>(raw[u][0], sc, y), c1 = quant8<false>(raw[u][1], sc, y);
-      const uint2 c2 = quant8<false>(raw[u][2], sc, y), c3 = quant8<false>(raw[u][3], sc, y);
+      const uint2 c0 = quant8<true>(raw[0], sc, y), c1 = quant8<true>(raw[1], sc, y);
+      const uint2 c2 = quant8<true>(raw[2], sc, y), c3 = quant8<true>(raw[3], sc, y);
       v8i f;
       f[0] = int(c0.x); f[1] = int(c0.y); f[2] = int(c1.x); f[3] = int(c1.y);
       f[4] = int(c2.x); f[5] = int(c2.y); f[6] = int(c3.x); f[7] = int(c3.y);

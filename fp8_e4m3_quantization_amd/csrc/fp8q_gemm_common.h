@@ -68,4 +68,65 @@ __device__ __forceinline__ v8i buffer_load32(__amdgpu_buffer_rsrc_t r, int off) 
   return o;
 }
 
+// ---------------------------------------------------------------------------------
+// Where a workgroup starts.  Block b walks strips first, first + grid, ...  Workgroups are
+// dealt to the chip's 8 XCDs round robin (block b runs on XCD b % 8), so with the plain
+// order first = b the 16-column strips of one 128-column output block land on 8 different
+// XCDs, and each XCD's L2 holds only 32-byte pieces of every output row.  When the grid is
+// a multiple of 64, blocks are permuted so that every run of 8 adjacent strips belongs to
+// the 8 blocks of a single XCD (the strips of a run are processed at the same time, so
+// that L2 gathers whole output lines before writing them back).
+__device__ __forceinline__ int first_strip(int b, int grid) {
+  if (grid % 64 != 0) return b;
+  const int xcd = b & 7, k = b >> 3;     // k-th block of XCD xcd
+  return (((k >> 3) * 8 + xcd) << 3) | (k & 7);
+}
+
+// ---------------------------------------------------------------------------------
+// Activation fragments through LDS.  The MFMA operand layout gives lane l row (l & 15) and
+// 32 consecutive k of a 128-wide group; loaded straight from global memory every load
+// instruction would touch 16 rows in partial lines, while every workgroup on the chip
+// reads the same activation at the same time.  Instead a wave reads a group's 16-row
+// tile row-major (16 bytes per lane, whole rows per instruction), passes it through a
+// wave-private LDS tile and reads its own fragment back.  The tile is swizzled so that
+// the row-major writes and the fragment reads are both free of bank conflicts.  A wave's
+// LDS operations complete in program order, so the tile is reused group after group with
+// no barrier.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+template <int kChunks>  // 16-byte chunks per tile row: 8 (E4M3 codes) or 16 (bf16)
+struct ActTile {
+  static_assert(kChunks == 8 || kChunks == 16, "tile rows of 128 or 256 bytes");
+  static constexpr int kLoads = 16 * kChunks / 64;  // 16-byte loads per lane per tile
+  static constexpr int kUints = 16 * kChunks;       // tile size in 16-byte chunks
+  __device__ static int row(int t, int lane) { return t * (64 / kChunks) + lane / kChunks; }
+  __device__ static int slot(int r, int c) {
+    return kChunks == 8 ? (c ^ (r & 7) ^ ((r >> 3) & 1)) : (c ^ r);
+  }
+  // Global reads of one tile: `group` is the group's first byte in row 0, rows are `pitch`
+  // bytes apart; rows >= m repeat row m - 1 (in bounds; their fragments are never used).
+  __device__ static void load(const uint8_t* group, int64_t pitch, int m, int lane,
+                              v4u (&out)[kLoads]) {
+#pragma unroll
+    for (int t = 0; t < kLoads; ++t) {
+      const int r = min(row(t, lane), m - 1);
+      out[t] = *reinterpret_cast<const v4u*>(group + r * pitch + 16 * (lane % kChunks));
+    }
+  }
+  // Tile -> LDS, then the lane's kFrag chunks first_chunk, first_chunk + 1, ... of row
+  // (lane & 15).
+  template <int kFrag>
+  __device__ static void exchange(uint4* tile, const v4u (&in)[kLoads], int lane,
+                                  int first_chunk, uint4 (&frag)[kFrag]) {
+#pragma unroll
+    for (int t = 0; t < kLoads; ++t) {
+      const int r = row(t, lane);
+      tile[r * kChunks + slot(r, lane % kChunks)] = make_uint4(in[t][0], in[t][1], in[t][2], in[t][3]);
+    }
+    const int r = lane & 15;
+#pragma unroll
+    for (int i = 0; i < kFrag; ++i) frag[i] = tile[r * kChunks + slot(r, first_chunk + i)];
+  }
+};
+
 }  // namespace fp8q

@@ -66,13 +66,13 @@ template <int kGpw>
 __global__ __launch_bounds__(64 * kPWaves) void w8a16_persistent_kernel(
     const uint16_t* __restrict__ a, ProjSet ps, int m, int k, int total_strips) {
   __shared__ float s_part[2][kGemvRound * kPWaves * 64];
+  __shared__ uint4 s_tile[kPWaves * ActTile<16>::kUints];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int groups = k >> 7;
   const int g0 = (groups * wv) / kPWaves;
   const int cnt = (groups * (wv + 1)) / kPWaves - g0;  // 0 <= cnt <= kGpw
   const int row = lane & 15, koff = (lane >> 4) * 32;
-  const int arow = row < m ? row : m - 1;  // rows >= m repeat row m-1 (in bounds, unused)
   int goff[kGpw];  // first k of slice group u (a short slice repeats its last group; the
                    // repeat is skipped in the multiply)
 #pragma unroll
@@ -91,19 +91,32 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a16_persistent_kernel(
   };
 
   const int stride = int(gridDim.x);
-  const int first = int(blockIdx.x);
+  const int first = first_strip(int(blockIdx.x), stride);
   const int nit = (total_strips - first + stride - 1) / stride;
   if (nit <= 0) return;
 
-  // activation fragments first (they stay in registers), then the first weight prefetch
-  uint4 af[kGpw][4];
-  const uint4* ap = reinterpret_cast<const uint4*>(a + int64_t(arow) * k + koff);
+  // activation tiles first, then the first weight prefetch, then the fragments (through
+  // LDS, see ActTile; they stay in registers for the whole launch)
+  using Tile = ActTile<16>;
+  v4u stage[kGpw][Tile::kLoads];
+  const uint8_t* ab = reinterpret_cast<const uint8_t*>(a);
 #pragma unroll
-  for (int u = 0; u < kGpw; ++u)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[u][i] = ap[(goff[u] >> 3) + i];
+  for (int u = 0; u < kGpw; ++u) Tile::load(ab + 2 * goff[u], 2 * int64_t(k), m, lane, stage[u]);
   GemvSlice<kGpw> buf[2];
-  fetch(first, buf[0]);
+  uint4 af[kGpw][4];
+  auto exchange_all = [&]() {
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u)
+      Tile::exchange(s_tile + wv * Tile::kUints, stage[u], lane, koff >> 3, af[u]);
+  };
+  if constexpr (kGpw <= 6) {
+    fetch(first, buf[0]);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the fragment exchange
+    exchange_all();
+  } else {  // staged tiles, fragments and a prefetched slice would not fit in registers
+    exchange_all();
+    fetch(first, buf[0]);
+  }
 
   auto multiply = [&](const GemvSlice<kGpw>& cur) {
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};

@@ -104,15 +104,15 @@ __global__ __launch_bounds__(kKvBlock) void kv_write_vec_kernel(
       for (int i = 0; i < kTokPerWave; ++i) {
         if (ok[i]) {
 #if FP8Q_KV_NT_STORE
-          const uint2 kq = quant8<true>(kx[i], k_scale, k_inv);
-          const uint2 vq = quant8<true>(vx[i], v_scale, v_inv);
+          const uint2 kq = quant8<false>(kx[i], k_scale, k_inv);
+          const uint2 vq = quant8<false>(vx[i], v_scale, v_inv);
           __builtin_nontemporal_store(uint64_t(kq.x) | (uint64_t(kq.y) << 32),
                                       reinterpret_cast<uint64_t*>(kc + dst[i] + c));
           __builtin_nontemporal_store(uint64_t(vq.x) | (uint64_t(vq.y) << 32),
                                       reinterpret_cast<uint64_t*>(vc + dst[i] + c));
 #else
-          kc[dst[i] + c] = quant8<true>(kx[i], k_scale, k_inv);
-          vc[dst[i] + c] = quant8<true>(vx[i], v_scale, v_inv);
+          kc[dst[i] + c] = quant8<false>(kx[i], k_scale, k_inv);
+          vc[dst[i] + c] = quant8<false>(vx[i], v_scale, v_inv);
 #endif
         }
       }
@@ -207,8 +207,8 @@ __global__ __launch_bounds__(kWideBlock) void kv_write_wide_kernel(
       int64_t blk = 0, off = 0;
       const int64_t tl = tok[st] < num_tokens ? tok[st] : num_tokens - 1;
       const bool ok = tok[st] < num_tokens && slot_to_block(slots[tl], nslots, bs, &blk, &off);
-      const uint2 a = quant8<true>(x0[st], sc, inv);
-      const uint2 b = quant8<true>(x1[st], sc, inv);
+      const uint2 a = quant8<false>(x0[st], sc, inv);
+      const uint2 b = quant8<false>(x1[st], sc, inv);
       if (ok) store16_nt(make_uint4(a.x, a.y, b.x, b.y), dpool + blk * cs + off * e + chunk * 16);
       if (kAmax && tok[st] < num_tokens) mx = fmaxf(mx, fmaxf(absmax8(x0[st]), absmax8(x1[st])));
     }

@@ -76,8 +76,8 @@ __global__ __launch_bounds__(kQuantBlock) void group_quant_kernel(
       const float amax = max_over_8_lanes(fmaxf(absmax8(w0[t]), absmax8(w1[t])));
       const float s = group_scale_from_amax(amax);
       const float y = 1.0f / s;  // IEEE division: RN(1/s)
-      const uint2 c0 = quant8<false>(w0[t], s, y);
-      const uint2 c1 = quant8<false>(w1[t], s, y);
+      const uint2 c0 = quant8<true>(w0[t], s, y);
+      const uint2 c1 = quant8<true>(w1[t], s, y);
       if (g[t] < num_groups) {
 #if FP8Q_QUANT_NT_STORE
         uint64_t* qp = reinterpret_cast<uint64_t*>(q + g[t] * 8 + sub);
