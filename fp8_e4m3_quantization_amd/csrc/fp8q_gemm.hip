@@ -158,7 +158,7 @@ struct Slice {
 // Where the activation comes from: already quantized (codes + token-major scales), or
 // bf16, quantized by the GEMM itself (each wave quantizes its own K-slice in registers
 // with the group quantizer's arithmetic, so the codes are bit-identical to
-// fp8_group_quant's; workgroup 0 optionally writes them out).
+// fp8_group_quant's; optionally they are written out, each workgroup a share).
 struct ActSrc {
   const uint8_t* a_q;
   const float* a_scale;
@@ -210,6 +210,7 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
   uint4* tile = s_tile + wv * Tile::kUints;
   v8i a[kGpw];
   float4 as[kGpw];
+  float scv[kGpw];  // kQuant: this lane's row scale of each slice group
   Slice<kGpw> buf[kDepth + 1];
   const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
   const int r0 = 4 * (lane >> 4);
@@ -251,7 +252,6 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
 #pragma unroll
     for (int j = 0; j < kDepth; ++j) fetch(first + j * stride, buf[j]);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the activation math
-    const bool write_out = blockIdx.x == 0 && act.q_out != nullptr;
 #pragma unroll
     for (int u = 0; u < kGpw; ++u) {
       const bool live = u < cnt;
@@ -276,14 +276,27 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
       as[u].y = (live && r0 + 1 < m) ? s1 : 0.0f;
       as[u].z = (live && r0 + 2 < m) ? s2 : 0.0f;
       as[u].w = (live && r0 + 3 < m) ? s3 : 0.0f;
-      if (write_out && live && row < m) {
-        uint4* qo = reinterpret_cast<uint4*>(act.q_out + int64_t(row) * k + goff[u] + koff);
-        qo[0] = make_uint4(c0.x, c0.y, c1.x, c1.y);
-        qo[1] = make_uint4(c2.x, c2.y, c3.x, c3.y);
-        if (lane < 16) act.s_out[int64_t(row) * groups + (goff[u] >> 7)] = sc;
-      }
+      scv[u] = sc;
     }
   }
+
+  // Optional code/scale output of the fused quantization.  Every workgroup holds every code
+  // (a[u] of the lanes of row (l & 15)), so the (row, group) tiles are dealt round robin
+  // over the workgroups and each writes its share.  The stores are issued once the first
+  // round's fetches and multiplies are issued: stores retire through the same in-order
+  // counter as loads, so earlier they would hold up the waits for the first strips.
+  auto write_codes = [&]() {
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u) {
+      const int g = goff[u] >> 7;
+      if (u < cnt && row < m && (row * groups + g) % stride == int(blockIdx.x)) {
+        uint4* qo = reinterpret_cast<uint4*>(act.q_out + int64_t(row) * k + goff[u] + koff);
+        qo[0] = make_uint4(uint32_t(a[u][0]), uint32_t(a[u][1]), uint32_t(a[u][2]), uint32_t(a[u][3]));
+        qo[1] = make_uint4(uint32_t(a[u][4]), uint32_t(a[u][5]), uint32_t(a[u][6]), uint32_t(a[u][7]));
+        if (lane < 16) act.s_out[int64_t(row) * groups + g] = scv[u];
+      }
+    }
+  };
 
   auto multiply = [&](const Slice<kGpw>& cur) {
     v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -311,6 +324,9 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) part[((j * kPWaves + wv) * 4 + q) * 64 + lane] = acc[q];
       }
+    }
+    if constexpr (kQuant) {
+      if (i == 0 && act.q_out != nullptr) write_codes();
     }
     lds_barrier();
     // Reduce: wave w owns half of round strip w/2 (128 of its 256 outputs, 2 per lane).
