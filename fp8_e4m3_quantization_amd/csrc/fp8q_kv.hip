@@ -139,10 +139,19 @@ __device__ __forceinline__ void store16_nt(uint4 v, uint8_t* p) {
 #endif
 }
 
+// The value of amax2[which] as the kernel starts, read by the thread that later folds into
+// it.  The slot only grows, so this early read is never larger than the slot's value at
+// fold time: skipping the atomic when the block's maximum does not exceed it stays
+// correct, and the read's latency hides under the kernel's own loads.
+__device__ __forceinline__ float seen_max(float* amax2, int which) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<unsigned int*>(amax2 + which),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 // Folds a workgroup's two maxima (K, V) into amax2[0..1]: wave DPP max, one LDS round, one
-// atomic each (skipped when the value there is already at least as large: it only grows).
+// atomic each (skipped when `seen`, thread t's seen_max(amax2, t), is already as large).
 template <int kBlock>
-__device__ __forceinline__ void fold_block_max2(float mk, float mv, float* amax2) {
+__device__ __forceinline__ void fold_block_max2(float mk, float mv, float* amax2, float seen) {
   __shared__ float red[2][kBlock / 64];
   const int tid = threadIdx.x;
   mk = max_over_wave(mk);
@@ -155,10 +164,8 @@ __device__ __forceinline__ void fold_block_max2(float mk, float mv, float* amax2
   if (tid < 2) {
     float b = red[tid][0];
     for (int w = 1; w < kBlock / 64; ++w) b = fmaxf(b, red[tid][w]);
-    unsigned int* dst = reinterpret_cast<unsigned int*>(amax2 + tid);
-    if (b > 0.0f && __float_as_uint(b) > __hip_atomic_load(dst, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT))
-      atomicMax(dst, __float_as_uint(b));
+    if (b > 0.0f && __float_as_uint(b) > __float_as_uint(seen))
+      atomicMax(reinterpret_cast<unsigned int*>(amax2 + tid), __float_as_uint(b));
   }
 }
 
@@ -186,6 +193,7 @@ __global__ __launch_bounds__(kWideBlock) void kv_write_wide_kernel(
   const int64_t nwaves = (int64_t(gridDim.x) * kWideBlock) >> 6;
   const int64_t per_iter = int64_t(tpw) * kWideSteps;
   float mx = 0.0f;  // kAmax: this lane's running max |x|
+  const float seen = (kAmax && threadIdx.x < 2) ? seen_max(amax2, int(threadIdx.x)) : 0.0f;
   for (int64_t t0 = wave * per_iter; t0 < num_tokens; t0 += nwaves * per_iter) {
     uint4 x0[kWideSteps], x1[kWideSteps];
     int64_t tok[kWideSteps];
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(kWideBlock) void kv_write_wide_kernel(
       if (kAmax && tok[st] < num_tokens) mx = fmaxf(mx, fmaxf(absmax8(x0[st]), absmax8(x1[st])));
     }
   }
-  if constexpr (kAmax) fold_block_max2<kWideBlock>(half ? 0.0f : mx, half ? mx : 0.0f, amax2);
+  if constexpr (kAmax) fold_block_max2<kWideBlock>(half ? 0.0f : mx, half ? mx : 0.0f, amax2, seen);
 }
 
 __device__ __forceinline__ uint8_t e4m3_one(float v) {
@@ -372,7 +380,8 @@ __global__ __launch_bounds__(64) void kv_mark_superseded_kernel(
 
 // Folds a workgroup's maximum into amax2[which]: one LDS reduction, then a single atomic,
 // skipped when the value already there is at least as large (it only grows).
-__device__ __forceinline__ void fold_block_max(float m, float* amax2, int which) {
+// seen: seen_max(amax2, which) as read by thread 0 at kernel start.
+__device__ __forceinline__ void fold_block_max(float m, float* amax2, int which, float seen) {
   __shared__ float red[kKvBlock / 64];
   const int tid = threadIdx.x + threadIdx.y * blockDim.x;
   m = max_over_wave(m);
@@ -381,10 +390,8 @@ __device__ __forceinline__ void fold_block_max(float m, float* amax2, int which)
   if (tid == 0) {
     float b = red[0];
     for (int w = 1; w < kKvBlock / 64; ++w) b = fmaxf(b, red[w]);
-    unsigned int* dst = reinterpret_cast<unsigned int*>(amax2 + which);
-    if (b > 0.0f && __float_as_uint(b) > __hip_atomic_load(dst, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT))
-      atomicMax(dst, __float_as_uint(b));
+    if (b > 0.0f && __float_as_uint(b) > __float_as_uint(seen))
+      atomicMax(reinterpret_cast<unsigned int*>(amax2 + which), __float_as_uint(b));
   }
 }
 
@@ -395,6 +402,7 @@ __global__ __launch_bounds__(kKvBlock) void amax_flat_kernel(const uint4* __rest
                                                              int64_t n8,
                                                              float* __restrict__ amax2) {
   const uint4* x = blockIdx.y ? v : k;
+  const float seen = threadIdx.x == 0 ? seen_max(amax2, int(blockIdx.y)) : 0.0f;
   const int64_t stride = int64_t(gridDim.x) * kKvBlock;
   float m = 0.0f;
   int64_t i = int64_t(blockIdx.x) * kKvBlock + threadIdx.x;
@@ -403,7 +411,7 @@ __global__ __launch_bounds__(kKvBlock) void amax_flat_kernel(const uint4* __rest
     m = fmaxf(m, fmaxf(fmaxf(absmax8(a), absmax8(b)), fmaxf(absmax8(c), absmax8(d))));
   }
   for (; i < n8; i += stride) m = fmaxf(m, absmax8(x[i]));
-  fold_block_max(m, amax2, blockIdx.y);
+  fold_block_max(m, amax2, blockIdx.y, seen);
 }
 
 // max |x| over `rows` rows of `row_elems` bf16 at row strides ks / vs (any alignment).
@@ -414,12 +422,13 @@ __global__ __launch_bounds__(kKvBlock) void amax_rows_kernel(const uint16_t* __r
                                                              float* __restrict__ amax2) {
   const uint16_t* x = blockIdx.y ? v : k;
   const int64_t s = blockIdx.y ? vs : ks;
+  const float seen = (threadIdx.x == 0 && threadIdx.y == 0) ? seen_max(amax2, int(blockIdx.y)) : 0.0f;
   float m = 0.0f;
   for (int64_t r = int64_t(blockIdx.x) * kRowsPerBlock + threadIdx.y; r < rows;
        r += int64_t(gridDim.x) * kRowsPerBlock)
     for (int c = threadIdx.x; c < row_elems; c += 64)
       m = fmaxf(m, fabsf(bf16_to_f32(x[r * s + c])));
-  fold_block_max(m, amax2, blockIdx.y);
+  fold_block_max(m, amax2, blockIdx.y, seen);
 }
 
 }  // namespace
