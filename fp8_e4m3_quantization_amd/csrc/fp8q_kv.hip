@@ -29,7 +29,7 @@ namespace {
 
 constexpr int kKvBlock = 256;
 #ifndef FP8Q_KV_WIDE_BLOCK
-#define FP8Q_KV_WIDE_BLOCK 256
+#define FP8Q_KV_WIDE_BLOCK 512
 #endif
 constexpr int kWideBlock = FP8Q_KV_WIDE_BLOCK;  // threads per block of the wide write
 
@@ -263,6 +263,10 @@ __global__ __launch_bounds__(kKvBlock) void kv_write_scalar_kernel(
 #define FP8Q_KV_READ_NT_STORE 1  // bf16 rows written with the non-temporal hint
 #endif
 constexpr int kReadUnroll = FP8Q_KV_READ_UNROLL;
+#ifndef FP8Q_KV_READ_BLOCK
+#define FP8Q_KV_READ_BLOCK 256
+#endif
+constexpr int kReadBlock = FP8Q_KV_READ_BLOCK;  // threads per block of the vector read
 
 __device__ __forceinline__ void store16_bf16(uint4 a, uint16_t* p) {
 #if FP8Q_KV_READ_NT_STORE
@@ -286,14 +290,14 @@ __device__ __forceinline__ uint4 dequant8_finite(uint2 w, float s) {
 // Idx is uint32_t when every item index and slot fits in 31 bits, else uint64_t; kPow2:
 // ipt is a power of two (ipt_log2 its exponent), so token and chunk are a shift and a mask.
 template <typename Idx, bool kPow2>
-__global__ __launch_bounds__(kKvBlock) void kv_read_vec_kernel(
+__global__ __launch_bounds__(kReadBlock) void kv_read_vec_kernel(
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const int64_t* __restrict__ slots, Idx items, uint32_t ipt, uint32_t ipt_log2, int64_t cs,
     uint32_t bs, int64_t nslots, float k_scale, float v_scale, uint16_t* __restrict__ ko,
     uint16_t* __restrict__ vo, int64_t kos, int64_t vos) {
-  const Idx nthreads = Idx(gridDim.x) * kKvBlock;
+  const Idx nthreads = Idx(gridDim.x) * kReadBlock;
   const int64_t e = int64_t(8) * ipt;
-  for (Idx i0 = Idx(blockIdx.x) * kKvBlock + threadIdx.x; i0 < items;
+  for (Idx i0 = Idx(blockIdx.x) * kReadBlock + threadIdx.x; i0 < items;
        i0 += nthreads * kReadUnroll) {
     Idx tok[kReadUnroll], c[kReadUnroll];
     int64_t slot[kReadUnroll];
@@ -381,15 +385,16 @@ __global__ __launch_bounds__(64) void kv_mark_superseded_kernel(
 // Folds a workgroup's maximum into amax2[which]: one LDS reduction, then a single atomic,
 // skipped when the value already there is at least as large (it only grows).
 // seen: seen_max(amax2, which) as read by thread 0 at kernel start.
+template <int kBlock>
 __device__ __forceinline__ void fold_block_max(float m, float* amax2, int which, float seen) {
-  __shared__ float red[kKvBlock / 64];
+  __shared__ float red[kBlock / 64];
   const int tid = threadIdx.x + threadIdx.y * blockDim.x;
   m = max_over_wave(m);
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
   if (tid == 0) {
     float b = red[0];
-    for (int w = 1; w < kKvBlock / 64; ++w) b = fmaxf(b, red[w]);
+    for (int w = 1; w < kBlock / 64; ++w) b = fmaxf(b, red[w]);
     if (b > 0.0f && __float_as_uint(b) > __float_as_uint(seen))
       atomicMax(reinterpret_cast<unsigned int*>(amax2 + which), __float_as_uint(b));
   }
@@ -397,21 +402,28 @@ __device__ __forceinline__ void fold_block_max(float m, float* amax2, int which,
 
 // max |x| over a packed run of n8 16-byte words; blockIdx.y picks K (0) or V (1).  Four
 // independent 16-byte loads per thread per step keep enough bytes in flight.
-__global__ __launch_bounds__(kKvBlock) void amax_flat_kernel(const uint4* __restrict__ k,
+#ifndef FP8Q_AMAX_BLOCK
+#define FP8Q_AMAX_BLOCK 1024
+#endif
+#ifndef FP8Q_AMAX_MAX_BLOCKS
+#define FP8Q_AMAX_MAX_BLOCKS 4096  // per tensor
+#endif
+constexpr int kAmaxBlock = FP8Q_AMAX_BLOCK;
+__global__ __launch_bounds__(kAmaxBlock) void amax_flat_kernel(const uint4* __restrict__ k,
                                                              const uint4* __restrict__ v,
                                                              int64_t n8,
                                                              float* __restrict__ amax2) {
   const uint4* x = blockIdx.y ? v : k;
   const float seen = threadIdx.x == 0 ? seen_max(amax2, int(blockIdx.y)) : 0.0f;
-  const int64_t stride = int64_t(gridDim.x) * kKvBlock;
+  const int64_t stride = int64_t(gridDim.x) * kAmaxBlock;
   float m = 0.0f;
-  int64_t i = int64_t(blockIdx.x) * kKvBlock + threadIdx.x;
+  int64_t i = int64_t(blockIdx.x) * kAmaxBlock + threadIdx.x;
   for (; i + 3 * stride < n8; i += 4 * stride) {
     const uint4 a = x[i], b = x[i + stride], c = x[i + 2 * stride], d = x[i + 3 * stride];
     m = fmaxf(m, fmaxf(fmaxf(absmax8(a), absmax8(b)), fmaxf(absmax8(c), absmax8(d))));
   }
   for (; i < n8; i += stride) m = fmaxf(m, absmax8(x[i]));
-  fold_block_max(m, amax2, blockIdx.y, seen);
+  fold_block_max<kAmaxBlock>(m, amax2, blockIdx.y, seen);
 }
 
 // max |x| over `rows` rows of `row_elems` bf16 at row strides ks / vs (any alignment).
@@ -428,7 +440,7 @@ __global__ __launch_bounds__(kKvBlock) void amax_rows_kernel(const uint16_t* __r
        r += int64_t(gridDim.x) * kRowsPerBlock)
     for (int c = threadIdx.x; c < row_elems; c += 64)
       m = fmaxf(m, fabsf(bf16_to_f32(x[r * s + c])));
-  fold_block_max(m, amax2, blockIdx.y, seen);
+  fold_block_max<kKvBlock>(m, amax2, blockIdx.y, seen);
 }
 
 }  // namespace
@@ -440,9 +452,9 @@ int kv_amax_rows(const uint16_t* k, const uint16_t* v, int64_t rows, int64_t row
   if (key_stride == row_elems && value_stride == row_elems && n % 8 == 0 && aligned(k, 16) &&
       aligned(v, 16)) {
     // four 16-byte words per thread per step; enough blocks to fill every CU
-    int64_t blocks = (n / 8 + 4 * kKvBlock - 1) / (4 * kKvBlock);
-    if (blocks > 4096) blocks = 4096;
-    launch(amax_flat_kernel, dim3(unsigned(blocks), 2), dim3(kKvBlock), 0, stream,
+    int64_t blocks = (n / 8 + 4 * kAmaxBlock - 1) / (4 * kAmaxBlock);
+    if (blocks > FP8Q_AMAX_MAX_BLOCKS) blocks = FP8Q_AMAX_MAX_BLOCKS;
+    launch(amax_flat_kernel, dim3(unsigned(blocks), 2), dim3(kAmaxBlock), 0, stream,
                        reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
                        n / 8, amax2);
   } else {
@@ -534,7 +546,7 @@ static int kv_read(const uint8_t* k_cache, const uint8_t* v_cache, const int64_t
                    aligned(k_out, 16) && aligned(v_out, 16) && e / 8 <= 0x7FFFFFFF;
   if (vec) {
     const int64_t items = int64_t(num_tokens) * (e / 8);
-    const int64_t per_block = int64_t(kKvBlock) * kReadUnroll;
+    const int64_t per_block = int64_t(kReadBlock) * kReadUnroll;
     const int64_t blocks = clamp_grid((items + per_block - 1) / per_block);
     // 32-bit indices when no item index the loop forms (< 2 * items + per_block) and no
     // slot can wrap
@@ -543,12 +555,12 @@ static int kv_read(const uint8_t* k_cache, const uint8_t* v_cache, const int64_t
     const uint32_t ipt_log2 = uint32_t(__builtin_ctz(ipt));
     if (items < (int64_t(1) << 31) - per_block && nslots <= 0x7FFFFFFF) {
       auto kern = pow2 ? kv_read_vec_kernel<uint32_t, true> : kv_read_vec_kernel<uint32_t, false>;
-      launch(kern, dim3(unsigned(blocks)), dim3(kKvBlock), 0, stream, k_cache, v_cache,
+      launch(kern, dim3(unsigned(blocks)), dim3(kReadBlock), 0, stream, k_cache, v_cache,
              slot_mapping, uint32_t(items), ipt, ipt_log2, cache_stride, uint32_t(block_size),
              nslots, k_scale, v_scale, k_out, v_out, out_key_stride, out_value_stride);
     } else {
       auto kern = pow2 ? kv_read_vec_kernel<uint64_t, true> : kv_read_vec_kernel<uint64_t, false>;
-      launch(kern, dim3(unsigned(blocks)), dim3(kKvBlock), 0, stream, k_cache, v_cache,
+      launch(kern, dim3(unsigned(blocks)), dim3(kReadBlock), 0, stream, k_cache, v_cache,
              slot_mapping, uint64_t(items), ipt, ipt_log2, cache_stride, uint32_t(block_size),
              nslots, k_scale, v_scale, k_out, v_out, out_key_stride, out_value_stride);
     }
