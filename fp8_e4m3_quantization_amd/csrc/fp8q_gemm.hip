@@ -282,9 +282,9 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
 
   // Optional code/scale output of the fused quantization.  Every workgroup holds every code
   // (a[u] of the lanes of row (l & 15)), so the (row, group) tiles are dealt round robin
-  // over the workgroups and each writes its share.  The stores are issued once the first
-  // round's fetches and multiplies are issued: stores retire through the same in-order
-  // counter as loads, so earlier they would hold up the waits for the first strips.
+  // over the workgroups and each writes its share.  The stores go out in the last round,
+  // after its fetches and multiplies are issued: stores retire through the same in-order
+  // counter as loads, so any strip waited for after them would wait for them too.
   auto write_codes = [&]() {
 #pragma unroll
     for (int u = 0; u < kGpw; ++u) {
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
       }
     }
     if constexpr (kQuant) {
-      if (i == 0 && act.q_out != nullptr) write_codes();
+      if (i + kRound >= nit && act.q_out != nullptr) write_codes();  // the last round
     }
     lds_barrier();
     // Reduce: wave w owns half of round strip w/2 (128 of its 256 outputs, 2 per lane).
