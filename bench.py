@@ -13,7 +13,8 @@ measured step time (GB/s).
 Also measured (same process, same rotation rule): each kernel on its own, timed with HIP
 events around every launch while the stream is held busy so no host latency leaks into
 an interval -- the group quantizer on the 4593-token prefill (K = 5120 and 16384), the
-GEMM at each N, the quant+GEMM pair at M = 5, 8, 12, 16 (N = 16384), and the KV write and
+GEMM at each N, the quant+GEMM pair at M = 5, 8, 12, 16 (N = 16384; as two launches and as
+one fused launch), and the KV write and
 absmax over a full 2048-block pool.  The roofline object covers the step's dominant
 kernel (the fused quant + four-projection GEMM); cpu_baseline times the CPU oracle on one
 full step.
@@ -401,18 +402,27 @@ def main():
             lg = [(lambda i=i: fq.w8a8_block_gemm(qs[i], ss[i], sets[i]["w"][n][0],
                                                   sets[i]["w"][n][1], outs[i]))
                   for i in range(len(sets))]
+            # the same pair as one launch: group quant fused into the GEMM
+            lf = [(lambda i=i: fq.fp8_quant_w8a8_gemm_grouped(
+                acts[i], [(sets[i]["w"][n][0], sets[i]["w"][n][1], outs[i])]))
+                  for i in range(len(sets))]
             for f in lq:
                 f()
             tq, _ = timer.kernel_us(lq, args.iters)
             tg, _ = timer.kernel_us(lg, args.iters)
+            tf, _ = timer.kernel_us(lf, args.iters)
             wb = gemm_weight_bytes(n, K_DECODE)
             t = tq + tg
             sweep[str(m)] = dict(us_quant=round(tq, 3), us_gemm=round(tg, 3), us=round(t, 3),
                                  weight_gbs=round(wb / (t * 1e-6) / 1e9, 1),
                                  frac_hbm=round(wb / (t * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                                 gemm_gbs=round(gemm_bytes(m, n, K_DECODE) / (tg * 1e-6) / 1e9, 1))
+                                 gemm_gbs=round(gemm_bytes(m, n, K_DECODE) / (tg * 1e-6) / 1e9, 1),
+                                 us_fused=round(tf, 3),
+                                 weight_gbs_fused=round(wb / (tf * 1e-6) / 1e9, 1),
+                                 frac_hbm_fused=round(wb / (tf * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
             log(f"sweep m={m}: quant {tq:.2f} us + gemm {tg:.2f} us, "
-                f"{sweep[str(m)]['weight_gbs']} GB/s of weights")
+                f"{sweep[str(m)]['weight_gbs']} GB/s of weights; fused in one launch "
+                f"{tf:.2f} us, {sweep[str(m)]['weight_gbs_fused']} GB/s of weights")
         kernels["quant_gemm_pair_n16384_k5120"] = sweep
 
     # ------------------------------------------------------------- prefill quant
