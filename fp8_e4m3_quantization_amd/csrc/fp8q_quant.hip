@@ -80,9 +80,9 @@ __global__ __launch_bounds__(kQuantBlock) void group_quant_kernel(
       const uint2 c1 = quant8<true>(w1[t], s, y);
       if (g[t] < num_groups) {
 #if FP8Q_QUANT_NT_STORE
-        uint64_t* qp = reinterpret_cast<uint64_t*>(q + g[t] * 8 + sub);
-        __builtin_nontemporal_store(uint64_t(c0.x) | (uint64_t(c0.y) << 32), qp);
-        __builtin_nontemporal_store(uint64_t(c1.x) | (uint64_t(c1.y) << 32), qp + 1);
+        typedef unsigned v4u __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(v4u{c0.x, c0.y, c1.x, c1.y},
+                                    reinterpret_cast<v4u*>(q + g[t] * 8 + sub));
 #else
         q[g[t] * 8 + sub] = make_uint4(c0.x, c0.y, c1.x, c1.y);
 #endif
