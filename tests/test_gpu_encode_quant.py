@@ -109,6 +109,30 @@ def test_group_quant_ties_through_the_whole_path():
     _assert_quant_equal(x)
 
 
+def test_group_quant_amax_quotient_just_above_448():
+    """Groups whose scale RN(amax/448) rounds down: the amax element's binary32 quotient
+    RN(amax/s) is then just above 448 (448 + ulp), and it must still encode as the max code
+    0x7E / 0xFE (the group quantizer feeds such quotients to the converter unclipped)."""
+    rng = np.random.default_rng(448)
+    cand = synth.to_bf16_bits(rng.uniform(0.01, 1000.0, size=4096))
+    amax = synth.bf16_bits_to_f32(cand).astype(np.float32)
+    s = amax / np.float32(448.0)                  # binary32 division, as the pages compute it
+    over = (amax / s) > np.float32(448.0)
+    assert over.sum() > 100                       # the case is common, so it is well covered
+    picks = cand[over][:64]
+    rows = []
+    for i, b in enumerate(picks):
+        row = synth.to_bf16_bits(rng.normal(0, 1, size=128) * float(synth.bf16_bits_to_f32(
+            np.array([b]))[0]) / 8.0)
+        row[i % 128] = b | (0x8000 if i % 2 else 0)  # the group's amax, both signs
+        rows.append(row)
+    x = np.stack(rows).astype(np.uint16)
+    q, _ = _gq(x)
+    for i in range(len(picks)):
+        assert q[i, i % 128] == (0xFE if i % 2 else 0x7E)
+    _assert_quant_equal(x)
+
+
 def test_group_quant_zero_rows_is_a_noop():
     x = torch.zeros((0, 256), dtype=torch.bfloat16, device=DEV)
     q, s = fq.fp8_group_quant(x)
