@@ -6,15 +6,17 @@
 // decode_w8a8_selected (n % 128, k % 128, ldc >= n), DECODE_W8A8_ROWS (<= 16 rows).
 //
 // At <= 16 rows the op is a stream over the N*K weight bytes (2*16 flop per byte against
-// a machine balance in the hundreds), so the kernel is built to keep HBM busy:
+// a machine balance in the hundreds), so the kernels are built to keep HBM busy:
 //   - one gfx950 MFMA v_mfma_f32_16x16x128_f8f6f4 covers exactly one 128-wide K-group of
 //     a 16(rows) x 16(columns) tile, so the block scales apply per instruction: the
 //     partial of group g is scaled by a_scale[r,g] * w_scale[c/128,g] and added in FP32;
-//   - a workgroup owns 16 output columns; its waves split K and each streams its slice
-//     of the 16 weight rows with 16-byte loads, a chunk of groups in flight at a time;
-//   - the activation (<= 16 x K bytes, L2-resident) is read per wave; its scales are
-//     staged once per workgroup in LDS, transposed to [group][row];
+//   - the work unit is a strip of 16 output columns; the waves of a workgroup split K and
+//     each streams its slice of the strip's 16 weight rows with 16-byte loads;
 //   - the K-split partials are summed in LDS and written once as bf16 (RNE).
+// Two forms: the persistent kernel below (k <= 8192; one workgroup per CU walks strips,
+// each wave keeping its activation slice in registers), and w8a8_gemm_kernel for longer k
+// (one workgroup per strip; the activation, <= 16 x K bytes and L2-resident, is read per
+// wave and its scales are staged in LDS, transposed to [group][row]).
 // Rows >= m are fed zeros and never stored, so only (m-1)*ldc + n elements are written.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -129,12 +131,13 @@ __global__ __launch_bounds__(64 * kWaves) void w8a8_gemm_kernel(
 // ---------------------------------------------------------------------------------
 // Persistent form: one 8-wave workgroup per CU walks output strips of 16 columns.
 // Wave w owns a fixed slice of K-groups: its activation fragments and scales for that
-// slice are loaded once and stay in registers for the whole kernel, so the only global
-// traffic in the strip loop is the weight stream.  Each wave prefetches the next strip's
-// weight slice while it multiplies the current one; the 8 K-slice partials of a strip
-// meet in LDS (double-buffered, one barrier per strip) and one pass writes bf16.
-// Several projections that read the same activation can share one launch: strips are
-// numbered across them.
+// slice are loaded once (the tiles through LDS, see ActTile) and stay in registers for the
+// whole kernel, so the only global traffic in the strip loop is the weight stream.  Each
+// wave prefetches the next strip's weight slice while it multiplies the current one; the
+// 8 K-slice partials of a strip meet in LDS (double-buffered, one barrier per round of
+// strips, below) and one pass writes bf16.  Several projections that read the same
+// activation can share one launch: strips are numbered across them, and each block walks
+// them from first_strip (adjacent strips on one XCD).
 // Weight loads go through a buffer descriptor per strip (make_strip_rsrc); the cache
 // policy bits of those loads:
 #ifndef FP8Q_GEMM_AUX
