@@ -488,9 +488,12 @@ extern "C" int fp8_quant_w8a8_gemm_grouped(const uint16_t* a, uint8_t* a_q, floa
                                            const fp8q_gemm_proj* projs, int32_t count,
                                            int32_t m, int32_t k, hipStream_t stream) {
   if (count < 1 || count > kMaxProj) return FP8Q_EINVAL;
-  if (m < 1 || m > 16 || k <= 0 || k % 128 != 0 || k > kPersistentMaxK) return FP8Q_EINVAL;
+  if (m < 1 || m > 16 || k <= 0 || k % 128 != 0 || k > kMaxGemmK) return FP8Q_EINVAL;
   if (!a || !projs) return FP8Q_ENULL;
   if ((a_q == nullptr) != (a_scale == nullptr)) return FP8Q_ENULL;
+  // beyond the persistent kernel's K the quantizer and the GEMM run as two launches, through
+  // the caller's code/scale buffers
+  if (k > kPersistentMaxK && a_q == nullptr) return FP8Q_ENULL;
   if (!aligned(a, 16) || (a_q && (!aligned(a_q, 16) || !aligned(a_scale, 4))))
     return FP8Q_EALIGN;
   ProjSet ps = {};
@@ -508,6 +511,11 @@ extern "C" int fp8_quant_w8a8_gemm_grouped(const uint16_t* a, uint8_t* a_q, floa
     ps.strip_end[p] = int(end);
   }
   ps.count = count;
+  if (k > kPersistentMaxK) {
+    int rc = fp8_group_quant(a, a_q, a_scale, m, k, stream);
+    if (rc == FP8Q_OK) rc = w8a8_block_gemm_grouped(a_q, a_scale, projs, count, m, k, stream);
+    return rc;
+  }
   const ActSrc act = {nullptr, nullptr, a, a_q, a_scale};
   return run_persistent<true>(act, ps, m, k, stream);
 }

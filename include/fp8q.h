@@ -162,8 +162,10 @@ int w8a8_block_gemm_grouped(const uint8_t* a_q, const float* a_scale,
  * would from those codes (same bits).
  *   a        device, bf16 [m, k] row-major, 16-byte aligned
  *   a_q, a_scale  optional outputs (both NULL or both set): the codes [m, k] and scales
- *            [m, k/128] as fp8_group_quant writes them (16- / 4-byte aligned)
- *   projs, count  as w8a8_block_gemm_grouped;  1 <= m <= 16;  k % 128 == 0, k <= 8192
+ *            [m, k/128] as fp8_group_quant writes them (16- / 4-byte aligned); required
+ *            when k > 8192, where the quantizer and the GEMM run as two launches through
+ *            them (FP8Q_ENULL if missing)
+ *   projs, count  as w8a8_block_gemm_grouped;  1 <= m <= 16;  k % 128 == 0, k <= 131072
  * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EALIGN, FP8Q_ELAUNCH. */
 int fp8_quant_w8a8_gemm_grouped(const uint16_t* a, uint8_t* a_q, float* a_scale,
                                 const fp8q_gemm_proj* projs, int32_t count, int32_t m,

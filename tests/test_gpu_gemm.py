@@ -273,6 +273,29 @@ def test_fused_quant_gemm_matches_separate_calls(m):
         assert np.array_equal(host(o), host(r))
 
 
+@pytest.mark.parametrize("k", [8320, 16384])
+def test_fused_quant_gemm_long_k_runs_through_the_code_buffers(k):
+    """Beyond the persistent kernel's K the fused call quantizes into the caller's buffers
+    and runs the grouped GEMM on them: same codes, scales and outputs as the two calls;
+    without the buffers it is refused before anything runs."""
+    m = 11
+    a = synth.decode_activation(m, k=k, seed=k + 1)
+    a_d = bf16_dev(a)
+    q, s = fq.fp8_group_quant(a_d)
+    projs = [(u8_dev(wq), f32_dev(ws)) for wq, ws in (_weights(384, k, 7), _weights(128, k, 8))]
+    ref = fq.w8a8_block_gemm_grouped(q, s, [(w, ws, None) for w, ws in projs])
+    q2 = torch.full_like(q, 0x5A)
+    s2 = torch.full_like(s, -1.0)
+    outs = fq.fp8_quant_w8a8_gemm_grouped(a_d, [(w, ws, None) for w, ws in projs], q=q2,
+                                          scales=s2)
+    assert np.array_equal(host(q2), host(q))
+    assert np.array_equal(host(s2).view(np.uint32), host(s).view(np.uint32))
+    for o, r in zip(outs, ref):
+        assert np.array_equal(host(o), host(r))
+    with pytest.raises(fq.Fp8qError):
+        fq.fp8_quant_w8a8_gemm_grouped(a_d, [(w, ws, None) for w, ws in projs])
+
+
 def test_fused_quant_gemm_edge_activation_values():
     """All-zero and negative-zero groups, a subnormal and huge values through the fused path."""
     rng = np.random.default_rng(12)
