@@ -137,6 +137,10 @@ class Timer:
         """launches: callables each enqueueing one library kernel, cycled over; returns
         (mean_us, median_us) of the kernels' own durations."""
         assert iters <= len(self.pool) // 2
+        # untimed warm-up: every buffer set at least once and ~20 launches in all, so that
+        # first-touch effects and an idle GPU's clock ramp stay out of the timed launches
+        for i in range(max(len(launches), 20)):
+            launches[i % len(launches)]()
         self.torch.cuda.synchronize()
         for i in range(iters):
             a, b = self.pool[2 * i], self.pool[2 * i + 1]
