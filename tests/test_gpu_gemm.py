@@ -296,6 +296,31 @@ def test_fused_quant_gemm_long_k_runs_through_the_code_buffers(k):
         fq.fp8_quant_w8a8_gemm_grouped(a_d, [(w, ws, None) for w, ws in projs])
 
 
+def test_every_row_count_fused_and_grouped_agree_and_rows_do_not_depend_on_m():
+    """m = 1..16 through the fused and the grouped launch: identical outputs and codes, and
+    a row's bits do not depend on how many rows the call has."""
+    k = 1024
+    a16 = synth.decode_activation(16, k=k, seed=77)
+    projs = [(u8_dev(wq), f32_dev(ws)) for wq, ws in (_weights(512, k, 21), _weights(256, k, 22))]
+    full = None
+    for m in range(16, 0, -1):
+        a_d = bf16_dev(np.ascontiguousarray(a16[:m]))
+        q, s = fq.fp8_group_quant(a_d)
+        ref = [host(o) for o in fq.w8a8_block_gemm_grouped(q, s, [(w, ws, None) for w, ws in projs])]
+        q2 = torch.empty_like(q)
+        s2 = torch.empty_like(s)
+        outs = fq.fp8_quant_w8a8_gemm_grouped(a_d, [(w, ws, None) for w, ws in projs], q=q2,
+                                              scales=s2)
+        assert np.array_equal(host(q2), host(q))
+        assert np.array_equal(host(s2).view(np.uint32), host(s).view(np.uint32))
+        for o, r in zip(outs, ref):
+            assert np.array_equal(host(o), r)
+        if full is None:
+            full = ref
+        for r, f in zip(ref, full):
+            assert np.array_equal(r, f[:m])
+
+
 def test_fused_quant_gemm_edge_activation_values():
     """All-zero and negative-zero groups, a subnormal and huge values through the fused path."""
     rng = np.random.default_rng(12)
