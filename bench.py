@@ -15,7 +15,8 @@ events around every launch while the stream is held busy so no host latency leak
 an interval -- the group quantizer on the 4593-token prefill (K = 5120 and 16384), the
 GEMM at each N, the quant+GEMM pair at M = 5, 8, 12, 16 (N = 16384; as two launches and as
 one fused launch), and the KV write and
-absmax over a full 2048-block pool.  The roofline object covers the step's dominant
+absmax over a full 2048-block pool, and the per-batch latency of the decode-time write
+(absmax fused in) for 1, 4, 16 and 64 tokens.  The roofline object covers the step's dominant
 kernel (the fused quant + four-projection GEMM); cpu_baseline times the CPU oracle on one
 full step.
 
@@ -480,6 +481,19 @@ def main():
                 gbs=round(b / (mean_us * 1e-6) / 1e9, 1),
                 frac_hbm=round(b / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), bytes=b)
             log(f"{name}: {mean_us:.2f} us {kernels[f'{name}_t{t}']['gbs']} GB/s")
+        # per-batch latency of a decode-time write (absmax fused in) for 1..64 tokens: the
+        # first T rows of each buffer set onto their (distinct) slots
+        lat = {}
+        for tb in (1, 4, 16, 64):
+            bl = [(lambda b=b, tb=tb: fq.fp8_kv_write_amax(
+                b[0][:tb], b[1][:tb], b[3], b[4], b[2][:tb], KV_H, KV_D, KV_BS, ks_, vs_, b[5]))
+                for b in bufs]
+            mean_us, med_us = timer.kernel_us(bl, args.iters)
+            lat[str(tb)] = dict(us=round(mean_us, 3), us_median=round(med_us, 3),
+                                bytes=kv_write_bytes(tb))
+        kernels["kv_write_amax_batch_latency"] = lat
+        log("kv write+absmax batch latency: " + ", ".join(
+            f"{tb} tok {v['us']:.2f} us" for tb, v in lat.items()))
         del bufs
 
     # ---------------------------------------------------------- CPU baseline
@@ -588,9 +602,17 @@ def cpu_baseline(synth, log):
     dt = time.perf_counter() - t0
     gbs = step_bytes() / dt / 1e9
     log(f"cpu baseline: {dt:.2f} s per step, {gbs:.4f} GB/s")
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         model)
+    except OSError:
+        pass
     return dict(value=round(gbs, 5), unit="GB/s", cores=1, kind="oracle",
                 sample="one full decode step (same shapes as the GPU step), "
-                       f"{dt:.2f} s single-threaded C oracle, FP64 GEMM")
+                       f"{dt:.2f} s single-threaded C oracle, FP64 GEMM",
+                cpu_model=model, host_cpus=os.cpu_count())
 
 
 if __name__ == "__main__":
