@@ -7,16 +7,29 @@
 // (E4M3 activations with per-token 1x128 FP32 scales times E4M3 weights with 128x128 FP32
 // block scales, FP32 epilogue).
 //
-// Tiling for gfx950: a 256-thread workgroup owns a 128 x 128 output tile and walks K one
-// 128-wide group at a time, two workgroups per CU.  Each step holds the group's 128 x 128
-// activation and weight codes in LDS (double-buffered).  Wave (wm, wn) of the 2 x 2 grid
-// owns 64 x 64 of the tile: 4 x 4 tiles of v_mfma_f32_16x16x128_f8f6f4, one instruction per
-// tile per group, so every instruction's result is one group's partial and takes its scale
-// a_scale[row, g] * w_scale[col/128, g] in one FMA per element.  The epilogue stages the bf16
-// tile through LDS and writes it with 16-byte row-contiguous stores.  Workgroups are
-// ordered so that concurrently running ones share operand tiles: 8 consecutive row tiles
-// per column tile, and each XCD (workgroup ids are dealt to the 8 XCDs round-robin) takes a
-// contiguous stretch of that order for its own L2.
+// Both kernels walk K one 128-wide group at a time; one v_mfma_f32_16x16x128_f8f6f4 covers
+// one group of a 16 x 16 output tile, so every instruction's result is one group's partial
+// and takes its scale a_scale[row, g] * w_scale[col/128, g] in one FMA per element.  The
+// operand tiles of each group are copied global -> LDS by the buffer unit itself
+// (buffer_load ... lds: no staging registers, no LDS store instructions) into one of two
+// stages, the next group's copies landing while the current group multiplies.
+//
+// tile256 (the large shapes): one 512-thread workgroup per CU owns a 256 x 256 output tile,
+// wave (wm, wn) of the 4 x 2 grid 64 x 128 of it (4 x 8 MFMA tiles).  A 256 x 256 tile
+// copies half the operand bytes per flop of a 128 x 128 one, which the copy path (the
+// texture/address unit, about 70 % busy with 128 x 128 tiles) needs, and 64 x 128 per wave
+// reads 0.75 KB of LDS per MFMA.  The column loop is software-pipelined: column c + 1's
+// weight fragment is read and column c - 1's products are scaled while column c
+// multiplies, one group of four FMAs between MFMAs.  When the tile count leaves the last
+// round of workgroups at most half full, each of those last tiles is split into two
+// 256 x 128 halves (wave tiles 64 x 64): twice as many work items, each half as long.
+//
+// tile128 (fewer than half a round of 256 x 256 tiles, e.g. a 1024-column projection):
+// 256-thread workgroups, two per CU, each a 128 x 128 tile (2 x 2 waves of 64 x 64).
+//
+// Workgroups are ordered so that concurrently running ones share operand tiles:
+// consecutive row tiles per column tile, and each XCD (workgroup ids are dealt to the 8
+// XCDs round-robin) takes a contiguous stretch of that order for its own L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,19 +43,268 @@
 namespace fp8q {
 namespace {
 
+constexpr int kXcds = 8;
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// E4M3 x E4M3 -> FP32 over one 128-wide K-group of a 16 x 16 tile (no scaling).
+__device__ __forceinline__ v4f mfma_group(v8i a, v8i b) {
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// Buffer descriptor over rows [r0, rows) of a [rows, k] byte matrix: reads past the last
+// row return zeros without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int r0, int rows,
+                                                            int k) {
+  const int valid = rows - r0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base + int64_t(r0) * k), 0,
+                                           valid > 0 ? valid * k : 0, kBufferDword3);
+}
+
+namespace tile256 {
+
+constexpr int kBM = 256, kBN = 256, kThreads = 512;
+constexpr int kCPitch = kBN + 8;          // bf16 elements per staged output row
+constexpr int kSlab = 64 * kCPitch * 2;   // 64 staged output rows (bytes)
+static_assert(kSlab >= kBM * 128, "a stage array holds one operand tile of one group");
+constexpr int kGroupM = 4;                // row tiles per column tile in the walk order
+
+// Two LDS stages.  The operand arrays are padded to kSlab so that the four of them also
+// hold the four 64-row slabs of the staged bf16 output tile.  They are separate objects:
+// the compiler can then see that a stage's operand reads never alias the copies landing
+// in the other stage, and keeps those copies in flight.
+struct Stages {
+  uint8_t (&a0)[kSlab];
+  uint8_t (&a1)[kSlab];
+  uint8_t (&b0)[kSlab];
+  uint8_t (&b1)[kSlab];
+  float (&s0)[kBM + 32];
+  float (&s1)[kBM + 32];
+};
+
+// One output tile: rows [m0, m0 + 256) x columns [n0, n0 + 32 kCols), kCols = 8 (256
+// columns, wave tiles 64 x 128) or 4 (128 columns, wave tiles 64 x 64).
+template <int kCols>
+__device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
+                                             const float* __restrict__ a_scale,
+                                             const uint8_t* __restrict__ w_q,
+                                             const float* __restrict__ w_scale,
+                                             uint16_t* __restrict__ out, int m, int n, int k,
+                                             int ldc, int vec_out, int m0, int n0,
+                                             const Stages& st) {
+  constexpr int kWaveCols = 16 * kCols;   // columns per wave
+  constexpr int kTileCols = 2 * kWaveCols;
+  constexpr int kBBlocks = kTileCols / 8 / 8;  // 1 KB weight copy blocks per wave per group
+  const int t = int(threadIdx.x), lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1;  // rows 64 wm .., columns kWaveCols * wn ..
+  const int groups = k >> 7;
+
+  const __amdgpu_buffer_rsrc_t ra_rsrc = tile_rsrc(a_q, m0, m, k);
+  const __amdgpu_buffer_rsrc_t rb_rsrc = tile_rsrc(w_q, n0, n, k);
+  const __amdgpu_buffer_rsrc_t none_rsrc = tile_rsrc(a_q, 0, 0, k);
+  // 1 KB copy blocks (8 rows each): wave w fills blocks w + 8q of each operand; lane L of
+  // block b loads row 8b + L/8, chunk (L % 8) ^ (L / 8) ^ (b & 1), which the swizzle below
+  // places at byte b * 1024 + 16 L
+  int voff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int b = wave + 8 * q, r = 8 * b + (lane >> 3);
+    voff[q] = r * k + (((lane & 7) ^ (lane >> 3) ^ (b & 1)) << 4);
+  }
+  // activation scales: lane L of wave w copies row 32 w + L into slot 32 w + L (lanes
+  // 32..63 repeat what wave w + 1 copies: same values, same slots; no branch)
+  const float* gsp = a_scale + int64_t(min(m0 + 32 * wave + lane, m - 1)) * groups;
+  const int nb = min((n0 + kWaveCols * wn) >> 7, (n >> 7) - 1);
+  const_float* wsp = (const_float*)(w_scale + int64_t(nb) * groups);
+
+  // The copies of group g; outside [0, groups) they read a zero-size buffer (zeros written,
+  // no memory traffic) and repeat a valid scale.  Every copy is unconditional: a branch
+  // here would split the step and let the compiler sink its FMAs past the next barrier.
+  auto copy_group = [&](uint8_t* sa, uint8_t* sb, float* ss, int g) {
+    const bool live = g >= 0 && g < groups;
+    const __amdgpu_buffer_rsrc_t ra = live ? ra_rsrc : none_rsrc;
+    const __amdgpu_buffer_rsrc_t rb = live ? rb_rsrc : none_rsrc;
+    const int goff = live ? g * 128 : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + (wave + 8 * q) * 1024), 16,
+                                               voff[q], goff, 0, 0);
+#pragma unroll
+    for (int q = 0; q < kBBlocks; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sb + (wave + 8 * q) * 1024), 16,
+                                               voff[q], goff, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(gsp + min(max(g, 0), groups - 1)),
+        (lds_void*)(ss + 32 * wave), 4, 0, 0);
+  };
+
+  v4f acc[4][kCols];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) acc[i][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // Staged 128-byte row r keeps its 16-byte chunk c at slot c ^ (r & 7) ^ (bit 3 of r): an
+  // operand read takes one chunk from 16 consecutive rows per 16 lanes, which land on 16
+  // distinct bank groups.  Fragment row 64 wm + 16 i + orow (or kWaveCols wn + 16 c + orow)
+  // has the swizzle of row orow, so every read is one of four lane offsets plus a constant.
+  const int orow = lane & 15, oh = lane >> 4;
+  const int sw = (orow & 7) ^ ((orow >> 3) & 1);
+  const int a_lo = (wm * 64 + orow) * 128 + (((2 * oh) ^ sw) << 4);
+  const int a_hi = (wm * 64 + orow) * 128 + (((2 * oh + 1) ^ sw) << 4);
+  const int b_lo = (wn * kWaveCols + orow) * 128 + (((2 * oh) ^ sw) << 4);
+  const int b_hi = (wn * kWaveCols + orow) * 128 + (((2 * oh + 1) ^ sw) << 4);
+  const int s_off = (wm * 64 + oh * 4) * 4;
+  auto ld32 = [&](const uint8_t* p, int lo, int hi) {
+    const v4u x = *reinterpret_cast<const v4u*>(p + lo);
+    const v4u y = *reinterpret_cast<const v4u*>(p + hi);
+    v8i r;
+    r[0] = int(x[0]); r[1] = int(x[1]); r[2] = int(x[2]); r[3] = int(x[3]);
+    r[4] = int(y[0]); r[5] = int(y[1]); r[6] = int(y[2]); r[7] = int(y[3]);
+    return r;
+  };
+
+  // Group g from stage (sa, sb, ss); the copies of group g + 1 go to (na, nbs, ns), which
+  // held group g - 1 (read by everyone before the barrier).
+  auto step = [&](int g, const uint8_t* sa, const uint8_t* sb, const float* ss, uint8_t* na,
+                  uint8_t* nbs, float* ns) {
+    __syncthreads();  // everyone's copies of group g landed (the fence drains them)
+    copy_group(na, nbs, ns, g + 1);
+    const float ws = wsp[min(max(g, 0), groups - 1)];
+    v8i af[4];
+    float f[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      af[i] = ld32(sa + i * 2048, a_lo, a_hi);
+      const float4 as = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(ss) +
+                                                         s_off + i * 64);
+      f[i][0] = as.x * ws; f[i][1] = as.y * ws; f[i][2] = as.z * ws; f[i][3] = as.w * ws;
+    }
+    v8i bcur = ld32(sb, b_lo, b_hi);
+    v4f pprev[4];
+#pragma unroll
+    for (int c = 0; c <= kCols; ++c) {
+      v8i bnxt = bcur;
+      if (c + 1 < kCols) bnxt = ld32(sb + (c + 1) * 2048, b_lo, b_hi);
+      v4f pcur[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (c < kCols) pcur[i] = mfma_group(af[i], bcur);
+        if (c > 0) {
+          acc[i][c - 1][0] = __builtin_fmaf(pprev[i][0], f[i][0], acc[i][c - 1][0]);
+          acc[i][c - 1][1] = __builtin_fmaf(pprev[i][1], f[i][1], acc[i][c - 1][1]);
+          acc[i][c - 1][2] = __builtin_fmaf(pprev[i][2], f[i][2], acc[i][c - 1][2]);
+          acc[i][c - 1][3] = __builtin_fmaf(pprev[i][3], f[i][3], acc[i][c - 1][3]);
+        }
+      }
+      if (c > 0 && c < kCols) {  // MFMA, its neighbour's four FMAs, MFMA, ...
+        if (c + 1 < kCols) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pprev[i] = pcur[i];
+      bcur = bnxt;
+    }
+  };
+
+  // An odd group count starts with one step over a zero group, so that steps come in
+  // pairs and each step's stage is fixed at compile time.
+  const int odd = groups & 1;
+  copy_group(st.a0, st.b0, st.s0, -odd);
+  for (int g = -odd; g < groups; g += 2) {
+    step(g, st.a0, st.b0, st.s0, st.a1, st.b1, st.s1);
+    step(g + 1, st.a1, st.b1, st.s1, st.a0, st.b0, st.s0);
+  }
+  __syncthreads();  // every copy landed and every wave is done reading the stages
+
+  // output rows 64 s .. 64 s + 63 are staged in operand array s
+  auto slab = [&](int s) -> uint8_t* {
+    return s == 0 ? st.a0 : s == 1 ? st.a1 : s == 2 ? st.b0 : st.b1;
+  };
+  {
+    uint16_t* sc = reinterpret_cast<uint16_t*>(slab(wm));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < kCols; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = i * 16 + oh * 4 + j;
+          const int col = wn * kWaveCols + c * 16 + (lane & 15);
+          sc[r * kCPitch + col] = f32_to_bf16_rne(acc[i][c][j]);
+        }
+  }
+  __syncthreads();
+  constexpr int kRowChunks = kTileCols / 8;  // 16-byte chunks per output row
+#pragma unroll 4
+  for (int q = 0; q < kBM * kRowChunks / kThreads; ++q) {
+    const int ch = t + kThreads * q, r = ch / kRowChunks, cc = (ch % kRowChunks) * 8;
+    const int gm = m0 + r, gn = n0 + cc;
+    if (gm < m && gn < n) {
+      const uint16_t* src =
+          reinterpret_cast<const uint16_t*>(slab(r >> 6)) + (r & 63) * kCPitch + cc;
+      uint16_t* dst = out + int64_t(gm) * ldc + gn;
+      if (vec_out) {
+        *reinterpret_cast<v4u*>(dst) = *reinterpret_cast<const v4u*>(src);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[e] = src[e];
+      }
+    }
+  }
+}
+
+// Work item b: items [0, n_full) are whole tiles, the rest are the two halves of each of
+// the last tiles of the walk order.
+__global__ __launch_bounds__(kThreads, 1) void w8a8_prefill_kernel(
+    const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale,
+    const uint8_t* __restrict__ w_q, const float* __restrict__ w_scale,
+    uint16_t* __restrict__ out, int m, int n, int k, int ldc, int tiles_m, int tiles_n,
+    int n_full, int vec_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t a0[kSlab], a1[kSlab], b0[kSlab], b1[kSlab];
+  __shared__ __attribute__((aligned(16))) float s0[kBM + 32], s1[kBM + 32];
+  const Stages st{a0, a1, b0, b1, s0, s1};
+
+  int item = int(blockIdx.x), tile = item, half = -1;
+  if (item < n_full) {
+    const int even = n_full - n_full % kXcds;
+    if (item < even) tile = (item % kXcds) * (even / kXcds) + item / kXcds;
+  } else {
+    tile = n_full + (item - n_full) / 2;
+    half = (item - n_full) & 1;
+  }
+  const int band = kGroupM * tiles_n;
+  const int first_m = (tile / band) * kGroupM;
+  const int band_m = min(kGroupM, tiles_m - first_m);
+  const int tm = first_m + (tile % band) % band_m;
+  const int tn = (tile % band) / band_m;
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  if (half < 0)
+    prefill_tile<8>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, m0, n0, st);
+  else
+    prefill_tile<4>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, m0, n0 + 128 * half,
+                    st);
+}
+
+}  // namespace tile256
+
+namespace tile128 {
+
 constexpr int kBM = 128, kBN = 128, kThreads = 256;
 constexpr int kAStage = kBM * 128;        // one group of the activation tile (bytes)
 constexpr int kBStage = kBN * 128;        // one group of the weight tile
 constexpr int kStage = kAStage + kBStage;
 constexpr int kCPitch = kBN + 8;          // bf16 elements per staged output row
-#ifndef FP8Q_PREFILL_GROUPM
-#define FP8Q_PREFILL_GROUPM 8
-#endif
-constexpr int kGroupM = FP8Q_PREFILL_GROUPM;  // row tiles per column tile in the walk order
-constexpr int kXcds = 8;
+constexpr int kGroupM = 8;                // row tiles per column tile in the walk order
 static_assert(kBM * kCPitch * 2 <= 2 * kStage, "output staging reuses the operand stages");
-
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 // LDS byte offset of 16-byte chunk c (0..7) of staged 128-byte row r: the chunk sits at
 // slot c ^ (r & 7) ^ (bit 3 of r).  An MFMA operand read takes one chunk index from 16
@@ -62,21 +324,6 @@ __device__ __forceinline__ v8i lds_load32(const uint8_t* base, int row, int h) {
   return r;
 }
 
-// E4M3 x E4M3 -> FP32 over one 128-wide K-group of a 16 x 16 tile (no scaling).
-__device__ __forceinline__ v4f mfma_group(v8i a, v8i b) {
-  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
-}
-
-// Buffer descriptor over rows [r0, rows) of a [rows, k] byte matrix: reads past the last
-// row return zeros without touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int r0, int rows,
-                                                            int k) {
-  const int valid = rows - r0;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base + int64_t(r0) * k), 0,
-                                           valid > 0 ? valid * k : 0, kBufferDword3);
-}
-
 // Operand tiles are copied global -> LDS by the buffer unit itself (buffer_load ... lds):
 // no staging registers and no LDS store instructions.  A wave's copy instruction fills one
 // contiguous 1 KB block of LDS, lane L writing bytes [16L, 16L + 16); so lane L of block b
@@ -85,7 +332,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base,
 // copies of the next group into the other buffer, then multiply -- the copies run under
 // the MFMAs.  (The copies are issued only after the group's LDS reads: the compiler orders
 // every LDS read after all outstanding copies, so a copy issued earlier would stall them.)
-__global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_kernel(
+__global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_small_kernel(
     const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale,
     const uint8_t* __restrict__ w_q, const float* __restrict__ w_scale,
     uint16_t* __restrict__ out, int m, int n, int k, int ldc, int tiles_m, int tiles_n,
@@ -123,7 +370,6 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_kernel(
   const float* gsp = a_scale + int64_t(min(m0 + 32 * wave + (lane & 31), m - 1)) * groups;
   const_float* wsp = (const_float*)(w_scale + int64_t(n0 >> 7) * groups);
 
-  typedef __attribute__((address_space(3))) void lds_void;
   auto copy_group = [&](int buf, int g) {
     uint8_t* base = lds + buf * kStage;
 #pragma unroll
@@ -209,6 +455,8 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_kernel(
   }
 }
 
+}  // namespace tile128
+
 }  // namespace
 }  // namespace fp8q
 
@@ -223,13 +471,27 @@ extern "C" int w8a8_block_gemm_prefill(const uint8_t* a_q, const float* a_scale,
   if (!aligned(a_q, 16) || !aligned(w_q, 16) || !aligned(a_scale, 4) || !aligned(w_scale, 4) ||
       !aligned(out, 2))
     return FP8Q_EALIGN;
-  const int64_t tiles_m = (int64_t(m) + kBM - 1) / kBM;
-  const int64_t tiles_n = (int64_t(n) + kBN - 1) / kBN;
-  if (tiles_m * tiles_n > 0x7FFFFFFF) return FP8Q_EINVAL;
   // buffer offsets within one 128-row tile are 32-bit
-  if (int64_t(kBM) * k > 0x7FFFFFFF) return FP8Q_EINVAL;
+  if (int64_t(128) * k > 0x7FFFFFFF) return FP8Q_EINVAL;
   const int vec_out = (ldc % 8 == 0 && aligned(out, 16)) ? 1 : 0;
-  launch(w8a8_prefill_kernel, dim3(unsigned(tiles_m * tiles_n)), dim3(kThreads), 0, stream,
-         a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, int(tiles_m), int(tiles_n), vec_out);
+  const int64_t cus = num_cus();
+  const int64_t big_m = (int64_t(m) + 255) / 256, big_n = (int64_t(n) + 255) / 256;
+  const int64_t big = big_m * big_n;
+  if (2 * big >= cus && int64_t(256) * k <= 0x7FFFFFFF && big <= 0x3FFFFFFF) {
+    // one workgroup per CU: split the tiles of a last round that would leave half the CUs
+    // idle
+    const int64_t tail = big % cus;
+    const int64_t split = (tail != 0 && 2 * tail <= cus) ? tail : 0;
+    const int64_t n_full = big - split;
+    launch(tile256::w8a8_prefill_kernel, dim3(unsigned(n_full + 2 * split)),
+           dim3(tile256::kThreads), 0, stream, a_q, a_scale, w_q, w_scale, out, m, n, k, ldc,
+           int(big_m), int(big_n), int(n_full), vec_out);
+    return launch_status();
+  }
+  const int64_t tiles_m = (int64_t(m) + 127) / 128, tiles_n = (int64_t(n) + 127) / 128;
+  if (tiles_m * tiles_n > 0x7FFFFFFF) return FP8Q_EINVAL;
+  launch(tile128::w8a8_prefill_small_kernel, dim3(unsigned(tiles_m * tiles_n)),
+         dim3(tile128::kThreads), 0, stream, a_q, a_scale, w_q, w_scale, out, m, n, k, ldc,
+         int(tiles_m), int(tiles_n), vec_out);
   return launch_status();
 }

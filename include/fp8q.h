@@ -120,8 +120,9 @@ int w8a8_block_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q
 /* ------------------------------------------------ W8A8 GEMM at prefill widths
  * [resid] DenseFp8Inputs::w8a8_kernels (the W8A8 prefill arm: per-token group quant, then
  * a block-scaled FP8 GEMM); [actq] module doc (a 4593-token prefill).  The arithmetic and
- * operand layouts are w8a8_block_gemm's; only the row range differs: any m >= 1 (the
- * kernel is tiled 128 x 128 and fills the chip from a few hundred rows up).
+ * operand layouts are w8a8_block_gemm's; only the row range differs: any m >= 1.  Tiled
+ * 256 x 256 (one workgroup per CU) once there are at least half as many such tiles as CUs,
+ * else 128 x 128 (two per CU); both tilings give bit-identical results.
  *   out[r, c] = bf16_rne( sum_g a_scale[r, g] * w_scale[c/128, g]
  *                                * sum_{j<128} dec(a_q[r, 128g+j]) * dec(w_q[c, 128g+j]) )
  * FP32 products and accumulation, one scaled FMA per group.  Only rows 0..m-1 are written

@@ -4,7 +4,12 @@ Bar as for the decode GEMM: |gpu - ref| <= 1e-2 |ref| + 1e-3 rms(ref) per bf16 o
 over the outputs compared); bit-exact where the sums are exact.  Small and ragged shapes
 are compared in full; the 4593-token prefill shape on sampled rows (first, middle, last
 row tiles, the ragged tail) and sampled 128-column blocks, which the oracle computes from
-the same codes and scales."""
+the same codes and scales.
+
+The library picks the 256 x 256 tiling once a problem has at least half a round of such
+tiles (128 on the 256-CU MI355X) and splits the tiles of a last round that is at most half
+full into 256 x 128 halves; the large-tile cases below are sized to take each of those
+paths, the smaller ones the 128 x 128 tiling."""
 import numpy as np
 import pytest
 import torch
@@ -37,6 +42,35 @@ def test_ragged_shapes_in_full(m, n, k):
     ref = oracle.gemm(host(q), host(s), wq, ws)
     ok, worst = gemm_tolerance_ok(out, ref)
     assert ok, f"worst error / bound = {worst:.3f}"
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (4096, 2048, 256),   # 128 tiles of 256 x 256: one half round, every tile split in halves
+    (4096, 2560, 384),   # 160 tiles: whole tiles only; three K-groups (odd: a zero step first)
+    (4096, 1920, 256),   # 128 tiles, split; the last column tile's second half is empty
+    (4000, 2304, 384),   # 144 tiles, whole; ragged last row tile, half-empty last column tile
+])
+def test_large_tile_shapes_in_full(m, n, k):
+    a = synth.prefill_activation(k, m=m, seed=m + 3 * n + k)
+    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=n + 7 * k))
+    q, s = _quant(a)
+    out = host(fq.w8a8_block_gemm_prefill(q, s, u8_dev(wq), f32_dev(ws)))
+    ref = oracle.gemm(host(q), host(s), wq, ws)
+    ok, worst = gemm_tolerance_ok(out, ref)
+    assert ok, f"worst error / bound = {worst:.3f}"
+
+
+def test_split_halves_match_whole_tiles_bit_for_bit():
+    # 4096 x 2048 runs as 256 x 128 halves, 4096 x 2560 as whole 256 x 256 tiles; both sum
+    # the same scaled group partials in the same order, so the shared columns agree exactly
+    m, k = 4096, 256
+    a = synth.prefill_activation(k, m=m, seed=515)
+    wq, ws = oracle.block_quant(synth.decode_weight(2560, k, seed=516))
+    q, s = _quant(a)
+    halves = host(fq.w8a8_block_gemm_prefill(q, s, u8_dev(wq[:2048].copy()),
+                                             f32_dev(ws[:16].copy())))
+    whole = host(fq.w8a8_block_gemm_prefill(q, s, u8_dev(wq), f32_dev(ws)))
+    assert np.array_equal(halves, whole[:, :2048])
 
 
 def test_small_integer_sums_are_exact():
@@ -88,9 +122,11 @@ def test_agrees_with_the_decode_kernel_on_sixteen_rows():
         2.0 ** -7 * np.max(np.abs(ref))
 
 
-@pytest.mark.parametrize("ldc,offset", [(640, 0), (517, 0), (640, 1)])
-def test_strided_and_unaligned_output_writes_exactly_its_extent(ldc, offset):
-    m, n, k = 140, 512, 256
+@pytest.mark.parametrize("m,n,k,ldc,offset", [
+    (140, 512, 256, 640, 0), (140, 512, 256, 517, 0), (140, 512, 256, 640, 1),
+    (4096, 2048, 128, 2056, 0),    # 256 x 128 halves, 16-byte row stores
+    (4096, 2560, 128, 2567, 1)])   # whole 256 x 256 tiles, element stores
+def test_strided_and_unaligned_output_writes_exactly_its_extent(m, n, k, ldc, offset):
     a = synth.prefill_activation(k, m=m, seed=9)
     wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=10))
     q, s = _quant(a)
