@@ -14,9 +14,10 @@ Also measured (same process, same rotation rule): each kernel on its own, timed 
 events around every launch while the stream is held busy so no host latency leaks into
 an interval -- the group quantizer on the 4593-token prefill (K = 5120 and 16384), the
 GEMM at each N, the quant+GEMM pair at M = 5, 8, 12, 16 (N = 16384; as two launches and as
-one fused launch), and the KV write and
-absmax over a full 2048-block pool, and the per-batch latency of the decode-time write
-(absmax fused in) for 1, 4, 16 and 64 tokens.  The roofline object covers the step's dominant
+one fused launch), the KV write, absmax and dequantizing read over a full 2048-block pool
+(slots a random permutation of all 32768; the write and read again with the slots of a
+paged prefill, blocks in random order and 16 consecutive tokens per block), and the
+per-batch latency of the decode-time write (absmax fused in) for 1, 4, 16 and 64 tokens.  The roofline object covers the step's dominant
 kernel (the fused quant + four-projection GEMM); cpu_baseline times the CPU oracle on one
 full step.
 
@@ -494,7 +495,24 @@ def main():
         kernels["kv_write_amax_batch_latency"] = lat
         log("kv write+absmax batch latency: " + ", ".join(
             f"{tb} tok {v['us']:.2f} us" for tb, v in lat.items()))
-        del bufs
+        # the same write and read with the slots of a paged prefill: blocks in random order,
+        # 16 consecutive tokens per block (8 KB contiguous per block and pool)
+        runs = torch.from_numpy(synth.kv_block_runs()).cuda()
+        run_slots = [runs.clone() for _ in bufs]
+        wl = [(lambda b=b, r=r: fq.fp8_kv_write(b[0], b[1], b[3], b[4], r, KV_H, KV_D, KV_BS,
+                                                ks_, vs_)) for b, r in zip(bufs, run_slots)]
+        rl = [(lambda b=b, r=r: fq.fp8_kv_read(b[3], b[4], r, KV_H, KV_D, KV_BS, ks_, vs_,
+                                               k_out=b[6], v_out=b[7]))
+              for b, r in zip(bufs, run_slots)]
+        for name, launches, b in (("kv_write_block_runs", wl, kv_write_bytes(t)),
+                                  ("kv_read_block_runs", rl, kv_read_bytes(t))):
+            mean_us, med_us = timer.kernel_us(launches, args.iters)
+            kernels[f"{name}_t{t}"] = dict(
+                us=round(mean_us, 3), us_median=round(med_us, 3),
+                gbs=round(b / (mean_us * 1e-6) / 1e9, 1),
+                frac_hbm=round(b / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), bytes=b)
+            log(f"{name}: {mean_us:.2f} us {kernels[f'{name}_t{t}']['gbs']} GB/s")
+        del bufs, run_slots
 
     # ---------------------------------------------------------- CPU baseline
     cpu = None

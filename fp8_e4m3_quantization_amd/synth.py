@@ -192,3 +192,14 @@ def kv_full_pool(seed: int = 5100, heads: int = KV_HEADS, head_dim: int = KV_HEA
     k = to_bf16_bits(normal_with_outliers(rng, (t, e), 3.0, 0.002, 40.0))
     v = to_bf16_bits(normal_with_outliers(rng, (t, e), 3.0, 0.002, 40.0))
     return KvBatch(k=k, v=v, slots=slots)
+
+
+def kv_block_runs(num_blocks: int = KV_NUM_BLOCKS, block_size: int = KV_BLOCK_SIZE,
+                  seed: int = 5101) -> np.ndarray:
+    """Slots of a prefill that fills every block of the pool: blocks handed out in random
+    order, each taking block_size consecutive tokens (offsets 0..block_size-1)."""
+    rng = np.random.default_rng(seed)
+    blocks = rng.permutation(num_blocks).astype(np.int64)
+    return (blocks[:, None] * block_size + np.arange(block_size, dtype=np.int64)).ravel()
+
+

@@ -26,12 +26,14 @@ def _pools(fill_k=0xAA, fill_v=0x55, nblk=NB, cs=CS):
     return kc, vc, torch.from_numpy(kc.copy()).to(DEV), torch.from_numpy(vc.copy()).to(DEV)
 
 
-def test_full_pool_write_matches_oracle():
+@pytest.mark.parametrize("pattern", ["permutation", "block_runs"])
+def test_full_pool_write_matches_oracle(pattern):
     b = synth.kv_full_pool()
+    slots = b.slots if pattern == "permutation" else synth.kv_block_runs()
     kc, vc, kcd, vcd = _pools()
     ks, vs = 3.0 * 17.0 / 448.0, 0.0625
-    fq.fp8_kv_write(bf16_dev(b.k), bf16_dev(b.v), kcd, vcd, i64_dev(b.slots), H, D, BS, ks, vs)
-    oracle.kv_write(b.k, b.v, kc, vc, b.slots, len(b.slots), H, D, BS, ks, vs, E, E, CS)
+    fq.fp8_kv_write(bf16_dev(b.k), bf16_dev(b.v), kcd, vcd, i64_dev(slots), H, D, BS, ks, vs)
+    oracle.kv_write(b.k, b.v, kc, vc, slots, len(slots), H, D, BS, ks, vs, E, E, CS)
     assert np.array_equal(host(kcd), kc) and np.array_equal(host(vcd), vc)
 
 
@@ -231,6 +233,18 @@ def test_read_full_pool_every_code_matches_oracle():
     kg, vg, ko, vo = _read_both(kc, vc, slots, H, D, BS, NB, 0.0234375, 3.0e-3, E, E, CS, t)
     assert np.array_equal(kg, ko) and np.array_equal(vg, vo)
     assert np.all(kg[5 * E:6 * E] == 0x1234) and np.all(vg[(t - 3) * E:(t - 2) * E] == 0x1234)
+
+
+def test_read_full_pool_block_runs_matches_oracle():
+    """The pool read back through the slots of a paged prefill (blocks in random order, 16
+    consecutive tokens each)."""
+    rng = np.random.default_rng(78)
+    kc = rng.integers(0, 256, size=NB * CS, dtype=np.uint8)
+    vc = rng.integers(0, 256, size=NB * CS, dtype=np.uint8)
+    slots = synth.kv_block_runs(NB, BS)
+    t = len(slots)
+    kg, vg, ko, vo = _read_both(kc, vc, slots, H, D, BS, NB, 0.0234375, 3.0e-3, E, E, CS, t)
+    assert np.array_equal(kg, ko) and np.array_equal(vg, vo)
 
 
 @pytest.mark.parametrize("t", [1, 2, 37, 129])
