@@ -60,6 +60,20 @@ def test_large_tile_shapes_in_full(m, n, k):
     assert ok, f"worst error / bound = {worst:.3f}"
 
 
+def test_large_tiles_long_k_on_sampled_rows():
+    # 128 tiles of 256 x 256 (split into halves) with K = 16384: 128 groups per tile
+    m, n, k = 4096, 2048, 16384
+    a = synth.prefill_activation(k, m=m, seed=717)
+    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=718))
+    q, s = _quant(a)
+    got = host(fq.w8a8_block_gemm_prefill(q, s, u8_dev(wq), f32_dev(ws)))
+    rows = np.r_[0:4, 254:258, 2047:2051, m - 4:m]
+    ref = oracle.gemm(np.ascontiguousarray(host(q)[rows]), np.ascontiguousarray(host(s)[rows]),
+                      wq, ws)
+    ok, worst = gemm_tolerance_ok(got[rows], ref)
+    assert ok, f"worst error / bound = {worst:.3f}"
+
+
 def test_split_halves_match_whole_tiles_bit_for_bit():
     # 4096 x 2048 runs as 256 x 128 halves, 4096 x 2560 as whole 256 x 256 tiles; both sum
     # the same scaled group partials in the same order, so the shared columns agree exactly
