@@ -54,11 +54,12 @@ __device__ __forceinline__ v4f mfma_group(v8i a, v8i b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
-// Buffer descriptor over rows [r0, rows) of a [rows, k] byte matrix: reads past the last
-// row return zeros without touching memory.
+// Buffer descriptor over the rows [r0, min(rows, r0 + tile_rows)) of a [rows, k] byte
+// matrix: reads past them return zeros without touching memory.  Its size is at most
+// tile_rows * k bytes, which the host keeps below 2^31.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int r0, int rows,
-                                                            int k) {
-  const int valid = rows - r0;
+                                                            int k, int tile_rows) {
+  const int valid = min(rows - r0, tile_rows);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base + int64_t(r0) * k), 0,
                                            valid > 0 ? valid * k : 0, kBufferDword3);
 }
@@ -102,9 +103,9 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
   const int wm = wave >> 1, wn = wave & 1;  // rows 64 wm .., columns kWaveCols * wn ..
   const int groups = k >> 7;
 
-  const __amdgpu_buffer_rsrc_t ra_rsrc = tile_rsrc(a_q, m0, m, k);
-  const __amdgpu_buffer_rsrc_t rb_rsrc = tile_rsrc(w_q, n0, n, k);
-  const __amdgpu_buffer_rsrc_t none_rsrc = tile_rsrc(a_q, 0, 0, k);
+  const __amdgpu_buffer_rsrc_t ra_rsrc = tile_rsrc(a_q, m0, m, k, kBM);
+  const __amdgpu_buffer_rsrc_t rb_rsrc = tile_rsrc(w_q, n0, n, k, kTileCols);
+  const __amdgpu_buffer_rsrc_t none_rsrc = tile_rsrc(a_q, 0, 0, k, 0);
   // 1 KB copy blocks (8 rows each): wave w fills blocks w + 8q of each operand; lane L of
   // block b loads row 8b + L/8, chunk (L % 8) ^ (L / 8) ^ (b & 1), which the swizzle below
   // places at byte b * 1024 + 16 L
@@ -356,8 +357,8 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_small_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int groups = k >> 7;
 
-  const __amdgpu_buffer_rsrc_t ra_rsrc = tile_rsrc(a_q, m0, m, k);
-  const __amdgpu_buffer_rsrc_t rb_rsrc = tile_rsrc(w_q, n0, n, k);
+  const __amdgpu_buffer_rsrc_t ra_rsrc = tile_rsrc(a_q, m0, m, k, kBM);
+  const __amdgpu_buffer_rsrc_t rb_rsrc = tile_rsrc(w_q, n0, n, k, kBN);
   // wave w fills blocks b = w + 4q (q < 4) of each operand stage: rows 8b .. 8b + 7
   int voff[4];
 #pragma unroll

@@ -74,6 +74,27 @@ def test_large_tiles_long_k_on_sampled_rows():
     assert ok, f"worst error / bound = {worst:.3f}"
 
 
+def test_rows_past_two_to_the_32_bytes_of_codes():
+    # 2^25 + 100 rows of k = 128: the codes hold more than 2^32 bytes, so a tile's buffer
+    # descriptor sized from all the rows left below it (rather than from the tile's own
+    # 256 rows) would wrap around to 12800 bytes and read the first tile's rows 100.. as 0
+    m, n, k = (1 << 25) + 100, 128, 128
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(4242)
+    aq = torch.randint(0, 0x78, (m, k), dtype=torch.uint8, device=DEV, generator=gen)
+    aq |= torch.randint(0, 2, (m, k), dtype=torch.uint8, device=DEV, generator=gen) << 7
+    as_ = torch.full((m, 1), 0.5, dtype=torch.float32, device=DEV)
+    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=4243))
+    out = fq.w8a8_block_gemm_prefill(aq, as_, u8_dev(wq), f32_dev(ws))
+    rows = np.r_[0:300, (1 << 24):(1 << 24) + 8, m - 300:m]
+    idx = torch.from_numpy(rows).to(DEV)
+    got = host(out.index_select(0, idx))
+    ref = oracle.gemm(host(aq.index_select(0, idx)), host(as_.index_select(0, idx)), wq, ws)
+    del aq, out
+    ok, worst = gemm_tolerance_ok(got, ref)
+    assert ok, f"worst error / bound = {worst:.3f}"
+
+
 def test_split_halves_match_whole_tiles_bit_for_bit():
     # 4096 x 2048 runs as 256 x 128 halves, 4096 x 2560 as whole 256 x 256 tiles; both sum
     # the same scaled group partials in the same order, so the shared columns agree exactly
