@@ -20,7 +20,10 @@
 // texture/address unit, about 70 % busy with 128 x 128 tiles) needs, and 64 x 128 per wave
 // reads 0.75 KB of LDS per MFMA.  The column loop is software-pipelined: column c + 1's
 // weight fragment is read and column c - 1's products are scaled while column c
-// multiplies, one group of four FMAs between MFMAs.  When the tile count leaves the last
+// multiplies, one group of four FMAs between MFMAs; after each group's barrier the first
+// MFMA waits only for its own two fragments, each later one being read an MFMA ahead.
+// Both scales come from LDS (the weight block scale rides in the activation-scale copy),
+// so no scalar load shares the LDS reads' wait counter.  When the tile count leaves the last
 // round of workgroups at most half full, each of those last tiles is split into two
 // 256 x 128 halves (wave tiles 64 x 64): twice as many work items, each half as long.
 //
@@ -117,9 +120,11 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
   }
   // activation scales: lane L of wave w copies row 32 w + L into slot 32 w + L (lanes
   // 32..63 repeat what wave w + 1 copies: same values, same slots; no branch)
+  // lanes 32 and 33 of wave 7 (whose slots 256.. lie past the tile's rows) copy the weight
+  // block scales of the two column halves instead, into slots 256 and 257
   const float* gsp = a_scale + int64_t(min(m0 + 32 * wave + lane, m - 1)) * groups;
-  const int nb = min((n0 + kWaveCols * wn) >> 7, (n >> 7) - 1);
-  const_float* wsp = (const_float*)(w_scale + int64_t(nb) * groups);
+  if (wave == 7 && (lane == 32 || lane == 33))
+    gsp = w_scale + int64_t(min((n0 + kWaveCols * (lane - 32)) >> 7, (n >> 7) - 1)) * groups;
 
   // The copies of group g; outside [0, groups) they read a zero-size buffer (zeros written,
   // no memory traffic) and repeat a valid scale.  Every copy is unconditional: a branch
@@ -174,39 +179,63 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
                   uint8_t* nbs, float* ns) {
     __syncthreads();  // everyone's copies of group g landed (the fence drains them)
     copy_group(na, nbs, ns, g + 1);
-    const float ws = wsp[min(max(g, 0), groups - 1)];
+    // Column 0 starts as soon as B_0 and A_0 are in: each later fragment is read one MFMA
+    // ahead of its use, the scales last (their first use is column 0's FMAs, in column 1).
     v8i af[4];
+    float4 as[4];
+    v4f pcur[4], pprev[4];
+    v8i bcur = ld32(sb, b_lo, b_hi);
+    af[0] = ld32(sa, a_lo, a_hi);
+    af[1] = ld32(sa + 2048, a_lo, a_hi);
+    __builtin_amdgcn_sched_barrier(0);
+    pcur[0] = mfma_group(af[0], bcur);
+    __builtin_amdgcn_sched_barrier(0);
+    af[2] = ld32(sa + 2 * 2048, a_lo, a_hi);
+    __builtin_amdgcn_sched_barrier(0);
+    pcur[1] = mfma_group(af[1], bcur);
+    __builtin_amdgcn_sched_barrier(0);
+    af[3] = ld32(sa + 3 * 2048, a_lo, a_hi);
+    __builtin_amdgcn_sched_barrier(0);
+    pcur[2] = mfma_group(af[2], bcur);
+    __builtin_amdgcn_sched_barrier(0);
+    v8i bnxt = ld32(sb + 2048, b_lo, b_hi);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      as[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(ss) + s_off +
+                                               i * 64);
+    const float ws = ss[kBM + wn];
+    __builtin_amdgcn_sched_barrier(0);
+    pcur[3] = mfma_group(af[3], bcur);
+    __builtin_amdgcn_sched_barrier(0);
     float f[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      af[i] = ld32(sa + i * 2048, a_lo, a_hi);
-      const float4 as = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(ss) +
-                                                         s_off + i * 64);
-      f[i][0] = as.x * ws; f[i][1] = as.y * ws; f[i][2] = as.z * ws; f[i][3] = as.w * ws;
+      f[i][0] = as[i].x * ws; f[i][1] = as[i].y * ws; f[i][2] = as[i].z * ws;
+      f[i][3] = as[i].w * ws;
+      pprev[i] = pcur[i];
     }
-    v8i bcur = ld32(sb, b_lo, b_hi);
-    v4f pprev[4];
+    bcur = bnxt;
 #pragma unroll
-    for (int c = 0; c <= kCols; ++c) {
-      v8i bnxt = bcur;
+    for (int c = 1; c <= kCols; ++c) {
+      bnxt = bcur;
       if (c + 1 < kCols) bnxt = ld32(sb + (c + 1) * 2048, b_lo, b_hi);
-      v4f pcur[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (c < kCols) pcur[i] = mfma_group(af[i], bcur);
-        if (c > 0) {
-          acc[i][c - 1][0] = __builtin_fmaf(pprev[i][0], f[i][0], acc[i][c - 1][0]);
-          acc[i][c - 1][1] = __builtin_fmaf(pprev[i][1], f[i][1], acc[i][c - 1][1]);
-          acc[i][c - 1][2] = __builtin_fmaf(pprev[i][2], f[i][2], acc[i][c - 1][2]);
-          acc[i][c - 1][3] = __builtin_fmaf(pprev[i][3], f[i][3], acc[i][c - 1][3]);
-        }
+        acc[i][c - 1][0] = __builtin_fmaf(pprev[i][0], f[i][0], acc[i][c - 1][0]);
+        acc[i][c - 1][1] = __builtin_fmaf(pprev[i][1], f[i][1], acc[i][c - 1][1]);
+        acc[i][c - 1][2] = __builtin_fmaf(pprev[i][2], f[i][2], acc[i][c - 1][2]);
+        acc[i][c - 1][3] = __builtin_fmaf(pprev[i][3], f[i][3], acc[i][c - 1][3]);
       }
-      if (c > 0 && c < kCols) {  // MFMA, its neighbour's four FMAs, MFMA, ...
+      if (c < kCols) {  // MFMA, its neighbour's four FMAs, MFMA, ...
         if (c + 1 < kCols) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          if (c == 1)
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+          else
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
