@@ -20,8 +20,9 @@
 // texture/address unit, about 70 % busy with 128 x 128 tiles) needs, and 64 x 128 per wave
 // reads 0.75 KB of LDS per MFMA.  The column loop is software-pipelined: column c + 1's
 // weight fragment is read and column c - 1's products are scaled while column c
-// multiplies, one group of four FMAs between MFMAs; after each group's barrier the first
-// MFMA waits only for its own two fragments, each later one being read an MFMA ahead.
+// multiplies, one group of four FMAs between MFMAs; after each group's barrier only B_0
+// and the first two activation fragments are read before the first MFMA, each later
+// fragment an MFMA ahead of its use.
 // Both scales come from LDS (the weight block scale rides in the activation-scale copy),
 // so no scalar load shares the LDS reads' wait counter.  When the tile count leaves the last
 // round of workgroups at most half full, each of those last tiles is split into two
@@ -179,7 +180,7 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
                   uint8_t* nbs, float* ns) {
     __syncthreads();  // everyone's copies of group g landed (the fence drains them)
     copy_group(na, nbs, ns, g + 1);
-    // Column 0 starts as soon as B_0 and A_0 are in: each later fragment is read one MFMA
+    // Column 0 starts once B_0, A_0 and A_1 are in: each later fragment is read one MFMA
     // ahead of its use, the scales last (their first use is column 0's FMAs, in column 1).
     v8i af[4];
     float4 as[4];
