@@ -72,3 +72,40 @@ def test_prefill_gemm_seeded_shapes_on_sampled_rows(m, n, k):
     ref = oracle.gemm(host(q.index_select(0, idx)), host(s.index_select(0, idx)), wq, ws)
     ok, worst = gemm_tolerance_ok(got, ref)
     assert ok, f"worst error / bound = {worst:.3f}"
+
+
+@pytest.mark.parametrize("seed", range(9500, 9512))
+def test_kv_write_and_read_seeded_geometries(seed):
+    # heads, head dims, block sizes, row and pool paddings and slot maps (with skipped
+    # slots) drawn from the seed; every kernel form (wide, 8-element, element-wise) is hit
+    rng = np.random.default_rng(seed)
+    h = int(rng.choice([1, 2, 3, 4, 8]))
+    d = int(rng.choice([8, 16, 24, 40, 64, 80, 128, 256]))
+    bs = int(rng.choice([1, 4, 16, 32]))
+    nblk = int(rng.integers(4, 65))
+    e = h * d
+    t = int(rng.integers(1, min(nblk * bs, 300) + 1))
+    ks, vs = e + int(rng.choice([0, 8, 64, 3])), e + int(rng.choice([0, 8, 5]))
+    cs = bs * e + int(rng.choice([0, 128, 16]))
+    k = synth.to_bf16_bits(rng.normal(0, 3, size=t * ks))
+    v = synth.to_bf16_bits(rng.normal(0, 3, size=t * vs))
+    slots = rng.permutation(nblk * bs)[:t].astype(np.int64)
+    slots[rng.random(t) < 0.05] = -1
+    k_scale, v_scale = float(2.0 ** rng.uniform(-4, 4)), float(2.0 ** rng.uniform(-4, 4))
+    kc = np.full(nblk * cs, 0xA5, dtype=np.uint8)
+    vc = np.full(nblk * cs, 0x5A, dtype=np.uint8)
+    kcd, vcd = torch.from_numpy(kc.copy()).cuda(), torch.from_numpy(vc.copy()).cuda()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    fq.fp8_kv_write(bf16_dev(k), bf16_dev(v), kcd, vcd, dev(slots), h, d, bs, k_scale, v_scale,
+                    key_stride=ks, value_stride=vs, cache_stride=cs, num_tokens=t)
+    oracle.kv_write(k, v, kc, vc, slots, t, h, d, bs, k_scale, v_scale, ks, vs, cs)
+    assert np.array_equal(host(kcd), kc) and np.array_equal(host(vcd), vc)
+    # read the pools back through the same slots into padded rows
+    kos, vos = e + int(rng.choice([0, 8, 2])), e + int(rng.choice([0, 16]))
+    ko = np.full(t * kos, 0x1234, dtype=np.uint16)
+    vo = np.full(t * vos, 0x1234, dtype=np.uint16)
+    kod, vod = bf16_dev(ko), bf16_dev(vo)
+    fq.fp8_kv_read(kcd, vcd, dev(slots), h, d, bs, k_scale, v_scale, k_out=kod, v_out=vod,
+                   out_key_stride=kos, out_value_stride=vos, cache_stride=cs, num_tokens=t)
+    oracle.kv_read(kc, vc, slots, h, d, bs, nblk, k_scale, v_scale, ko, vo, kos, vos, cs)
+    assert np.array_equal(host(kod), ko) and np.array_equal(host(vod), vo)
