@@ -109,3 +109,16 @@ def test_kv_write_and_read_seeded_geometries(seed):
                    out_key_stride=kos, out_value_stride=vos, cache_stride=cs, num_tokens=t)
     oracle.kv_read(kc, vc, slots, h, d, bs, nblk, k_scale, v_scale, ko, vo, kos, vos, cs)
     assert np.array_equal(host(kod), ko) and np.array_equal(host(vod), vo)
+
+
+@pytest.mark.parametrize("m,n,k", _shapes(9600, 8, (1, 5), (1, 97), (1, 97)))
+def test_w8a16_seeded_shapes(m, n, k):
+    # the W8A16 tier's bound from its own arithmetic (tests/test_gpu_gemv.py): products exact
+    # in FP32, at most k/128 + 144 rounded additions, one bf16 rounding
+    a = synth.decode_activation(m, k=k, seed=m * 17 + k)
+    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=n + 3 * k))
+    out = host(fq.w8a16_block_gemv(bf16_dev(a), u8_dev(wq), f32_dev(ws)))
+    ref, mag = oracle.gemm_w8a16(a, wq, ws)
+    got = (out.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    bound = 2.0 ** -8 * np.abs(ref) + 2 * (k / 128 + 144) * 2.0 ** -24 * mag
+    assert np.all(np.abs(got - ref) <= bound)
