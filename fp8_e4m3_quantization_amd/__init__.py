@@ -11,7 +11,9 @@ from ._lib import (  # noqa: F401
     FP8Q_CALIB_FROZEN,
     FP8Q_CALIB_STAGE,
     Fp8qError,
+    KvCalibOps,
     KvCalibrator,
+    KvTarget,
     fp8_block_quant,
     fp8_e4m3_encode,
     fp8_group_quant,

@@ -22,9 +22,11 @@ FP8Q_CALIB_STAGE, FP8Q_CALIB_DECLINE, FP8Q_CALIB_FREEZE, FP8Q_CALIB_FROZEN = 0, 
 EXPORTS = (
     "fp8q_strerror", "fp8q_version", "fp8q_time_next_launch", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
     "w8a8_block_gemm", "w8a8_block_gemm_prefill", "w8a8_block_gemm_grouped",
-    "fp8_quant_w8a8_gemm_grouped", "w8a16_block_gemv", "w8a16_block_gemv_grouped", "fp8_kv_write", "fp8_kv_write_amax", "fp8_kv_read", "fp8_kv_amax", "fp8q_kv_calib_create",
-    "fp8q_kv_calib_observe", "fp8q_kv_calib_decide", "fp8q_kv_calib_scales",
-    "fp8q_kv_calib_get_info", "fp8q_kv_calib_destroy",
+    "fp8_quant_w8a8_gemm_grouped", "w8a16_block_gemv", "w8a16_block_gemv_grouped",
+    "fp8_kv_write", "fp8_kv_write_amax", "fp8_kv_read", "fp8_kv_amax",
+    "fp8q_kv_calib_create", "fp8q_kv_calib_create_with_ops", "fp8q_kv_calib_observe",
+    "fp8q_kv_calib_decide", "fp8q_kv_calib_scales", "fp8q_kv_calib_state",
+    "fp8q_kv_calib_destroy",
 )
 
 
@@ -59,6 +61,26 @@ class KvCalibInfo(ctypes.Structure):
         ("k_amax", ctypes.c_float), ("v_amax", ctypes.c_float),
         ("headroom", ctypes.c_float), ("provisional_scale", ctypes.c_float),
     ]
+
+
+_P, _I32, _I64, _U64, _F32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                              ctypes.c_float)
+
+
+class KvCalibOps(ctypes.Structure):
+    """fp8q_kv_calib_ops: the calibrator's device work as callbacks (see include/fp8q.h)."""
+    DEVICE = ctypes.CFUNCTYPE(ctypes.c_int, _P, ctypes.POINTER(_I32))
+    ALLOC = ctypes.CFUNCTYPE(ctypes.c_int, _P, _U64, ctypes.POINTER(_P), _P)
+    RELEASE = ctypes.CFUNCTYPE(ctypes.c_int, _P, _P, _P, _I32)
+    ZERO = ctypes.CFUNCTYPE(ctypes.c_int, _P, _P, _U64, _P)
+    AMAX_ROWS = ctypes.CFUNCTYPE(ctypes.c_int, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P)
+    COPY2D = ctypes.CFUNCTYPE(ctypes.c_int, _P, _P, _P, _I64, _I64, _I64, _P)
+    READ = ctypes.CFUNCTYPE(ctypes.c_int, _P, _P, _P, _U64, _P)
+    REPLAY = ctypes.CFUNCTYPE(ctypes.c_int, _P, _P, _P, _P, _P, _I32, _I32,
+                              ctypes.POINTER(KvTarget), _F32, _F32, _P)
+    _fields_ = [("ctx", _P), ("device", DEVICE), ("alloc", ALLOC), ("release", RELEASE),
+                ("zero", ZERO), ("amax_rows", AMAX_ROWS), ("copy2d", COPY2D), ("read", READ),
+                ("replay", REPLAY)]
 
 
 _lib = None
@@ -97,12 +119,15 @@ def load() -> ctypes.CDLL:
         "fp8_kv_read": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, I64, F32, F32, P, P,
                                        I32, I32, I64, P]),
         "fp8_kv_amax": (ctypes.c_int, [P, P, I64, P, P]),
-        "fp8q_kv_calib_create": (ctypes.c_int, [I32, F32, ctypes.POINTER(P)]),
+        "fp8q_kv_calib_create": (ctypes.c_int, [I32, F32, F32, ctypes.POINTER(P)]),
+        "fp8q_kv_calib_create_with_ops": (ctypes.c_int, [I32, F32, F32,
+                                                         ctypes.POINTER(KvCalibOps),
+                                                         ctypes.POINTER(P)]),
         "fp8q_kv_calib_observe": (ctypes.c_int, [P, P, P, I32, I32, I32,
                                                  ctypes.POINTER(KvTarget), P]),
         "fp8q_kv_calib_decide": (ctypes.c_int, [P, I32, I32]),
         "fp8q_kv_calib_scales": (ctypes.c_int, [P, ctypes.POINTER(F32), ctypes.POINTER(F32)]),
-        "fp8q_kv_calib_get_info": (ctypes.c_int, [P, ctypes.POINTER(KvCalibInfo)]),
+        "fp8q_kv_calib_state": (ctypes.c_int, [P, ctypes.POINTER(KvCalibInfo)]),
         "fp8q_kv_calib_destroy": (None, [P]),
     }
     for name, (res, args) in sig.items():
@@ -328,25 +353,49 @@ def fp8_quant_w8a8_gemm_grouped(a: torch.Tensor, projections, q: torch.Tensor | 
     return outs
 
 
+def _room(t: torch.Tensor) -> int:
+    """Elements a kernel may address from t.data_ptr(): the tensor itself when contiguous,
+    else the rest of its storage (row views of a wider buffer)."""
+    if t.is_contiguous():
+        return t.numel()
+    return t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+
+
+def _kv_num_blocks(k_cache, v_cache, cache_stride) -> int:
+    if k_cache.numel() != v_cache.numel() or k_cache.numel() % cache_stride:
+        raise ValueError("pools must be equal and a whole number of blocks")
+    return k_cache.numel() // cache_stride
+
+
+def _kv_tokens(slot_mapping, num_tokens) -> int:
+    t = slot_mapping.numel() if num_tokens is None else num_tokens
+    if t > slot_mapping.numel():
+        raise ValueError(f"num_tokens ({t}) exceeds slot_mapping ({slot_mapping.numel()} slots)")
+    return t
+
+
+def _kv_rows_fit(pairs, t, e) -> None:
+    for name, rows, stride in pairs:
+        if t > 0 and _room(rows) < (t - 1) * stride + e:
+            raise ValueError(f"{name} is smaller than its {t} rows")
+
+
 def _kv_write(fn, k, v, k_cache, v_cache, slot_mapping, num_kv_heads, head_dim, block_size,
               k_scale, v_scale, key_stride, value_stride, cache_stride, num_tokens, stream,
-              extra=()):
+              amax2=None):
     e = num_kv_heads * head_dim
-    t = slot_mapping.numel() if num_tokens is None else num_tokens
+    t = _kv_tokens(slot_mapping, num_tokens)
     key_stride = e if key_stride is None else key_stride
     value_stride = e if value_stride is None else value_stride
     cache_stride = block_size * e if cache_stride is None else cache_stride
-    if k_cache.numel() != v_cache.numel() or k_cache.numel() % cache_stride:
-        raise ValueError("pools must be equal and a whole number of blocks")
-    num_blocks = k_cache.numel() // cache_stride
-    for name, src, stride in (("k", k, key_stride), ("v", v, value_stride)):
-        if t > 0 and src.numel() < (t - 1) * stride + e:
-            raise ValueError(f"{name} is smaller than its rows")
+    num_blocks = _kv_num_blocks(k_cache, v_cache, cache_stride)
+    _kv_rows_fit((("k", k, key_stride), ("v", v, value_stride)), t, e)
     st = getattr(load(), fn)(_dev(k, "k", _BF16, False), _dev(v, "v", _BF16, False),
                              _dev(k_cache, "k_cache", _U8), _dev(v_cache, "v_cache", _U8),
                              _dev(slot_mapping, "slot_mapping", torch.int64), t, num_kv_heads,
                              head_dim, block_size, num_blocks, k_scale, v_scale, key_stride,
-                             value_stride, cache_stride, *extra,
+                             value_stride, cache_stride,
+                             *(() if amax2 is None else (_dev(amax2, "amax2", torch.float32),)),
                              current_stream(k.device) if stream is None else stream)
     check(fn, st)
 
@@ -374,7 +423,7 @@ def fp8_kv_write_amax(k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor,
         raise ValueError("amax2 holds two floats")
     _kv_write("fp8_kv_write_amax", k, v, k_cache, v_cache, slot_mapping, num_kv_heads,
               head_dim, block_size, k_scale, v_scale, key_stride, value_stride, cache_stride,
-              num_tokens, stream, extra=(_dev(amax2, "amax2", torch.float32),))
+              num_tokens, stream, amax2=amax2)
     return amax2
 
 
@@ -387,21 +436,16 @@ def fp8_kv_read(k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: torc
     """Dequantizing gather of paged E4M3 K/V back to bf16 rows (k_out, v_out); rows of
     tokens whose slot is out of range are left as they were (zeros when allocated here)."""
     e = num_kv_heads * head_dim
-    t = slot_mapping.numel() if num_tokens is None else num_tokens
+    t = _kv_tokens(slot_mapping, num_tokens)
     out_key_stride = e if out_key_stride is None else out_key_stride
     out_value_stride = e if out_value_stride is None else out_value_stride
     cache_stride = block_size * e if cache_stride is None else cache_stride
-    if k_cache.numel() != v_cache.numel() or k_cache.numel() % cache_stride:
-        raise ValueError("pools must be equal and a whole number of blocks")
-    num_blocks = k_cache.numel() // cache_stride
+    num_blocks = _kv_num_blocks(k_cache, v_cache, cache_stride)
     if k_out is None:
         k_out = torch.zeros((t, out_key_stride), dtype=torch.bfloat16, device=k_cache.device)
     if v_out is None:
         v_out = torch.zeros((t, out_value_stride), dtype=torch.bfloat16, device=k_cache.device)
-    for name, dst, stride in (("k_out", k_out, out_key_stride),
-                              ("v_out", v_out, out_value_stride)):
-        if t > 0 and dst.numel() < (t - 1) * stride + e:
-            raise ValueError(f"{name} is smaller than its rows")
+    _kv_rows_fit((("k_out", k_out, out_key_stride), ("v_out", v_out, out_value_stride)), t, e)
     st = load().fp8_kv_read(_dev(k_cache, "k_cache", _U8), _dev(v_cache, "v_cache", _U8),
                             _dev(slot_mapping, "slot_mapping", torch.int64), t, num_kv_heads,
                             head_dim, block_size, num_blocks, k_scale, v_scale,
@@ -425,14 +469,23 @@ def fp8_kv_amax(k: torch.Tensor, v: torch.Tensor, amax2: torch.Tensor,
 
 
 class KvCalibrator:
-    """One attention layer's online FP8 KV scale calibration (fp8q_kv_calib_*)."""
+    """One attention layer's online FP8 KV scale calibration (fp8q_kv_calib_*).  `ops`, if
+    given, is a KvCalibOps table the library calls for the calibrator's device work (kept
+    referenced here for the calibrator's lifetime); by default the library's HIP path."""
 
-    def __init__(self, window_tokens: int, headroom: float = 1.0):
+    def __init__(self, window_tokens: int, headroom: float = 1.0,
+                 provisional_scale: float = 2.0, ops: KvCalibOps | None = None):
         lib = load()
         h = ctypes.c_void_p()
-        check("fp8q_kv_calib_create", lib.fp8q_kv_calib_create(window_tokens, headroom,
-                                                                 ctypes.byref(h)))
+        if ops is None:
+            st = lib.fp8q_kv_calib_create(window_tokens, headroom, provisional_scale,
+                                          ctypes.byref(h))
+        else:
+            st = lib.fp8q_kv_calib_create_with_ops(window_tokens, headroom, provisional_scale,
+                                                   ctypes.byref(ops), ctypes.byref(h))
+        check("fp8q_kv_calib_create", st)
         self._h = h.value
+        self._ops = ops
 
     def decide(self, num_tokens: int, elems_per_token: int) -> int:
         st = load().fp8q_kv_calib_decide(self._h, num_tokens, elems_per_token)
@@ -445,19 +498,23 @@ class KvCalibrator:
                 block_size: int, key_stride: int | None = None,
                 value_stride: int | None = None, cache_stride: int | None = None,
                 stream: int | None = None) -> None:
+        """Fold the batch of slot_mapping.numel() tokens in (k, v rows at their strides);
+        the freeze replays into k_cache / v_cache."""
         e = num_kv_heads * head_dim
         cs = block_size * e if cache_stride is None else cache_stride
+        ks = e if key_stride is None else key_stride
+        vs = e if value_stride is None else value_stride
+        t = slot_mapping.numel()
+        num_blocks = _kv_num_blocks(k_cache, v_cache, cs)
+        _kv_rows_fit((("k", k, ks), ("v", v, vs)), t, e)
         tgt = KvTarget(k_pool=_dev(k_cache, "k_cache", _U8),
                        v_pool=_dev(v_cache, "v_cache", _U8),
                        slot_mapping=_dev(slot_mapping, "slot_mapping", torch.int64),
-                       block_size=block_size,
-                       key_stride=e if key_stride is None else key_stride,
-                       value_stride=e if value_stride is None else value_stride,
-                       reserved=0, cache_stride=cs, num_blocks=k_cache.numel() // cs)
+                       block_size=block_size, key_stride=ks, value_stride=vs, reserved=0,
+                       cache_stride=cs, num_blocks=num_blocks)
         st = load().fp8q_kv_calib_observe(
-            self._h, _dev(k, "k", _BF16, False), _dev(v, "v", _BF16, False),
-            slot_mapping.numel(), num_kv_heads, head_dim, ctypes.byref(tgt),
-            current_stream(k.device) if stream is None else stream)
+            self._h, _dev(k, "k", _BF16, False), _dev(v, "v", _BF16, False), t, num_kv_heads,
+            head_dim, ctypes.byref(tgt), current_stream(k.device) if stream is None else stream)
         check("fp8q_kv_calib_observe", st)
 
     def scales(self):
@@ -468,8 +525,7 @@ class KvCalibrator:
 
     def info(self) -> dict:
         inf = KvCalibInfo()
-        check("fp8q_kv_calib_get_info", load().fp8q_kv_calib_get_info(self._h,
-                                                                         ctypes.byref(inf)))
+        check("fp8q_kv_calib_state", load().fp8q_kv_calib_state(self._h, ctypes.byref(inf)))
         return {name: getattr(inf, name) for name, _ in KvCalibInfo._fields_}
 
     def close(self) -> None:

@@ -16,7 +16,7 @@
 // Two forms: the persistent kernel below (k <= 8192; one workgroup per CU walks strips,
 // each wave keeping its activation slice in registers), and w8a8_gemm_kernel for longer k
 // (one workgroup per strip; the activation, <= 16 x K bytes and L2-resident, is read per
-// wave and its scales are staged in LDS, transposed to [group][row]).
+// wave together with its row scales, so the LDS it needs does not grow with k).
 // Rows >= m are fed zeros and never stored, so only (m-1)*ldc + n elements are written.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -31,7 +31,7 @@
 namespace fp8q {
 namespace {
 
-constexpr int kMaxGemmK = 131072;  // LDS holds the [k/128][16] activation scales
+constexpr int kMaxGemmK = 131072;
 
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
   const uint4* q = reinterpret_cast<const uint4*>(p);
@@ -54,18 +54,10 @@ __global__ __launch_bounds__(64 * kWaves) void w8a8_gemm_kernel(
     const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale,
     const uint8_t* __restrict__ w_q, const float* __restrict__ w_scale,
     uint16_t* __restrict__ out, int m, int k, int ldc) {
-  extern __shared__ float smem[];
+  __shared__ float s_part[kWaves * 4 * 64];
   const int groups = k >> 7;
-  float* s_as = smem;                    // [groups][16]
-  float* s_part = smem + groups * 16;    // [kWaves][4][64]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n0 = blockIdx.x * 16;
-
-  for (int i = tid; i < groups * 16; i += 64 * kWaves) {
-    const int g = i >> 4, r = i & 15;
-    s_as[i] = r < m ? a_scale[int64_t(r) * groups + g] : 0.0f;
-  }
-  __syncthreads();
 
   // Operand layout: lane l supplies row (l & 15) of the 16-row operand and bytes
   // [32*(l>>4), 32*(l>>4)+32) of the group; A (activation rows) and B (weight rows,
@@ -77,41 +69,52 @@ __global__ __launch_bounds__(64 * kWaves) void w8a8_gemm_kernel(
   const bool a_live = row < m;
   const uint8_t* ap = a_q + int64_t(a_live ? row : 0) * k + koff;
   const float* wsp = w_scale + int64_t(n0 >> 7) * groups;
-  const float* asp = s_as + (lane >> 4) * 4;  // the 4 output rows this lane holds
+  // The 4 output rows this lane's accumulators hold: r0 .. r0 + 3.  Their activation scales
+  // are read per group from the token-major grid (L2-resident: at most 16 * k/128 floats);
+  // rows >= m read row m - 1 (in bounds) and are weighted by zero.
+  const int r0 = 4 * (lane >> 4);
+  const float* asr[4];
+  float live[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    asr[j] = a_scale + int64_t(min(r0 + j, m - 1)) * groups;
+    live[j] = r0 + j < m ? 1.0f : 0.0f;
+  }
 
   const int g_begin = (groups * wv) / kWaves;
   const int g_end = (groups * (wv + 1)) / kWaves;
   v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
   const v8i zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 
+  auto step = [&](const v8i& a, const v8i& b, float ws, const float4& as) {
+    const v4f c = mfma_group(a, b);
+    acc[0] = __builtin_fmaf(c[0], as.x * ws, acc[0]);
+    acc[1] = __builtin_fmaf(c[1], as.y * ws, acc[1]);
+    acc[2] = __builtin_fmaf(c[2], as.z * ws, acc[2]);
+    acc[3] = __builtin_fmaf(c[3], as.w * ws, acc[3]);
+  };
+  auto row_scales = [&](int g) {
+    return make_float4(asr[0][g] * live[0], asr[1][g] * live[1], asr[2][g] * live[2],
+                       asr[3][g] * live[3]);
+  };
+
   int g = g_begin;
   for (; g + kChunk <= g_end; g += kChunk) {
     v8i b[kChunk], a[kChunk];
+    float4 as[kChunk];
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) b[u] = load32(wp + int64_t(g + u) * 128);
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) a[u] = a_live ? load32(ap + int64_t(g + u) * 128) : zero8;
 #pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-      const v4f c = mfma_group(a[u], b[u]);
-      const float ws = wsp[g + u];
-      const float4 as = *reinterpret_cast<const float4*>(asp + (g + u) * 16);
-      acc[0] = __builtin_fmaf(c[0], as.x * ws, acc[0]);
-      acc[1] = __builtin_fmaf(c[1], as.y * ws, acc[1]);
-      acc[2] = __builtin_fmaf(c[2], as.z * ws, acc[2]);
-      acc[3] = __builtin_fmaf(c[3], as.w * ws, acc[3]);
-    }
+    for (int u = 0; u < kChunk; ++u) as[u] = row_scales(g + u);
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) step(a[u], b[u], wsp[g + u], as[u]);
   }
   for (; g < g_end; ++g) {
     const v8i b = load32(wp + int64_t(g) * 128);
     const v8i a = a_live ? load32(ap + int64_t(g) * 128) : zero8;
-    const v4f c = mfma_group(a, b);
-    const float ws = wsp[g];
-    const float4 as = *reinterpret_cast<const float4*>(asp + g * 16);
-    acc[0] = __builtin_fmaf(c[0], as.x * ws, acc[0]);
-    acc[1] = __builtin_fmaf(c[1], as.y * ws, acc[1]);
-    acc[2] = __builtin_fmaf(c[2], as.z * ws, acc[2]);
-    acc[3] = __builtin_fmaf(c[3], as.w * ws, acc[3]);
+    step(a, b, wsp[g], row_scales(g));
   }
 
   // Accumulator layout: lane l, register j holds row 4*(l>>4) + j, column l & 15.
@@ -367,9 +370,8 @@ template <int kWaves, int kChunk>
 int launch_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
                 const float* w_scale, uint16_t* out, int m, int n, int k, int ldc,
                 hipStream_t stream) {
-  const size_t lds = size_t(k / 128) * 16 * sizeof(float) + size_t(kWaves) * 256 * sizeof(float);
-  launch((w8a8_gemm_kernel<kWaves, kChunk>), dim3(n / 16), dim3(64 * kWaves),
-                     lds, stream, a_q, a_scale, w_q, w_scale, out, m, k, ldc);
+  launch((w8a8_gemm_kernel<kWaves, kChunk>), dim3(n / 16), dim3(64 * kWaves), 0, stream, a_q,
+         a_scale, w_q, w_scale, out, m, k, ldc);
   return launch_status();
 }
 

@@ -285,16 +285,18 @@ int fp8_kv_amax(const uint16_t* k, const uint16_t* v, int64_t n_elems, float* am
  * One attention layer's per-tensor K/V scale calibration.  Inside the window each
  * observed batch's |K|/|V| maximum folds into a running maximum kept on the device, and
  * the batch (bf16 rows + slots) is copied into packed staging; the caller then writes
- * it at the provisional scale 2.0.  The observe whose token count reaches the window
- * freezes scale = (max(amax, 1e-10) * headroom) / 448 for K and V over every observed
- * token including its own batch, replays the staged batches at the frozen scales into
- * the target pools (one write of every staged token whose slot no later staged token
- * writes, which leaves the bytes an in-order replay leaves), and frees the staging; the caller then writes
- * that batch at the frozen scales.  Later observes do nothing.  A batch whose heads x
- * head_dim differ from the first staged batch is not staged (it keeps the provisional
- * scale).  The window is clamped to 4096 tokens and headroom to >= 1.
+ * it at the provisional scale.  The observe whose token count reaches the window freezes
+ * scale = (max(amax, 1e-10) * headroom) / 448 for K and V over every observed token
+ * including its own batch, replays the staged batches at the frozen scales into the
+ * target pools (one write of every staged token whose slot no later staged token writes,
+ * which leaves the bytes an in-order replay leaves), and releases the staging in stream
+ * order; the caller then writes that batch at the frozen scales.  Later observes do
+ * nothing.  A batch whose heads x head_dim differ from the first staged batch, or that
+ * would overflow the window's staging, is not staged (it keeps the provisional scale).
+ * The window is clamped to 4096 tokens and headroom to >= 1.
  * Call order per batch: fp8q_kv_calib_observe, then fp8q_kv_calib_scales, then the
- * caller's fp8_kv_write of that batch, all on one stream. */
+ * caller's fp8_kv_write of that batch, all on one stream.  Not capturable in a HIP graph
+ * (the freeze reads the running maximum back to the host). */
 typedef struct fp8q_kv_calib fp8q_kv_calib;
 
 /* Where the replay writes (the live write's own pools and geometry). */
@@ -333,14 +335,66 @@ typedef struct fp8q_kv_calib_info {
 #define FP8Q_CALIB_FREEZE 2
 #define FP8Q_CALIB_FROZEN 3
 
-/* window_tokens > 0 (window 0 means no calibrator: FP8Q_EINVAL); headroom finite.
- * Allocates host state only; device buffers are allocated on the first observe, on the
- * device current then.  *out receives the handle. */
-int fp8q_kv_calib_create(int32_t window_tokens, float headroom, fp8q_kv_calib** out);
+/* The device work of a calibrator, as a table of callbacks ([staging] and [calib] take a
+ * GPU backend object for the same purpose).  The calibrator's bookkeeping (window, stage,
+ * decline, freeze formula and range check, replay order, counters) only calls these; it
+ * never touches device memory itself, so a table backed by host memory runs the whole
+ * state machine on a CPU.  fp8q_kv_calib_create uses the library's own HIP table.
+ * Every callback returns FP8Q_OK or a negative FP8Q_E* status, which observe returns.
+ *   device      the current device (observe refuses a device other than the first one)
+ *   alloc       *out = `bytes` of device memory, usable by work enqueued on `stream` after
+ *               this call (HIP: hipMallocAsync)
+ *   release     free what alloc returned: in stream order after the work enqueued on
+ *               `stream` when at_destroy == 0; when at_destroy != 0 (from
+ *               fp8q_kv_calib_destroy, stream unused) only once all device work is done
+ *   zero        bytes of p = 0, stream-ordered
+ *   amax_rows   amax2[0] = max(amax2[0], max|k|), amax2[1] likewise for v, over `rows` rows of
+ *               `elems` bf16 at key/value strides (elements), stream-ordered
+ *   copy2d      `rows` rows of row_bytes bytes from src (rows src_pitch bytes apart) to dst,
+ *               packed, stream-ordered
+ *   read        bytes from device src to host dst once the work enqueued on `stream` is done
+ *               (blocks the caller)
+ *   replay      write n staged packed rows (`elems` bf16 each, K and V) to the target's pools
+ *               at (k_scale, v_scale) as fp8_kv_write would write them one after another in
+ *               staging order (a slot staged twice keeps its later row); scratch_slots is
+ *               int64 [n] of device scratch the callback may use; stream-ordered */
+typedef struct fp8q_kv_calib_ops {
+  void* ctx;
+  int (*device)(void* ctx, int32_t* dev);
+  int (*alloc)(void* ctx, uint64_t bytes, void** out, hipStream_t stream);
+  int (*release)(void* ctx, void* p, hipStream_t stream, int32_t at_destroy);
+  int (*zero)(void* ctx, void* p, uint64_t bytes, hipStream_t stream);
+  int (*amax_rows)(void* ctx, const uint16_t* k, const uint16_t* v, int64_t rows,
+                   int64_t elems, int64_t key_stride, int64_t value_stride, float* amax2,
+                   hipStream_t stream);
+  int (*copy2d)(void* ctx, void* dst, const void* src, int64_t src_pitch, int64_t row_bytes,
+                int64_t rows, hipStream_t stream);
+  int (*read)(void* ctx, void* host_dst, const void* src, uint64_t bytes, hipStream_t stream);
+  int (*replay)(void* ctx, const uint16_t* k, const uint16_t* v, const int64_t* slots,
+                int64_t* scratch_slots, int32_t n, int32_t elems, const fp8q_kv_target* target,
+                float k_scale, float v_scale, hipStream_t stream);
+} fp8q_kv_calib_ops;
+
+/* window_tokens > 0 (window 0 means no calibrator: FP8Q_EINVAL); headroom finite and
+ * <= 2^64 (values below 1 are raised to 1); provisional_scale in [2^-64, 2^64] (the
+ * pages use 2.0).  Allocates host state only; device buffers are allocated on the first
+ * observe, on the device current then.  *out receives the handle.
+ * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EHIP (host allocation). */
+int fp8q_kv_calib_create(int32_t window_tokens, float headroom, float provisional_scale,
+                         fp8q_kv_calib** out);
+/* As fp8q_kv_calib_create, with the device work going through `ops` (copied; every
+ * callback must be set; the table's ctx must outlive the calibrator). */
+int fp8q_kv_calib_create_with_ops(int32_t window_tokens, float headroom,
+                                  float provisional_scale, const fp8q_kv_calib_ops* ops,
+                                  fp8q_kv_calib** out);
 /* Fold one batch in (see above).  k, v: device bf16 [num_tokens] rows at the target's
- * key/value strides.  Enqueues work on `stream`; synchronizes `stream` only at the freeze
- * (to read the 8-byte running maximum, and again before freeing the staging).  The
- * first staged batch allocates the staging (window * H * D * 2 * 2 + window * 16 bytes).
+ * key/value strides.  Enqueues work on `stream`; blocks only at the freeze, to read the
+ * 8-byte running maximum back.  The first staged batch allocates the staging (window * H *
+ * D * 2 * 2 + window * 16 bytes, stream-ordered), the freeze releases it in stream order.
+ * A frozen scale outside [2^-64, 2^64] (the write's scale range) fails the freezing
+ * observe with FP8Q_EINVAL and leaves the calibrator as it was (the batch's absmax may
+ * already be folded into the running maximum; folding the same batch again changes
+ * nothing).
  * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EHIP, FP8Q_ELAUNCH, FP8Q_ESTATE. */
 int fp8q_kv_calib_observe(fp8q_kv_calib* c, const uint16_t* k, const uint16_t* v,
                           int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
@@ -348,10 +402,11 @@ int fp8q_kv_calib_observe(fp8q_kv_calib* c, const uint16_t* k, const uint16_t* v
 /* Pure query: FP8Q_CALIB_* for a batch of num_tokens x elems_per_token, or < 0. */
 int fp8q_kv_calib_decide(const fp8q_kv_calib* c, int32_t num_tokens,
                          int32_t elems_per_token);
-/* The scales the caller writes with now (provisional 2.0 until the freeze). */
+/* The scales the caller writes with now (provisional until the freeze). */
 int fp8q_kv_calib_scales(const fp8q_kv_calib* c, float* k_scale, float* v_scale);
-int fp8q_kv_calib_get_info(const fp8q_kv_calib* c, fp8q_kv_calib_info* info);
-/* Frees staging and device state (synchronizing the device that owns them). NULL ok. */
+/* Snapshot of the calibrator's counters, scales and running maxima. */
+int fp8q_kv_calib_state(const fp8q_kv_calib* c, fp8q_kv_calib_info* info);
+/* Frees staging and device state (after all device work is done). NULL ok. */
 void fp8q_kv_calib_destroy(fp8q_kv_calib* c);
 
 #ifdef __cplusplus

@@ -5,12 +5,16 @@ may import this package.  The product path (the HIP library and its Python bindi
 does, and the two share no code: this file wraps the plain C in ``fp8_oracle.c`` with
 numpy arrays.  Every function states the passage of the pages it follows in the C source.
 
-Functions (all single-threaded, in the order the pages define them):
+Functions (single-threaded, in the order the pages define them; the *_rows wrappers run the
+same C routine on disjoint row ranges in parallel threads, so every element is computed by
+exactly the arithmetic of the single-threaded call):
   e4m3_decode(codes)                 -> float64 values (NaN for S.1111.111)
   e4m3_encode(v), e4m3_encode_search(v) -> uint8 codes (two independent encoders)
   group_quant(x_bf16[m,k])           -> (q uint8[m,k], scales f32[m,k/128])
   block_quant(w_bf16[n,k])           -> (wq uint8[n,k], ws f32[ceil(n/128),ceil(k/128)])
   gemm(a_q, a_s, w_q, w_s)           -> float64[m,n] reference
+  gemm_rows(a_q, a_s, w_q, w_s, threads) the same, rows split over host threads
+  group_quant_rows(x_bf16, threads)  group_quant, rows split over host threads
   gemm_w8a16(a_bf16, w_q, w_s)       -> (float64[m,n] reference, float64[m,n] sum of |terms|)
   amax(x_bf16)                       -> float32
   kv_write(...)                      in-place on the uint8 pools
@@ -162,6 +166,73 @@ def gemm(a_q, a_s, w_q, w_s) -> np.ndarray:
     ref = np.empty((m, n), dtype=np.float64)
     lib.oracle_gemm(_ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), m, n, k, _ptr(ref))
     return ref
+
+
+MAX_THREADS = 16  # a single-GPU host's CPU share
+
+
+def default_threads() -> int:
+    """Host threads the *_rows wrappers use by default: the CPUs this process may run on,
+    at most MAX_THREADS."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, MAX_THREADS))
+
+
+def _row_ranges(m, threads):
+    threads = max(1, min(int(threads or default_threads()), m))
+    step = -(-m // threads)
+    return [(r, min(m, r + step)) for r in range(0, m, step)]
+
+
+def gemm_rows(a_q, a_s, w_q, w_s, threads=None) -> np.ndarray:
+    """gemm() with the rows of the result split over `threads` host threads (default:
+    default_threads()); each range is one call of the same C routine, which keeps no shared
+    state, so the result equals gemm()'s bit for bit."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    lib = _load()
+    a_q = np.ascontiguousarray(a_q, dtype=np.uint8)
+    a_s = np.ascontiguousarray(a_s, dtype=np.float32)
+    w_q = np.ascontiguousarray(w_q, dtype=np.uint8)
+    w_s = np.ascontiguousarray(w_s, dtype=np.float32)
+    m, k = a_q.shape
+    n = w_q.shape[0]
+    assert w_q.shape[1] == k and a_s.shape == (m, k // 128)
+    assert w_s.shape == ((n + 127) // 128, k // 128)
+    ref = np.empty((m, n), dtype=np.float64)
+
+    def run(rng):
+        r0, r1 = rng
+        lib.oracle_gemm(a_q[r0:].ctypes.data, a_s[r0:].ctypes.data, _ptr(w_q), _ptr(w_s),
+                        r1 - r0, n, k, ref[r0:].ctypes.data)
+
+    with ThreadPoolExecutor(len(_row_ranges(m, threads))) as ex:
+        list(ex.map(run, _row_ranges(m, threads)))
+    return ref
+
+
+def group_quant_rows(x_bf16, threads=None):
+    """group_quant() with the rows split over `threads` host threads (default:
+    default_threads()); equal to group_quant() bit for bit."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    lib = _load()
+    x = _u16(x_bf16)
+    m, k = x.shape
+    q = np.empty((m, k), dtype=np.uint8)
+    s = np.empty((m, k // 128), dtype=np.float32)
+
+    def run(rng):
+        r0, r1 = rng
+        lib.oracle_group_quant(x[r0:].ctypes.data, r1 - r0, k, q[r0:].ctypes.data,
+                               s[r0:].ctypes.data)
+
+    with ThreadPoolExecutor(len(_row_ranges(m, threads))) as ex:
+        list(ex.map(run, _row_ranges(m, threads)))
+    return q, s
 
 
 def gemm_w8a16(a_bf16, w_q, w_s):

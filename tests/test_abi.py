@@ -106,9 +106,9 @@ def test_calibrator_host_logic_without_gpu():
     """create / decide / scales / info / destroy never touch the device."""
     lib = fq.load()
     h = ctypes.c_void_p()
-    assert lib.fp8q_kv_calib_create(0, 1.0, ctypes.byref(h)) == EINVAL  # window 0: none
-    assert lib.fp8q_kv_calib_create(8, float("nan"), ctypes.byref(h)) == EINVAL
-    assert lib.fp8q_kv_calib_create(8, 1.0, None) == ENULL
+    assert lib.fp8q_kv_calib_create(0, 1.0, 2.0, ctypes.byref(h)) == EINVAL  # window 0: none
+    assert lib.fp8q_kv_calib_create(8, float("nan"), 2.0, ctypes.byref(h)) == EINVAL
+    assert lib.fp8q_kv_calib_create(8, 1.0, 2.0, None) == ENULL
     cal = fq.KvCalibrator(10 ** 6, 0.25)
     info = cal.info()
     assert info["window_tokens"] == 4096 and info["requested_tokens"] == 10 ** 6

@@ -247,6 +247,37 @@ def test_long_k_both_kernel_forms(k):
     _check(synth.decode_activation(7, k=k, seed=k), wq, ws)
 
 
+@pytest.mark.parametrize("k", [122880 + 128, 131072])
+def test_documented_k_maximum_single_grouped_and_fused(k):
+    """The top of the documented k range (k <= 131072), where the long-k kernel runs: the
+    single call, the grouped call and the fused call (quantizing through the caller's code
+    buffers) all within the tolerance of the oracle, and the three bit-identical."""
+    m = 3
+    a = synth.decode_activation(m, k=k, seed=k + 7)
+    q_ref, s_ref = oracle.group_quant(a)
+    w1 = _weights(256, k, 11)
+    ref1 = oracle.gemm(q_ref, s_ref, *w1)
+    w2q, w2s = oracle.block_quant(synth.decode_weight(128, k, seed=12))
+    ref2 = oracle.gemm(q_ref, s_ref, w2q, w2s)
+    a_d = bf16_dev(a)
+    q, s = fq.fp8_group_quant(a_d)
+    assert np.array_equal(host(q), q_ref)
+    single = host(fq.w8a8_block_gemm(q, s, u8_dev(w1[0]), f32_dev(w1[1])))
+    ok, worst = gemm_tolerance_ok(single, ref1)
+    assert ok, worst
+    projs = [(u8_dev(w1[0]), f32_dev(w1[1]), None), (u8_dev(w2q), f32_dev(w2s), None)]
+    grouped = [host(o) for o in fq.w8a8_block_gemm_grouped(q, s, projs)]
+    q2 = torch.full_like(q, 0x5A)
+    s2 = torch.full_like(s, -1.0)
+    fused = [host(o) for o in fq.fp8_quant_w8a8_gemm_grouped(a_d, projs, q=q2, scales=s2)]
+    assert np.array_equal(host(q2), q_ref)
+    ok, worst = gemm_tolerance_ok(grouped[1], ref2)
+    assert ok, worst
+    for g, f in zip(grouped, fused):
+        assert np.array_equal(g, f)
+    assert np.array_equal(grouped[0], single)
+
+
 @pytest.mark.parametrize("m", [16, 5, 1])
 def test_fused_quant_gemm_matches_separate_calls(m):
     """Quantizing inside the GEMM gives the standalone quantizer's codes/scales and the

@@ -2,9 +2,10 @@
 
 Bar as for the decode GEMM: |gpu - ref| <= 1e-2 |ref| + 1e-3 rms(ref) per bf16 output (rms
 over the outputs compared); bit-exact where the sums are exact.  Small and ragged shapes
-are compared in full; the 4593-token prefill shape on sampled rows (first, middle, last
-row tiles, the ragged tail) and sampled 128-column blocks, which the oracle computes from
-the same codes and scales.
+are compared in full; the 4593-token prefill shapes on every row of one 128-column block in
+each 2048 columns, and on sampled rows (first, middle, last row tiles, the ragged tail) of
+the first, middle and last blocks, which the oracle computes from the same codes and
+scales.
 
 The library picks the 256 x 256 tiling once a problem has at least half a round of such
 tiles (128 on the 256-CU MI355X) and splits the tiles of a last round that is at most half
@@ -139,6 +140,25 @@ def test_prefill_shape_on_sampled_outputs(n):
                           np.ascontiguousarray(wq[b * 128:(b + 1) * 128]),
                           np.ascontiguousarray(ws[b:b + 1]))
         ok, worst = gemm_tolerance_ok(got[rows, b * 128:(b + 1) * 128], ref)
+        assert ok, f"block {b}: worst error / bound = {worst:.3f}"
+
+
+@pytest.mark.parametrize("n", [5120, 16384])
+def test_prefill_shape_every_row_of_one_block_per_2048_columns(n):
+    """The 4593-token shapes (18 row tiles of 256 with a ragged tail of 241 rows, the XCD
+    tile walk, the split last round) on every output row, for one 128-column block in each
+    2048 columns (block position varies), against the oracle run row-parallel."""
+    k, m = 5120, synth.PREFILL_TOKENS
+    a = synth.prefill_activation(k, seed=3100)
+    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=2100 + n))
+    q, s = _quant(a)
+    got = host(fq.w8a8_block_gemm_prefill(q, s, u8_dev(wq), f32_dev(ws)))
+    qh, sh = host(q), host(s)
+    for i in range(-(-n // 2048)):
+        b = min(i * 16 + (5 * i + 3) % 16, n // 128 - 1)
+        ref = oracle.gemm_rows(qh, sh, np.ascontiguousarray(wq[b * 128:(b + 1) * 128]),
+                               np.ascontiguousarray(ws[b:b + 1]))
+        ok, worst = gemm_tolerance_ok(got[:, b * 128:(b + 1) * 128], ref)
         assert ok, f"block {b}: worst error / bound = {worst:.3f}"
 
 

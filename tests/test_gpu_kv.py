@@ -202,6 +202,39 @@ def test_calibration_replay_with_heavy_slot_reuse_matches_oracle():
     assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
 
 
+def test_calibrator_destroyed_inside_the_window_releases_its_staging():
+    """Staging allocated in stream order and never frozen: destroy waits for the device and
+    releases it; a second calibrator on the same pools then runs to the oracle's result."""
+    batches, _ = synth.kv_batches(num_tokens_total=synth.KV_WINDOW + 96, seed=5030)
+    kc, vc, kcd, vcd = _pools()
+    first = fq.KvCalibrator(synth.KV_WINDOW)
+    for b in batches[:3]:
+        first.observe(bf16_dev(b.k), bf16_dev(b.v), H, D, kcd, vcd, i64_dev(b.slots), BS)
+    assert first.info()["staged_tokens"] == sum(len(b.slots) for b in batches[:3])
+    first.close()
+    got_k, got_v, info = _calibrate_on_gpu(batches, synth.KV_WINDOW)
+    kc_ref, vc_ref, ref = _calibrate_oracle(batches, synth.KV_WINDOW)
+    assert info["replayed_tokens"] == ref["replayed_tokens"]
+    assert np.array_equal(got_k, kc_ref) and np.array_equal(got_v, vc_ref)
+
+
+def test_calibrator_frozen_scale_out_of_range_is_refused_on_the_gpu():
+    """headroom 2^64 over |K| ~ 1e4 puts the frozen scale above 2^64: the freezing observe
+    fails with EINVAL and nothing is replayed or frozen."""
+    rng = np.random.default_rng(31)
+    k = synth.to_bf16_bits(rng.normal(0, 1e4, size=(8, E)))
+    v = synth.to_bf16_bits(rng.normal(0, 1, size=(8, E)))
+    kc, vc, kcd, vcd = _pools()
+    cal = fq.KvCalibrator(8, 2.0 ** 64)
+    with pytest.raises(fq.Fp8qError) as err:
+        cal.observe(bf16_dev(k), bf16_dev(v), H, D, kcd, vcd, i64_dev(np.arange(8)), BS)
+    assert err.value.status == -1
+    info = cal.info()
+    assert info["frozen"] == 0 and info["tokens_seen"] == 0 and cal.scales() == (2.0, 2.0)
+    cal.close()
+    assert np.array_equal(host(kcd), kc) and np.array_equal(host(vcd), vc)
+
+
 # ------------------------------------------------------------------ dequantizing read
 
 

@@ -202,3 +202,19 @@ def test_w8a16_integer_exact_case_by_brute_force(orc):
         for j in range(0, n, 37):
             want = sum(av[i, kk] * wv[j, kk] * float(w_s[j // 128, kk // 128]) for kk in range(k))
             assert ref[i, j] == want
+
+
+def test_row_parallel_wrappers_equal_the_single_threaded_calls(orc):
+    """gemm_rows / group_quant_rows run the same C routine on disjoint row ranges: results
+    identical to the single-threaded calls (uneven ranges, more threads than rows)."""
+    rng = np.random.default_rng(17)
+    a = synth.to_bf16_bits(rng.normal(0, 2, size=(37, 384)))
+    q, s = orc.group_quant(a)
+    for threads in (1, 3, 8, 64):
+        q2, s2 = orc.group_quant_rows(a, threads)
+        assert np.array_equal(q, q2) and np.array_equal(s.view(np.uint32), s2.view(np.uint32))
+    wq, ws = orc.block_quant(synth.to_bf16_bits(rng.normal(0, 0.02, size=(256, 384))))
+    ref = orc.gemm(q, s, wq, ws)
+    for threads in (1, 5, 64):
+        assert np.array_equal(orc.gemm_rows(q, s, wq, ws, threads), ref)
+    assert 1 <= orc.default_threads() <= orc.MAX_THREADS
