@@ -18,9 +18,13 @@ one fused launch), the KV write, absmax and dequantizing read over a full 2048-b
 (slots a random permutation of all 32768; the write and read again with the slots of a
 paged prefill, blocks in random order and 16 consecutive tokens per block), and the
 per-batch latency of the decode-time write (absmax fused in) for 1, 4, 16 and 64 tokens.
-The roofline object covers the step's dominant kernel (the fused quant + four-projection
-GEMM); cpu_baseline times the CPU oracle on full steps (about 10 s of single-threaded CPU
-work).
+The K-split entry point is timed at each N beside the plain GEMM; the prefill GEMM's
+operands rotate over >= 1 GB like every other leg.  Reference rows: an empty kernel and a
+plain 2:1 read/write stream of the group quantizer's and the KV write's bytes, timed by the
+same hook.  The calibration window (256 tokens of seeded paged batches) reports the latency
+of an in-window observe and of the freezing observe.  The roofline object covers the step's
+dominant kernel (the fused quant + four-projection GEMM); cpu_baseline times the CPU oracle
+on full steps, single-threaded and with quant and GEMM split by rows over the host threads.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -49,7 +53,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="",
                    help="comma list of sections: step,gemm,grouped,sweep,gemv,prefill,quant,"
-                        "kv (default all)")
+                        "kv,calib (default all)")
     return p.parse_args()
 
 
@@ -225,7 +229,7 @@ def main():
     fq.load()
     timer = Timer(torch, fq.load())
     only = (set(args.only.split(",")) if args.only
-            else {"step", "gemm", "grouped", "sweep", "gemv", "prefill", "quant", "kv"})
+            else {"step", "gemm", "grouped", "sweep", "gemv", "prefill", "quant", "kv", "calib"})
     kernels = {}
 
     def log(msg):
@@ -323,6 +327,21 @@ def main():
                 tflops=round(fl / (mean_us * 1e-6) / 1e12, 2), bytes=b)
             log(f"gemm n={n}: {mean_us:.2f} us (median {med_us:.2f}) "
                 f"{kernels[f'w8a8_gemm_m16_n{n}_k5120']['gbs']} GB/s")
+            # the same projection through the K-split entry point (its own workspace per
+            # stream; shapes with enough strips run the kernel above unchanged)
+            ws_bytes = fq.w8a8_block_gemm_workspace_size(M_DECODE, n, K_DECODE)
+            launches = [(lambda s=s, n=n: fq.w8a8_block_gemm_ws(s["q"], s["s"], s["w"][n][0],
+                                                                s["w"][n][1], s["out"][n]))
+                        for s in sets]
+            mean_us, med_us = timer.kernel_us(launches, args.iters)
+            kernels[f"w8a8_gemm_ws_m16_n{n}_k5120"] = dict(
+                us=round(mean_us, 3), us_median=round(med_us, 3),
+                gbs=round(b / (mean_us * 1e-6) / 1e9, 1),
+                frac_hbm=round(b / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                tflops=round(fl / (mean_us * 1e-6) / 1e12, 2), bytes=b,
+                workspace_bytes=ws_bytes, split=ws_bytes > 0)
+            log(f"gemm (K-split entry) n={n}: {mean_us:.2f} us, workspace {ws_bytes} B, "
+                f"{kernels[f'w8a8_gemm_ws_m16_n{n}_k5120']['gbs']} GB/s")
 
     if "grouped" in only:
         for s in sets:
@@ -373,25 +392,30 @@ def main():
 
     # --------------------------------------- W8A8 GEMM at the 4593-token prefill width
     if "prefill" in only:
+        # operands and outputs rotate over >= 1 GB of sets (codes, scales, weights, output)
         m = synth.PREFILL_TOKENS
         a = bf16_dev(torch, synth.prefill_activation(K_DECODE, seed=3100))
-        q, s = fq.fp8_group_quant(a)
+        q0, s0 = fq.fp8_group_quant(a)
         del a
         for n in (16384, 5120):
-            wq, ws = sets[0]["w"][n]
-            outs = [torch.empty((m, n), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
-            launches = [(lambda o=o: fq.w8a8_block_gemm_prefill(q, s, wq, ws, o)) for o in outs]
+            wq0, ws0 = sets[0]["w"][n]
+            per = m * K_DECODE + n * K_DECODE + m * n * 2
+            nset = rotation_sets(per)
+            ps = [(q0.clone(), s0.clone(), wq0.clone(), ws0.clone(),
+                   torch.empty((m, n), dtype=torch.bfloat16, device="cuda")) for _ in range(nset)]
+            launches = [(lambda p=p: fq.w8a8_block_gemm_prefill(*p[:4], p[4])) for p in ps]
             launches[0]()
             mean_us, med_us = timer.kernel_us(launches, min(args.iters, 50))
             fl = 2.0 * m * n * K_DECODE
             key = f"w8a8_gemm_prefill_m{m}_n{n}_k5120"
             kernels[key] = dict(us=round(mean_us, 3), us_median=round(med_us, 3),
                                 tflops=round(fl / (mean_us * 1e-6) / 1e12, 1),
-                                frac_mfma_fp8=round(fl / (mean_us * 1e-6) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4))
+                                frac_mfma_fp8=round(fl / (mean_us * 1e-6) / 1e12 / FP8_MFMA_PEAK_TFLOPS, 4),
+                                rotation_sets=nset)
             log(f"prefill gemm m={m} n={n}: {mean_us:.1f} us {kernels[key]['tflops']} TFLOP/s "
-                f"({kernels[key]['frac_mfma_fp8']:.3f} of fp8 MFMA peak)")
-            del outs
-        del q, s
+                f"({kernels[key]['frac_mfma_fp8']:.3f} of fp8 MFMA peak, {nset} operand sets)")
+            del ps, launches
+        del q0, s0
 
     # ----------------------------------------------------------- width sweep
     if "sweep" in only:
@@ -515,6 +539,43 @@ def main():
             log(f"{name}: {mean_us:.2f} us {kernels[f'{name}_t{t}']['gbs']} GB/s")
         del bufs, run_slots
 
+    # ------------------------------------------------- measurement references
+    # What a launch costs with no work, and a plain 2:1 read/write stream of the same bytes
+    # as the group quantizer and the KV write (no arithmetic), timed by the same hook: the
+    # ceiling the bandwidth kernels are read against.
+    if "quant" in only or "kv" in only:
+        lib = fq.load()
+        stream = torch.cuda.current_stream().cuda_stream
+        mean_us, med_us = timer.kernel_us([lambda: lib.fp8q_reference_empty(stream)], args.iters)
+        refs = {"empty_kernel": dict(us=round(mean_us, 3), us_median=round(med_us, 3))}
+        log(f"reference empty kernel: {mean_us:.2f} us (median {med_us:.2f})")
+        shapes = {f"group_quant_m{synth.PREFILL_TOKENS}_k{k}": (quant_bytes(synth.PREFILL_TOKENS, k),
+                                                               synth.PREFILL_TOKENS * k * 2)
+                  for k in synth.PREFILL_K}
+        shapes["kv_write_full_pool_t32768"] = (kv_write_bytes(KV_NB * KV_BS), 2 * KV_NB * KV_BS * e * 2)
+        for name, (alg_bytes, read_bytes) in shapes.items():
+            nset = rotation_sets(read_bytes * 3 // 2)
+            bufs = [(torch.ones(read_bytes // 2, dtype=torch.int16, device="cuda"),
+                     torch.empty(read_bytes // 2, dtype=torch.uint8, device="cuda"))
+                    for _ in range(nset)]
+            launches = [(lambda b=b, rb=read_bytes: lib.fp8q_reference_stream(
+                b[0].data_ptr(), b[1].data_ptr(), rb, stream)) for b in bufs]
+            mean_us, med_us = timer.kernel_us(launches, args.iters)
+            moved = read_bytes * 3 // 2
+            ent = dict(us=round(mean_us, 3), us_median=round(med_us, 3), bytes=moved,
+                       gbs=round(moved / (mean_us * 1e-6) / 1e9, 1),
+                       frac_hbm=round(moved / (mean_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+            refs[f"stream_2to1_as_{name}"] = ent
+            if name in kernels:
+                kernels[name]["frac_of_stream_reference"] = round(ent["us"] / kernels[name]["us"], 4)
+            log(f"reference 2:1 stream for {name}: {mean_us:.2f} us, {ent['frac_hbm']:.3f} of HBM")
+            del bufs, launches
+        kernels["references"] = refs
+
+    # ----------------------------------------- calibration window (one layer, 256 tokens)
+    if "calib" in only:
+        kernels["calibration_window"] = calib_window(torch, fq, synth, log)
+
     # ---------------------------------------------------------- CPU baseline
     cpu = None
     if not args.no_cpu_baseline and "step" in only:
@@ -593,8 +654,80 @@ def sources_sha(rels):
     return h.hexdigest()
 
 
+def calib_window(torch, fq, synth, log, repeats=5):
+    """One layer's calibration over the 256-token window of the seeded paged batches (4 KV
+    heads x 128, block 16, 2048 blocks), through the library's calibrator: per in-window
+    observe (absmax folded on the device + staging copies, no host wait) and for the
+    freezing observe (the one 8-byte read, the last-writer mask, the one-launch replay and
+    the stream-ordered release), the host time of the call and the GPU time of the work it
+    enqueued (events around the call on an otherwise idle stream).  Beside them, what the
+    per-observe synchronization of a design that reads the absmax back every batch costs
+    here: the same absmax kernel, then a blocking 8-byte read."""
+    import numpy as np
+
+    e = KV_H * KV_D
+    batches, _ = synth.kv_batches(num_tokens_total=synth.KV_WINDOW + 96, seed=5000)
+    dev = [(bf16_dev(torch, b.k), bf16_dev(torch, b.v), torch.from_numpy(b.slots).cuda())
+           for b in batches]
+    kc = torch.zeros(KV_NB * KV_BS * e, dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stage_host, stage_gpu, freeze_host, freeze_gpu, sync_host = [], [], [], [], []
+    for rep in range(repeats + 1):  # the first pass warms up allocations and code
+        cal = fq.KvCalibrator(synth.KV_WINDOW)
+        for (k, v, sl), b in zip(dev, batches):
+            step = cal.decide(len(b.slots), e)
+            if step == fq.FP8Q_CALIB_FROZEN:
+                break
+            torch.cuda.synchronize()
+            ev0.record()
+            t0 = time.perf_counter()
+            cal.observe(k, v, KV_H, KV_D, kc, vc, sl, KV_BS)
+            t1 = time.perf_counter()
+            ev1.record()
+            ks, vs = cal.scales()
+            fq.fp8_kv_write(k, v, kc, vc, sl, KV_H, KV_D, KV_BS, ks, vs)
+            torch.cuda.synchronize()
+            if rep == 0:
+                continue
+            host_us, gpu_us = (t1 - t0) * 1e6, ev0.elapsed_time(ev1) * 1e3
+            if step == fq.FP8Q_CALIB_STAGE:
+                stage_host.append(host_us)
+                stage_gpu.append(gpu_us)
+            elif step == fq.FP8Q_CALIB_FREEZE:
+                freeze_host.append(host_us)
+                freeze_gpu.append(gpu_us)
+        staged = cal.info()["replayed_tokens"]
+        cal.close()
+        if rep > 0:
+            amax2 = torch.zeros(2, dtype=torch.float32, device="cuda")
+            for k, v, sl in dev[:8]:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                fq.fp8_kv_amax(k, v, amax2)
+                amax2.cpu()  # blocking 8-byte read
+                sync_host.append((time.perf_counter() - t0) * 1e6)
+    res = dict(window_tokens=synth.KV_WINDOW, batches_in_window=len(stage_host) // repeats,
+               replayed_tokens=staged, repeats=repeats,
+               observe_in_window=dict(host_us=round(float(np.mean(stage_host)), 2),
+                                      gpu_us=round(float(np.mean(stage_gpu)), 2),
+                                      host_waits=0),
+               observe_freeze=dict(host_us=round(float(np.mean(freeze_host)), 2),
+                                   gpu_us=round(float(np.mean(freeze_gpu)), 2), host_waits=1),
+               per_observe_sync_removed=dict(host_us=round(float(np.mean(sync_host)), 2),
+                                             what="absmax kernel + blocking 8-byte read"))
+    log(f"calibration window: in-window observe host {res['observe_in_window']['host_us']} us, "
+        f"gpu {res['observe_in_window']['gpu_us']} us; freeze host "
+        f"{res['observe_freeze']['host_us']} us, gpu {res['observe_freeze']['gpu_us']} us; "
+        f"a per-observe sync would cost {res['per_observe_sync_removed']['host_us']} us")
+    return res
+
+
 def cpu_baseline(synth, log):
-    """The CPU oracle, as it stands, on full decode steps (single thread, ~10 s in all)."""
+    """The CPU oracle, as it stands, on full decode steps: single-threaded (about 10 s in
+    all), and with the group quant and the GEMM split by rows over the host threads (the
+    oracle's row-parallel wrappers; the KV write stays sequential, its order is part of its
+    definition)."""
     import numpy as np
 
     import oracle
@@ -610,22 +743,36 @@ def cpu_baseline(synth, log):
     slots = rng.permutation(KV_NB * KV_BS)[:M_DECODE].astype(np.int64)
     kc = np.zeros(KV_NB * KV_BS * e, dtype=np.uint8)
     vc = np.zeros_like(kc)
-    # whole steps until ~10 s of CPU work (at least one, at most ten)
-    steps, total = 0, 0.0
-    while steps < 1 or (total < 10.0 and steps < 10):
-        t0 = time.perf_counter()
-        q, s = oracle.group_quant(a)
-        for n in N_DECODE:
-            oracle.gemm(q, s, *ws[n])
+    threads = oracle.default_threads()
+
+    def step(parallel):
+        if parallel:
+            q, s = oracle.group_quant_rows(a, threads)
+            for n in N_DECODE:
+                oracle.gemm_rows(q, s, *ws[n], threads=threads)
+        else:
+            q, s = oracle.group_quant(a)
+            for n in N_DECODE:
+                oracle.gemm(q, s, *ws[n])
         oracle.amax(k)
         oracle.amax(v)
         oracle.kv_write(k, v, kc, vc, slots, M_DECODE, KV_H, KV_D, KV_BS, 0.1, 0.1, e, e,
                         KV_BS * e)
-        total += time.perf_counter() - t0
-        steps += 1
-    dt = total / steps
-    gbs = step_bytes() / dt / 1e9
-    log(f"cpu baseline: {steps} steps, {dt:.2f} s per step, {gbs:.4f} GB/s")
+
+    def timed(parallel, budget, max_steps):
+        steps, total = 0, 0.0
+        while steps < 1 or (total < budget and steps < max_steps):
+            t0 = time.perf_counter()
+            step(parallel)
+            total += time.perf_counter() - t0
+            steps += 1
+        return steps, total / steps
+
+    n1, dt1 = timed(False, 10.0, 10)
+    np_, dtp = timed(True, 5.0, 40)
+    gbs1, gbsp = step_bytes() / dt1 / 1e9, step_bytes() / dtp / 1e9
+    log(f"cpu baseline: 1 thread {n1} steps, {dt1:.2f} s per step, {gbs1:.4f} GB/s; "
+        f"{threads} threads {np_} steps, {dtp:.3f} s per step, {gbsp:.4f} GB/s")
     model = "unknown CPU"
     try:
         with open("/proc/cpuinfo") as f:
@@ -633,9 +780,12 @@ def cpu_baseline(synth, log):
                          model)
     except OSError:
         pass
-    return dict(value=round(gbs, 5), unit="GB/s", cores=1, kind="oracle",
-                sample=f"{steps} full decode steps (same shapes as the GPU step), "
-                       f"{dt:.2f} s each, single-threaded C oracle, FP64 GEMM",
+    return dict(value=round(gbsp, 5), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{np_} full decode steps (same shapes as the GPU step), {dtp:.3f} s "
+                       f"each, C oracle with group quant and FP64 GEMM split by rows over "
+                       f"{threads} threads, KV write sequential",
+                single_thread=dict(value=round(gbs1, 5), unit="GB/s", cores=1,
+                                   sample=f"{n1} full decode steps, {dt1:.2f} s each"),
                 cpu_model=model, host_cpus=os.cpu_count())
 
 

@@ -24,7 +24,10 @@ from ._lib import (  # noqa: F401
     fp8_quant_w8a8_gemm_grouped,
     load,
     strerror,
+    gemm_workspace,
     w8a8_block_gemm,
+    w8a8_block_gemm_workspace_size,
+    w8a8_block_gemm_ws,
     w8a8_block_gemm_prefill,
     w8a8_block_gemm_grouped,
     w8a16_block_gemv,

@@ -20,8 +20,10 @@ FP8Q_CALIB_STAGE, FP8Q_CALIB_DECLINE, FP8Q_CALIB_FREEZE, FP8Q_CALIB_FROZEN = 0, 
 
 # Every symbol include/fp8q.h declares.
 EXPORTS = (
-    "fp8q_strerror", "fp8q_version", "fp8q_time_next_launch", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
-    "w8a8_block_gemm", "w8a8_block_gemm_prefill", "w8a8_block_gemm_grouped",
+    "fp8q_strerror", "fp8q_version", "fp8q_time_next_launch", "fp8q_reference_empty",
+    "fp8q_reference_stream", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
+    "w8a8_block_gemm", "w8a8_block_gemm_workspace_size", "w8a8_block_gemm_ws",
+    "w8a8_block_gemm_prefill", "w8a8_block_gemm_grouped",
     "fp8_quant_w8a8_gemm_grouped", "w8a16_block_gemv", "w8a16_block_gemv_grouped",
     "fp8_kv_write", "fp8_kv_write_amax", "fp8_kv_read", "fp8_kv_amax",
     "fp8q_kv_calib_create", "fp8q_kv_calib_create_with_ops", "fp8q_kv_calib_observe",
@@ -100,10 +102,16 @@ def load() -> ctypes.CDLL:
         "fp8q_strerror": (ctypes.c_char_p, [ctypes.c_int]),
         "fp8q_version": (ctypes.c_int, []),
         "fp8q_time_next_launch": (ctypes.c_int, [P, P]),
+        "fp8q_reference_empty": (ctypes.c_int, [P]),
+        "fp8q_reference_stream": (ctypes.c_int, [P, P, I64, P]),
         "fp8_group_quant": (ctypes.c_int, [P, P, P, I64, I32, P]),
         "fp8_block_quant": (ctypes.c_int, [P, P, P, I32, I32, P]),
         "fp8_e4m3_encode": (ctypes.c_int, [P, P, I64, P]),
         "w8a8_block_gemm": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, P]),
+        "w8a8_block_gemm_workspace_size": (ctypes.c_int, [I32, I32, I32,
+                                                          ctypes.POINTER(ctypes.c_uint64)]),
+        "w8a8_block_gemm_ws": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, P,
+                                              ctypes.c_uint64, P]),
         "w8a8_block_gemm_grouped": (ctypes.c_int, [P, P, ctypes.POINTER(GemmProj), I32, I32,
                                                    I32, P]),
         "fp8_quant_w8a8_gemm_grouped": (ctypes.c_int, [P, P, P, ctypes.POINTER(GemmProj), I32,
@@ -247,6 +255,65 @@ def w8a8_block_gemm(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tensor,
                     ldc: int | None = None, stream: int | None = None) -> torch.Tensor:
     """E4M3 a_q [m <= 16, k] x E4M3 w_q [n, k]^T with block scales -> bf16 out [m, ldc]."""
     return _w8a8("w8a8_block_gemm", a_q, a_scale, w_q, w_scale, out, ldc, stream)
+
+
+def w8a8_block_gemm_workspace_size(m: int, n: int, k: int) -> int:
+    """Bytes of workspace w8a8_block_gemm_ws needs for this shape on the current device (0:
+    the shape runs unsplit)."""
+    b = ctypes.c_uint64()
+    check("w8a8_block_gemm_workspace_size",
+          load().w8a8_block_gemm_workspace_size(m, n, k, ctypes.byref(b)))
+    return b.value
+
+
+_WORKSPACES = {}  # (device index, stream) -> uint8 tensor whose counts are zero between calls
+
+
+def gemm_workspace(nbytes: int, device=None, stream: int | None = None) -> torch.Tensor:
+    """A zero-filled workspace of at least nbytes for calls on `stream`, kept and reused: a
+    call leaves its counts at zero, so the buffer needs no clearing between calls on one
+    stream (calls on other streams get their own)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    key = (dev.index, current_stream(dev) if stream is None else stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def w8a8_block_gemm_ws(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tensor,
+                       w_scale: torch.Tensor, out: torch.Tensor | None = None,
+                       ldc: int | None = None, workspace: torch.Tensor | None = None,
+                       stream: int | None = None) -> torch.Tensor:
+    """w8a8_block_gemm with K split across workgroups where the shape has too few 16-column
+    strips to fill the CUs.  workspace: a uint8 tensor of at least
+    w8a8_block_gemm_workspace_size(m, n, k) bytes whose counts are zero (torch.zeros); by
+    default one kept per stream by this module."""
+    m, k = a_q.shape
+    n = w_q.shape[0]
+    if w_q.shape[1] != k:
+        raise ValueError("a_q and w_q disagree on k")
+    if a_scale.numel() != m * (k // 128) or w_scale.numel() != (n // 128) * (k // 128):
+        raise ValueError("scale grids do not match the operand shapes")
+    if out is None:
+        ldc = n if ldc is None else ldc
+        out = torch.empty((m, ldc), dtype=torch.bfloat16, device=a_q.device)
+    else:
+        ldc = out.shape[-1] if ldc is None else ldc
+        if out.numel() < (m - 1) * ldc + n:
+            raise ValueError("out is smaller than (m - 1) * ldc + n elements")
+    st_ = current_stream(a_q.device) if stream is None else stream
+    need = w8a8_block_gemm_workspace_size(m, n, k)
+    if workspace is None and need:
+        workspace = gemm_workspace(need, a_q.device, st_)
+    wp, wb = (0, 0) if workspace is None else (_dev(workspace, "workspace", torch.uint8),
+                                               workspace.numel())
+    st = load().w8a8_block_gemm_ws(_dev(a_q, "a_q", _U8), _dev(a_scale, "a_scale", torch.float32),
+                                   _dev(w_q, "w_q", _U8), _dev(w_scale, "w_scale", torch.float32),
+                                   _dev(out, "out", _BF16), m, n, k, ldc, wp or None, wb, st_)
+    check("w8a8_block_gemm_ws", st)
+    return out
 
 
 def w8a8_block_gemm_prefill(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tensor,

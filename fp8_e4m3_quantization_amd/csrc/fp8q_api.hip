@@ -1,6 +1,32 @@
-// fp8q_api.hip -- status strings and version of the C ABI.
+// fp8q_api.hip -- status strings and version of the C ABI, the measurement hook, and two
+// reference kernels that measurements of the path are read against.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
 #include "fp8q.h"
 #include "fp8q_launch.h"
+
+namespace {
+
+// Nothing: what a launch costs on this device before it does any work.
+__global__ __launch_bounds__(256) void reference_empty_kernel() {}
+
+// A plain stream with the path's 2:1 read/write mix (bf16 in, one byte per element out, as
+// the group quantizer and the KV write move data): each lane reads 16 bytes and writes 8,
+// grid-stride over a grid of 4 blocks per CU (the fastest of the one-pass and persistent
+// shapes measured for it).  The written word depends on the read one, so no read is dead.
+constexpr int kRefBlock = 256;
+__global__ __launch_bounds__(kRefBlock) void reference_stream_kernel(const uint4* __restrict__ src,
+                                                                     uint2* __restrict__ dst,
+                                                                     int64_t n16) {
+  const int64_t stride = int64_t(gridDim.x) * kRefBlock;
+  for (int64_t i = int64_t(blockIdx.x) * kRefBlock + threadIdx.x; i < n16; i += stride) {
+    const uint4 v = src[i];
+    dst[i] = make_uint2(v.x ^ v.y, v.z ^ v.w);
+  }
+}
+
+}  // namespace
 
 extern "C" const char* fp8q_strerror(int status) {
   switch (status) {
@@ -15,10 +41,26 @@ extern "C" const char* fp8q_strerror(int status) {
   }
 }
 
-extern "C" int fp8q_version(void) { return 10000; }
+extern "C" int fp8q_version(void) { return 10100; }
 
 extern "C" int fp8q_time_next_launch(hipEvent_t start, hipEvent_t stop) {
   fp8q::g_next_launch_events.start = start;
   fp8q::g_next_launch_events.stop = stop;
   return FP8Q_OK;
+}
+
+extern "C" int fp8q_reference_empty(hipStream_t stream) {
+  fp8q::launch(reference_empty_kernel, dim3(1), dim3(kRefBlock), 0, stream);
+  return fp8q::launch_status();
+}
+
+extern "C" int fp8q_reference_stream(const void* src, void* dst, int64_t src_bytes,
+                                     hipStream_t stream) {
+  if (src_bytes < 0 || src_bytes % 16 != 0) return FP8Q_EINVAL;
+  if (src_bytes == 0) return FP8Q_OK;
+  if (!src || !dst) return FP8Q_ENULL;
+  if (!fp8q::aligned(src, 16) || !fp8q::aligned(dst, 8)) return FP8Q_EALIGN;
+  fp8q::launch(reference_stream_kernel, dim3(unsigned(4 * fp8q::num_cus())), dim3(kRefBlock), 0,
+               stream, static_cast<const uint4*>(src), static_cast<uint2*>(dst), src_bytes / 16);
+  return fp8q::launch_status();
 }

@@ -141,14 +141,9 @@ __global__ __launch_bounds__(64 * kWaves) void w8a8_gemm_kernel(
 // strips, below) and one pass writes bf16.  Several projections that read the same
 // activation can share one launch: strips are numbered across them, and each block walks
 // them from first_strip (adjacent strips on one XCD).
-// Weight loads go through a buffer descriptor per strip (make_strip_rsrc); the cache
-// policy bits of those loads:
-#ifndef FP8Q_GEMM_AUX
-#define FP8Q_GEMM_AUX 0
-#endif
-#ifndef FP8Q_GEMM_NT_OUT
-#define FP8Q_GEMM_NT_OUT 0  // 1: bf16 outputs written with the non-temporal hint
-#endif
+// Weight loads go through a buffer descriptor per strip (make_strip_rsrc), with the
+// default cache policy.
+constexpr int kGemmAux = 0;
 
 template <int kGpw>
 struct Slice {
@@ -173,18 +168,40 @@ struct ActSrc {
   float* s_out;
 };
 
-template <int kGpw, int kDepth, int kAux, int kRound, bool kQuant>
+// K split across workgroups (parts > 1; used when there are too few strips to give every
+// CU a full share).  The grid is `parts` equal sets of workgroups; set p multiplies groups
+// [G*p/parts, G*(p+1)/parts) of every strip it walks, its waves splitting that range, and
+// writes the strip's part sum (the 16x16 fp32 tile in accumulator order) to
+// partial[strip][p].  At the end of the kernel each workgroup counts its strips in; the one
+// that completes a strip's count sums the parts in the order p = 0, 1, ... (the same sum
+// whichever workgroup arrives last), writes bf16 and sets the count back to zero, so the
+// counts are zero again for the next launch.  No workgroup ever waits for another.
+struct SplitK {
+  float* partial;   // [total_strips][parts][256]
+  uint32_t* count;  // [total_strips]
+  int parts;
+};
+
+template <int kGpw, int kDepth, int kAux, int kRound, bool kQuant, bool kSplit>
 __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
-    ActSrc act, ProjSet ps, int m, int k, int total_strips) {
+    ActSrc act, ProjSet ps, int m, int k, int total_strips, SplitK sk) {
   static_assert(kRound % (kDepth + 1) == 0, "buffer index must be static within a round");
   static_assert(kRound * 256 == kPWaves * 64 * 2, "reduce: two outputs per lane");
+  static_assert(!(kQuant && kSplit), "the fused quantizer runs unsplit");
   __shared__ float s_part[2][kRound * kPWaves * 4 * 64];
   __shared__ uint4 s_tile[kPWaves * ActTile<kQuant ? 16 : 8>::kUints];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int groups = k >> 7;
-  const int g0 = (groups * wv) / kPWaves;
-  const int cnt = (groups * (wv + 1)) / kPWaves - g0;  // 0 <= cnt <= kGpw
+  // this workgroup's set (K part) and its place in the set
+  const int parts = kSplit ? sk.parts : 1;
+  const int set_size = int(gridDim.x) / parts;
+  const int kpart = kSplit ? int(blockIdx.x) / set_size : 0;
+  const int in_set = kSplit ? int(blockIdx.x) % set_size : int(blockIdx.x);
+  const int gb = (groups * kpart) / parts;
+  const int gp = (groups * (kpart + 1)) / parts - gb;  // groups of this K part
+  const int g0 = gb + (gp * wv) / kPWaves;
+  const int cnt = gb + (gp * (wv + 1)) / kPWaves - g0;  // 0 <= cnt <= kGpw
   const int row = lane & 15, koff = (lane >> 4) * 32;
   int goff[kGpw];  // first k of slice group u (a short slice re-reads its last group,
                    // whose activation fragment below is zero)
@@ -203,8 +220,8 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
     for (int u = 0; u < kGpw; ++u) sl.ws[u] = wsp[goff[u] >> 7];
   };
 
-  const int stride = int(gridDim.x);
-  const int first = first_strip(int(blockIdx.x), stride);
+  const int stride = set_size;
+  const int first = first_strip(in_set, stride);
   const int nit = (total_strips - first + stride - 1) / stride;
   if (nit <= 0) return;
 
@@ -347,22 +364,68 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
 #pragma unroll
         for (int w = 0; w < kPWaves; ++w) sum[x] += part[((j * kPWaves + w) * 4 + q0 + x) * 64 + lane];
       if (i + j < nit) {
-        int p, n0;
-        locate_strip(ps, first + (i + j) * stride, &p, &n0);
-        uint16_t* o = ps.out[p] + n0 + (lane & 15);
-        const int ldc = ps.ldc[p];
+        const int strip = first + (i + j) * stride;
+        if constexpr (kSplit) {
+          // device-scope stores: written at the point where every XCD sees them
+          float* dst = sk.partial + (int64_t(strip) * parts + kpart) * 256 + q0 * 64 + lane;
+          __hip_atomic_store(dst, sum[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(dst + 64, sum[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          int p, n0;
+          locate_strip(ps, strip, &p, &n0);
+          uint16_t* o = ps.out[p] + n0 + (lane & 15);
+          const int ldc = ps.ldc[p];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int r = 4 * (lane >> 4) + q0 + x;
-#if FP8Q_GEMM_NT_OUT
-          if (r < m) __builtin_nontemporal_store(f32_to_bf16_rne(sum[x]), o + int64_t(r) * ldc);
-#else
-          if (r < m) o[int64_t(r) * ldc] = f32_to_bf16_rne(sum[x]);
-#endif
+          for (int x = 0; x < 2; ++x) {
+            const int r = 4 * (lane >> 4) + q0 + x;
+            if (r < m) o[int64_t(r) * ldc] = f32_to_bf16_rne(sum[x]);
+          }
         }
       }
     }
     par ^= 1;
+  }
+
+  if constexpr (kSplit) {
+    // Count this workgroup's strips in, then finish every strip whose count it completed.
+    // The part tiles and the counts are touched only by device-scope atomic accesses, which
+    // are performed where every XCD sees them; each wave waits until its tile stores have
+    // completed (acknowledged at that scope) before the barrier after which the counts are
+    // raised, and a finishing workgroup reads the tiles only after its count returned.  A
+    // device-scope fence would instead write back and invalidate the whole L2 of the XCD,
+    // once per workgroup, which costs far more than the split saves.
+    __shared__ int s_last[64 * kPWaves];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int c0 = 0; c0 < nit; c0 += 64 * kPWaves) {
+      const int t = c0 + int(threadIdx.x);
+      if (t < nit) {
+        const int strip = first + t * stride;
+        const uint32_t before = __hip_atomic_fetch_add(sk.count + strip, 1u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+        s_last[threadIdx.x] = before == uint32_t(parts - 1) ? strip : -1;
+      }
+      __syncthreads();
+      const int nc = min(64 * kPWaves, nit - c0);
+      for (int i = 0; i < nc; ++i) {
+        const int strip = s_last[i];  // uniform
+        if (strip < 0) continue;
+        if (threadIdx.x < 256) {
+          const float* src = sk.partial + int64_t(strip) * parts * 256 + threadIdx.x;
+          float sum = 0.0f;
+          for (int q = 0; q < parts; ++q)
+            sum += __hip_atomic_load(src + q * 256, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int l = threadIdx.x & 63;
+          const int r = 4 * (l >> 4) + (threadIdx.x >> 6);
+          int p, n0;
+          locate_strip(ps, strip, &p, &n0);
+          if (r < m) ps.out[p][int64_t(r) * ps.ldc[p] + n0 + (l & 15)] = f32_to_bf16_rne(sum);
+        }
+        if (threadIdx.x == 0)
+          __hip_atomic_store(sk.count + strip, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+    }
   }
 }
 
@@ -375,36 +438,62 @@ int launch_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
   return launch_status();
 }
 
-template <int kGpw, bool kQuant>
+template <int kGpw, bool kQuant, bool kSplit>
 int launch_persistent(const ActSrc& act, const ProjSet& ps, int m, int k, int total,
-                      hipStream_t stream) {
-  const int grid = total < num_cus() ? total : num_cus();
-  constexpr int kDepth = 1;
+                      const SplitK& sk, int grid, hipStream_t stream) {
+  // a short slice per wave (split K) keeps more strips in flight to cover the latency
+  constexpr int kDepth = (kSplit && kGpw <= 2) ? 3 : 1;
   constexpr int kRound = 4;
-  launch((w8a8_persistent_kernel<kGpw, kDepth, FP8Q_GEMM_AUX, kRound, kQuant>), dim3(grid),
-         dim3(64 * kPWaves), 0, stream, act, ps, m, k, total);
+  launch((w8a8_persistent_kernel<kGpw, kDepth, kGemmAux, kRound, kQuant, kSplit>),
+         dim3(grid), dim3(64 * kPWaves), 0, stream, act, ps, m, k, total, sk);
   return launch_status();
 }
 
-// Persistent kernel for k <= 8 * 8 * 128 (each wave holds at most 8 groups).
-template <bool kQuant>
-int run_persistent(const ActSrc& act, const ProjSet& ps, int m, int k, hipStream_t stream) {
+// Persistent kernel for k <= 8 * 8 * 128 (each wave holds at most 8 groups).  kSplit:
+// sk.parts > 1 sets of workgroups split K (the grid is parts * set size).
+template <bool kQuant, bool kSplit = false>
+int run_persistent(const ActSrc& act, const ProjSet& ps, int m, int k, hipStream_t stream,
+                   const SplitK& sk = SplitK{nullptr, nullptr, 1}) {
   const int total = ps.strip_end[ps.count - 1];
-  const int gpw = (k / 128 + kPWaves - 1) / kPWaves;
+  const int parts = kSplit ? sk.parts : 1;
+  const int part_groups = (k / 128 + parts - 1) / parts;
+  const int gpw = (part_groups + kPWaves - 1) / kPWaves;
+  const int set = total < num_cus() / parts ? total : num_cus() / parts;
+  const int grid = set * parts;
   switch (gpw) {
-    case 1: return launch_persistent<1, kQuant>(act, ps, m, k, total, stream);
-    case 2: return launch_persistent<2, kQuant>(act, ps, m, k, total, stream);
-    case 3: return launch_persistent<3, kQuant>(act, ps, m, k, total, stream);
-    case 4: return launch_persistent<4, kQuant>(act, ps, m, k, total, stream);
-    case 5: return launch_persistent<5, kQuant>(act, ps, m, k, total, stream);
-    case 6: return launch_persistent<6, kQuant>(act, ps, m, k, total, stream);
-    case 7: return launch_persistent<7, kQuant>(act, ps, m, k, total, stream);
-    case 8: return launch_persistent<8, kQuant>(act, ps, m, k, total, stream);
+    case 1: return launch_persistent<1, kQuant, kSplit>(act, ps, m, k, total, sk, grid, stream);
+    case 2: return launch_persistent<2, kQuant, kSplit>(act, ps, m, k, total, sk, grid, stream);
+    case 3: return launch_persistent<3, kQuant, kSplit>(act, ps, m, k, total, sk, grid, stream);
+    case 4: return launch_persistent<4, kQuant, kSplit>(act, ps, m, k, total, sk, grid, stream);
+    case 5: return launch_persistent<5, kQuant, kSplit>(act, ps, m, k, total, sk, grid, stream);
+    case 6: return launch_persistent<6, kQuant, kSplit>(act, ps, m, k, total, sk, grid, stream);
+    case 7: return launch_persistent<7, kQuant, kSplit>(act, ps, m, k, total, sk, grid, stream);
+    case 8: return launch_persistent<8, kQuant, kSplit>(act, ps, m, k, total, sk, grid, stream);
     default: return FP8Q_EINVAL;
   }
 }
 
 constexpr int kPersistentMaxK = kPWaves * 8 * 128;
+
+// K parts for `strips` 16-column strips of `groups` K-groups on `cus` CUs.  A launch
+// costs a fixed part (about 7 us on MI355X at K = 5120, half of it the launch itself) plus
+// about 1 us per round of strips; splitting K into two parts halves the groups each wave
+// streams per strip and adds a partial-tile write, count and read.  Measured over N = 128 ..
+// 8192 and 2..8 parts (K = 5120, 16 rows): two parts win (by 0.3 to 1.9 us) exactly when
+// both parts' workgroups still run in one round, i.e. 2 * strips <= CUs, and more parts
+// never beat two by more than noise; once a split adds a round it loses.  A part also needs
+// a group per wave to stream (groups >= 16).
+constexpr int kMaxParts = 2;
+
+int split_parts(int strips, int groups, int cus) {
+  return (2 * strips <= cus && groups >= 2 * kPWaves) ? kMaxParts : 1;
+}
+
+// Workspace of a split launch: the counts first (256-byte aligned), then the tiles.
+uint64_t split_counts_bytes(int strips) { return (uint64_t(strips) * 4 + 255) & ~uint64_t(255); }
+uint64_t split_workspace_bytes(int strips, int parts) {
+  return parts <= 1 ? 0 : split_counts_bytes(strips) + uint64_t(strips) * parts * 256 * 4;
+}
 
 }  // namespace
 }  // namespace fp8q
@@ -447,6 +536,58 @@ extern "C" int w8a8_block_gemm(const uint8_t* a_q, const float* a_scale, const u
     return run_persistent<false>(act, ps, m, k, stream);
   }
   return launch_gemm<4, 5>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, stream);
+}
+
+namespace {
+// The K split w8a8_block_gemm_ws uses for this shape on the current device (1: none).
+int ws_parts(int32_t n, int32_t k) {
+  if (k > kPersistentMaxK) return 1;
+  return split_parts(n / 16, k / 128, num_cus());
+}
+
+// One projection with K split in `parts` over the workspace (counts, then tiles).
+int run_split(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
+              const float* w_scale, uint16_t* out, int32_t m, int32_t n, int32_t k,
+              int32_t ldc, void* workspace, int parts, hipStream_t stream) {
+  ProjSet ps = {};
+  ps.w[0] = w_q;
+  ps.ws[0] = w_scale;
+  ps.out[0] = out;
+  ps.ldc[0] = ldc;
+  ps.strip_end[0] = n / 16;
+  ps.count = 1;
+  const ActSrc act = {a_q, a_scale, nullptr, nullptr, nullptr};
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  const SplitK sk = {reinterpret_cast<float*>(base + split_counts_bytes(n / 16)),
+                     reinterpret_cast<uint32_t*>(base), parts};
+  return run_persistent<false, true>(act, ps, m, k, stream, sk);
+}
+}  // namespace
+
+extern "C" int w8a8_block_gemm_workspace_size(int32_t m, int32_t n, int32_t k,
+                                              uint64_t* bytes) {
+  if (!bytes) return FP8Q_ENULL;
+  *bytes = 0;
+  if (m < 1 || m > 16 || k <= 0 || k % 128 != 0 || k > kMaxGemmK || n <= 0 || n % 128 != 0)
+    return FP8Q_EINVAL;
+  *bytes = split_workspace_bytes(n / 16, ws_parts(n, k));
+  return FP8Q_OK;
+}
+
+extern "C" int w8a8_block_gemm_ws(const uint8_t* a_q, const float* a_scale,
+                                  const uint8_t* w_q, const float* w_scale, uint16_t* out,
+                                  int32_t m, int32_t n, int32_t k, int32_t ldc,
+                                  void* workspace, uint64_t workspace_bytes,
+                                  hipStream_t stream) {
+  int rc = check_gemm_common(a_q, a_scale, m, k);
+  if (rc == FP8Q_OK) rc = check_proj(w_q, w_scale, out, n, ldc);
+  if (rc != FP8Q_OK) return rc;
+  const int parts = ws_parts(n, k);
+  if (parts <= 1) return w8a8_block_gemm(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, stream);
+  if (!workspace) return FP8Q_ENULL;
+  if (workspace_bytes < split_workspace_bytes(n / 16, parts)) return FP8Q_EINVAL;
+  if (!aligned(workspace, 256)) return FP8Q_EALIGN;
+  return run_split(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, workspace, parts, stream);
 }
 
 extern "C" int w8a8_block_gemm_grouped(const uint8_t* a_q, const float* a_scale,

@@ -28,10 +28,10 @@ namespace fp8q {
 namespace {
 
 constexpr int kKvBlock = 256;
-#ifndef FP8Q_KV_WIDE_BLOCK
-#define FP8Q_KV_WIDE_BLOCK 512
-#endif
-constexpr int kWideBlock = FP8Q_KV_WIDE_BLOCK;  // threads per block of the wide write
+// Threads per block of the wide write: one pass over the tokens in 512-thread blocks.
+// Measured against 256 and 1024 threads and against persistent grids of 2 to 8 blocks per
+// CU with one to four tokens' loads in flight per wave: none was faster.
+constexpr int kWideBlock = 512;
 
 __device__ __forceinline__ bool slot_to_block(int64_t slot, int64_t nslots, int bs,
                                               int64_t* blk, int64_t* off) {
@@ -61,19 +61,7 @@ __device__ __forceinline__ int64_t uniform(int64_t v) {
 // A wave takes kTokPerWave consecutive tokens: their slots are read first (scalar loads),
 // then every 16-byte load of the group is issued before any conversion, so each wave
 // keeps 2 * kTokPerWave loads in flight instead of waiting on one token at a time.
-#ifndef FP8Q_KV_TOKENS_PER_WAVE
-#define FP8Q_KV_TOKENS_PER_WAVE 4
-#endif
-#ifndef FP8Q_KV_BLOCKS_PER_CU
-#define FP8Q_KV_BLOCKS_PER_CU 0  // 0: one pass per wave; else a persistent grid
-#endif
-#ifndef FP8Q_KV_NT_LOAD
-#define FP8Q_KV_NT_LOAD 0
-#endif
-#ifndef FP8Q_KV_NT_STORE
-#define FP8Q_KV_NT_STORE 1
-#endif
-constexpr int kTokPerWave = FP8Q_KV_TOKENS_PER_WAVE;
+constexpr int kTokPerWave = 4;
 
 __global__ __launch_bounds__(kKvBlock) void kv_write_vec_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v, uint2* __restrict__ kc,
@@ -103,17 +91,12 @@ __global__ __launch_bounds__(kKvBlock) void kv_write_vec_kernel(
 #pragma unroll
       for (int i = 0; i < kTokPerWave; ++i) {
         if (ok[i]) {
-#if FP8Q_KV_NT_STORE
           const uint2 kq = quant8<false>(kx[i], k_scale, k_inv);
           const uint2 vq = quant8<false>(vx[i], v_scale, v_inv);
           __builtin_nontemporal_store(uint64_t(kq.x) | (uint64_t(kq.y) << 32),
                                       reinterpret_cast<uint64_t*>(kc + dst[i] + c));
           __builtin_nontemporal_store(uint64_t(vq.x) | (uint64_t(vq.y) << 32),
                                       reinterpret_cast<uint64_t*>(vc + dst[i] + c));
-#else
-          kc[dst[i] + c] = quant8<false>(kx[i], k_scale, k_inv);
-          vc[dst[i] + c] = quant8<false>(vx[i], v_scale, v_inv);
-#endif
         }
       }
     }
@@ -124,19 +107,13 @@ __global__ __launch_bounds__(kKvBlock) void kv_write_vec_kernel(
 // a token takes 2 * lpt lanes -- the first lpt convert 16 elements of its K row each (two
 // 16-byte loads, one 16-byte store), the next lpt the same 16 elements of its V row -- so a
 // wave covers 64 / (2 * lpt) tokens per step and every store instruction writes whole
-// 16-byte lanes.  kSteps such steps are loaded before any is converted.
-#ifndef FP8Q_KV_WIDE_STEPS
-#define FP8Q_KV_WIDE_STEPS 1
-#endif
-constexpr int kWideSteps = FP8Q_KV_WIDE_STEPS;
+// 16-byte lanes.
 
+// Codes of a lane's 16 elements: one 16-byte store with the non-temporal hint (the pool is
+// not read again by this kernel), so each store instruction writes whole lines.
 __device__ __forceinline__ void store16_nt(uint4 v, uint8_t* p) {
-#if FP8Q_KV_NT_STORE
-  __builtin_nontemporal_store(uint64_t(v.x) | (uint64_t(v.y) << 32), reinterpret_cast<uint64_t*>(p));
-  __builtin_nontemporal_store(uint64_t(v.z) | (uint64_t(v.w) << 32), reinterpret_cast<uint64_t*>(p + 8));
-#else
-  *reinterpret_cast<uint4*>(p) = v;
-#endif
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p));
 }
 
 // The value of amax2[which] as the kernel starts, read by the thread that later folds into
@@ -191,35 +168,19 @@ __global__ __launch_bounds__(kWideBlock) void kv_write_wide_kernel(
   const float sc = half ? v_scale : k_scale, inv = half ? v_inv : k_inv;
   const int64_t wave = (int64_t(blockIdx.x) * kWideBlock + threadIdx.x) >> 6;
   const int64_t nwaves = (int64_t(gridDim.x) * kWideBlock) >> 6;
-  const int64_t per_iter = int64_t(tpw) * kWideSteps;
   float mx = 0.0f;  // kAmax: this lane's running max |x|
   const float seen = (kAmax && threadIdx.x < 2) ? seen_max(amax2, int(threadIdx.x)) : 0.0f;
-  for (int64_t t0 = wave * per_iter; t0 < num_tokens; t0 += nwaves * per_iter) {
-    uint4 x0[kWideSteps], x1[kWideSteps];
-    int64_t tok[kWideSteps];
-#pragma unroll
-    for (int st = 0; st < kWideSteps; ++st) {
-      tok[st] = t0 + st * tpw + slot_in_wave;
-      const int64_t tl = tok[st] < num_tokens ? tok[st] : num_tokens - 1;  // in bounds
-      const uint4* p = reinterpret_cast<const uint4*>(src + tl * sstride + chunk * 16);
-#if FP8Q_KV_NT_LOAD
-      x0[st] = load16_nt(p);
-      x1[st] = load16_nt(p + 1);
-#else
-      x0[st] = p[0];
-      x1[st] = p[1];
-#endif
-    }
-#pragma unroll
-    for (int st = 0; st < kWideSteps; ++st) {
-      int64_t blk = 0, off = 0;
-      const int64_t tl = tok[st] < num_tokens ? tok[st] : num_tokens - 1;
-      const bool ok = tok[st] < num_tokens && slot_to_block(slots[tl], nslots, bs, &blk, &off);
-      const uint2 a = quant8<false>(x0[st], sc, inv);
-      const uint2 b = quant8<false>(x1[st], sc, inv);
-      if (ok) store16_nt(make_uint4(a.x, a.y, b.x, b.y), dpool + blk * cs + off * e + chunk * 16);
-      if (kAmax && tok[st] < num_tokens) mx = fmaxf(mx, fmaxf(absmax8(x0[st]), absmax8(x1[st])));
-    }
+  for (int64_t t0 = wave * tpw; t0 < num_tokens; t0 += nwaves * tpw) {
+    const int64_t tok = t0 + slot_in_wave;
+    const int64_t tl = tok < num_tokens ? tok : num_tokens - 1;  // in bounds
+    const uint4* p = reinterpret_cast<const uint4*>(src + tl * sstride + chunk * 16);
+    const uint4 x0 = p[0], x1 = p[1];
+    int64_t blk = 0, off = 0;
+    const bool ok = tok < num_tokens && slot_to_block(slots[tl], nslots, bs, &blk, &off);
+    const uint2 a = quant8<false>(x0, sc, inv);
+    const uint2 b = quant8<false>(x1, sc, inv);
+    if (ok) store16_nt(make_uint4(a.x, a.y, b.x, b.y), dpool + blk * cs + off * e + chunk * 16);
+    if (kAmax && tok < num_tokens) mx = fmaxf(mx, fmaxf(absmax8(x0), absmax8(x1)));
   }
   if constexpr (kAmax) fold_block_max2<kWideBlock>(half ? 0.0f : mx, half ? mx : 0.0f, amax2, seen);
 }
@@ -256,25 +217,15 @@ __global__ __launch_bounds__(kKvBlock) void kv_write_scalar_kernel(
 // (no instruction leaves holes in a cache line).  A lane takes kReadUnroll items a pass,
 // all loads issued before any conversion.  Tokens whose slot is out of range read pool
 // row 0 (in bounds) and store nothing.
-#ifndef FP8Q_KV_READ_UNROLL
-#define FP8Q_KV_READ_UNROLL 4
-#endif
-#ifndef FP8Q_KV_READ_NT_STORE
-#define FP8Q_KV_READ_NT_STORE 1  // bf16 rows written with the non-temporal hint
-#endif
-constexpr int kReadUnroll = FP8Q_KV_READ_UNROLL;
-#ifndef FP8Q_KV_READ_BLOCK
-#define FP8Q_KV_READ_BLOCK 256
-#endif
-constexpr int kReadBlock = FP8Q_KV_READ_BLOCK;  // threads per block of the vector read
+// A lane takes four items a pass (all loads issued before any conversion), in 256-thread
+// blocks, and writes its bf16 rows with the non-temporal hint; measured against 128/512
+// threads and other unrolls.
+constexpr int kReadUnroll = 4;
+constexpr int kReadBlock = 256;  // threads per block of the vector read
 
 __device__ __forceinline__ void store16_bf16(uint4 a, uint16_t* p) {
-#if FP8Q_KV_READ_NT_STORE
   typedef unsigned v4u __attribute__((ext_vector_type(4)));
   __builtin_nontemporal_store(v4u{a.x, a.y, a.z, a.w}, reinterpret_cast<v4u*>(p));
-#else
-  *reinterpret_cast<uint4*>(p) = a;
-#endif
 }
 
 __device__ __forceinline__ uint4 dequant8(uint2 w, float s) {
@@ -402,13 +353,8 @@ __device__ __forceinline__ void fold_block_max(float m, float* amax2, int which,
 
 // max |x| over a packed run of n8 16-byte words; blockIdx.y picks K (0) or V (1).  Four
 // independent 16-byte loads per thread per step keep enough bytes in flight.
-#ifndef FP8Q_AMAX_BLOCK
-#define FP8Q_AMAX_BLOCK 1024
-#endif
-#ifndef FP8Q_AMAX_MAX_BLOCKS
-#define FP8Q_AMAX_MAX_BLOCKS 4096  // per tensor
-#endif
-constexpr int kAmaxBlock = FP8Q_AMAX_BLOCK;
+constexpr int kAmaxBlock = 1024;
+constexpr int64_t kAmaxMaxBlocks = 4096;  // per tensor
 __global__ __launch_bounds__(kAmaxBlock) void amax_flat_kernel(const uint4* __restrict__ k,
                                                              const uint4* __restrict__ v,
                                                              int64_t n8,
@@ -453,7 +399,7 @@ int kv_amax_rows(const uint16_t* k, const uint16_t* v, int64_t rows, int64_t row
       aligned(v, 16)) {
     // four 16-byte words per thread per step; enough blocks to fill every CU
     int64_t blocks = (n / 8 + 4 * kAmaxBlock - 1) / (4 * kAmaxBlock);
-    if (blocks > FP8Q_AMAX_MAX_BLOCKS) blocks = FP8Q_AMAX_MAX_BLOCKS;
+    if (blocks > kAmaxMaxBlocks) blocks = kAmaxMaxBlocks;
     launch(amax_flat_kernel, dim3(unsigned(blocks), 2), dim3(kAmaxBlock), 0, stream,
                        reinterpret_cast<const uint4*>(k), reinterpret_cast<const uint4*>(v),
                        n / 8, amax2);
@@ -483,7 +429,7 @@ int kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t* v_
   if (wide) {
     const int lpt = int(e / 16);
     const int lpt_log2 = __builtin_ctz(unsigned(lpt));
-    const int64_t per_block = int64_t(kWideBlock / 64) * (64 / (2 * lpt)) * kWideSteps;
+    const int64_t per_block = int64_t(kWideBlock / 64) * (64 / (2 * lpt));
     const int64_t blocks = clamp_grid((int64_t(num_tokens) + per_block - 1) / per_block);
     if (amax2)
       launch(kv_write_wide_kernel<true>, dim3(unsigned(blocks)), dim3(kWideBlock), 0, stream,
@@ -505,9 +451,7 @@ int kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t* v_
                    cache_stride % 8 == 0 && aligned(k, 16) && aligned(v, 16) &&
                    aligned(k_cache, 8) && aligned(v_cache, 8);
   const int64_t rows_per_block = vec ? kRowsPerBlock * kTokPerWave : kRowsPerBlock;
-  int64_t blocks = clamp_grid((int64_t(num_tokens) + rows_per_block - 1) / rows_per_block);
-  if (FP8Q_KV_BLOCKS_PER_CU > 0 && blocks > int64_t(FP8Q_KV_BLOCKS_PER_CU) * num_cus())
-    blocks = int64_t(FP8Q_KV_BLOCKS_PER_CU) * num_cus();
+  const int64_t blocks = clamp_grid((int64_t(num_tokens) + rows_per_block - 1) / rows_per_block);
   if (vec)
     launch(kv_write_vec_kernel, dim3(unsigned(blocks)), dim3(64, kRowsPerBlock), 0,
                        stream, reinterpret_cast<const uint4*>(k),

@@ -54,6 +54,16 @@ int fp8q_version(void);
  * nothing (zero sizes, errors) and the calibrator.  Always returns FP8Q_OK. */
 int fp8q_time_next_launch(hipEvent_t start, hipEvent_t stop);
 
+/* Measurement references (not steps of the path): kernels that the path's timings are read
+ * against, launched through the same hook.  fp8q_reference_empty enqueues one empty
+ * 256-thread block (what a launch costs before any work).  fp8q_reference_stream reads
+ * src_bytes (a multiple of 16) from src and writes src_bytes / 2 to dst -- the 2:1
+ * read/write mix of the group quantizer and the KV write, with no arithmetic -- over a grid
+ * of 4 blocks per CU.  src 16-byte and dst 8-byte aligned device memory.
+ * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EALIGN, FP8Q_ELAUNCH. */
+int fp8q_reference_empty(hipStream_t stream);
+int fp8q_reference_stream(const void* src, void* dst, int64_t src_bytes, hipStream_t stream);
+
 /* ------------------------------------------------ per-token 1x128 group quant
  * [actq] module doc: one FP32 scale per 128-wide K-group of one token row;
  * [decode] decode_w8a8_quant_act: the activation is quantized once and shared by every
@@ -116,6 +126,34 @@ int fp8_e4m3_encode(const float* x, uint8_t* q, int64_t n, hipStream_t stream);
 int w8a8_block_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
                     const float* w_scale, uint16_t* out, int32_t m, int32_t n, int32_t k,
                     int32_t ldc, hipStream_t stream);
+
+/* ------------------------------------ block-scaled W8A8 decode GEMM, K split
+ * [decode] module doc, WHY table: a decode projection is a stream over its weight, and the
+ * pages' own library splits K (a split-K pass plus a reduce) when an output alone cannot
+ * keep the machine busy.  Computes exactly what w8a8_block_gemm specifies (same operands,
+ * layouts, rows written and errors), but when the shape has too few 16-column output
+ * strips to give every CU a full share, K is split over `parts` sets of workgroups: each
+ * writes its part's FP32 16x16 tile sums to the workspace, and the workgroup that completes
+ * a strip adds the parts in a fixed order (p = 0, 1, ...), so the result is deterministic
+ * (it may differ from w8a8_block_gemm's in the last bits: another FP32 summation order).
+ * Shapes that do not benefit run w8a8_block_gemm's kernel and touch no workspace.
+ *
+ * w8a8_block_gemm_workspace_size: *bytes = the workspace this shape needs on the current
+ *   device (0: no split).  Errors: FP8Q_ENULL, FP8Q_EINVAL (shape as w8a8_block_gemm).
+ * w8a8_block_gemm_ws:
+ *   workspace        device memory of workspace_bytes >= the size above, 256-byte aligned,
+ *                    owned by the caller; its counts (the first ceil(n/16 * 4 / 256) * 256
+ *                    bytes) must be zero before the first call that uses it (e.g. zero-filled
+ *                    at allocation); every call leaves them zero again, so later calls need
+ *                    no clearing.  Calls sharing a workspace must not overlap in time (calls
+ *                    on one stream never do).  NULL / 0 is fine when the size is 0.
+ * Errors: as w8a8_block_gemm, and FP8Q_ENULL (no workspace where one is needed),
+ * FP8Q_EINVAL (workspace_bytes too small), FP8Q_EALIGN (workspace not 256-byte aligned). */
+int w8a8_block_gemm_workspace_size(int32_t m, int32_t n, int32_t k, uint64_t* bytes);
+int w8a8_block_gemm_ws(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
+                       const float* w_scale, uint16_t* out, int32_t m, int32_t n, int32_t k,
+                       int32_t ldc, void* workspace, uint64_t workspace_bytes,
+                       hipStream_t stream);
 
 /* ------------------------------------------------ W8A8 GEMM at prefill widths
  * [resid] DenseFp8Inputs::w8a8_kernels (the W8A8 prefill arm: per-token group quant, then

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = fq.load()
-    assert lib.fp8q_version() == 10000
+    assert lib.fp8q_version() == 10100
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert fq.strerror(code) and fq.strerror(code) != "unknown status"
     assert fq.strerror(-99) == "unknown status"
@@ -63,6 +63,27 @@ def test_gemm_argument_checks():
     assert lib.w8a8_block_gemm(FAKE, FAKE, None, FAKE, FAKE, 4, 128, 128, 128, None) == ENULL
     assert lib.w8a8_block_gemm(FAKE + 4, FAKE, FAKE, FAKE, FAKE, 4, 128, 128, 128, None) == EALIGN
     assert lib.w8a8_block_gemm(FAKE, FAKE, FAKE, FAKE, FAKE + 1, 4, 128, 128, 128, None) == EALIGN
+
+
+def test_workspace_gemm_and_reference_argument_checks():
+    lib = fq.load()
+    b = ctypes.c_uint64(7)
+    assert lib.w8a8_block_gemm_workspace_size(16, 1024, 5120, None) == ENULL
+    for m, n, k in [(0, 1024, 5120), (17, 1024, 5120), (16, 1000, 5120), (16, 1024, 5000),
+                    (16, 1024, 131072 + 128)]:
+        assert lib.w8a8_block_gemm_workspace_size(m, n, k, ctypes.byref(b)) == EINVAL
+        assert b.value == 0
+    assert lib.w8a8_block_gemm_workspace_size(16, 16384, 5120, ctypes.byref(b)) == 0
+    assert b.value == 0  # enough strips: no split, no workspace
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert lib.w8a8_block_gemm_ws(*ok, 17, 1024, 5120, 1024, FAKE, 1 << 30, None) == EINVAL
+    assert lib.w8a8_block_gemm_ws(*ok, 16, 1024, 5120, 1000, FAKE, 1 << 30, None) == EINVAL
+    assert lib.w8a8_block_gemm_ws(FAKE, None, FAKE, FAKE, FAKE, 16, 1024, 5120, 1024, FAKE,
+                                  1 << 30, None) == ENULL
+    assert lib.fp8q_reference_stream(FAKE, FAKE, 24, None) == EINVAL
+    assert lib.fp8q_reference_stream(None, FAKE, 32, None) == ENULL
+    assert lib.fp8q_reference_stream(FAKE + 8, FAKE, 32, None) == EALIGN
+    assert lib.fp8q_reference_stream(None, None, 0, None) == 0
 
 
 def test_kv_write_argument_checks():

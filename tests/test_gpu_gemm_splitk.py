@@ -1,0 +1,107 @@
+"""GPU parity: the K-split decode GEMM (w8a8_block_gemm_ws) against the FP64 oracle.
+
+Same bar as w8a8_block_gemm: |gpu - ref| <= 1e-2 |ref| + 1e-3 rms(ref) per bf16 output.
+Beyond it: the split is deterministic (repeated calls give the same bits), the workspace's
+counts are back at zero after every call, only the documented output extent is written,
+and against the unsplit kernel the difference stays within FP32 reordering."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import fp8_e4m3_quantization_amd as fq
+from fp8_e4m3_quantization_amd import synth
+from tests.gpu_util import (DEV, bf16_host_to_f64, f32_dev, gemm_tolerance_ok, host,
+                            need_gpu, u8_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(_):
+    need_gpu()
+
+
+def _operands(m, n, k, seed):
+    a = synth.decode_activation(m, k=k, seed=seed)
+    q, s = oracle.group_quant(a)
+    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=seed + 1))
+    return q, s, wq, ws
+
+
+def _counts_bytes(n):
+    return -(-(n // 16) * 4 // 256) * 256
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 1024, 5120), (5, 1024, 5120), (1, 128, 5120),
+                                   (16, 256, 4096), (12, 128, 8192), (3, 384, 5120),
+                                   (7, 512, 8192)])
+def test_split_matches_oracle_deterministic_and_leaves_counts_zero(m, n, k):
+    q, s, wq, ws = _operands(m, n, k, 7000 + n + k + m)
+    need = fq.w8a8_block_gemm_workspace_size(m, n, k)
+    assert need > 0, "shape expected to take the split path"
+    work = torch.zeros(need + 512, dtype=torch.uint8, device=DEV)
+    args = (u8_dev(q), f32_dev(s), u8_dev(wq), f32_dev(ws))
+    out1 = host(fq.w8a8_block_gemm_ws(*args, workspace=work))
+    assert not host(work[:_counts_bytes(n)]).any(), "counts not back at zero"
+    out2 = host(fq.w8a8_block_gemm_ws(*args, workspace=work))
+    assert np.array_equal(out1, out2)
+    ref = oracle.gemm(q, s, wq, ws)
+    ok, worst = gemm_tolerance_ok(out1, ref)
+    assert ok, f"worst error / bound = {worst:.3f}"
+    plain = host(fq.w8a8_block_gemm(*args))
+    assert np.max(np.abs(bf16_host_to_f64(plain) - bf16_host_to_f64(out1))) <= \
+        2.0 ** -7 * np.max(np.abs(ref))
+
+
+def test_decode_projection_n1024_with_the_bindings_own_workspace():
+    """The configuration's N = 1024 projection (M = 16, K = 5120) through the workspace the
+    binding keeps per stream, over several calls with other shapes in between."""
+    q, s, wq, ws = _operands(16, 1024, 5120, 2000)
+    args = (u8_dev(q), f32_dev(s), u8_dev(wq), f32_dev(ws))
+    ref = oracle.gemm(q, s, wq, ws)
+    first = host(fq.w8a8_block_gemm_ws(*args))
+    q2, s2, wq2, ws2 = _operands(4, 128, 2048, 11)
+    other = host(fq.w8a8_block_gemm_ws(u8_dev(q2), f32_dev(s2), u8_dev(wq2), f32_dev(ws2)))
+    assert gemm_tolerance_ok(other, oracle.gemm(q2, s2, wq2, ws2))[0]
+    again = host(fq.w8a8_block_gemm_ws(*args))
+    assert np.array_equal(first, again)
+    assert gemm_tolerance_ok(first, ref)[0]
+
+
+def test_unsplit_shapes_equal_w8a8_block_gemm_bit_for_bit():
+    """A shape with enough strips runs the unsplit kernel and needs no workspace."""
+    q, s, wq, ws = _operands(16, 16384, 5120, 2116)
+    assert fq.w8a8_block_gemm_workspace_size(16, 16384, 5120) == 0
+    args = (u8_dev(q), f32_dev(s), u8_dev(wq), f32_dev(ws))
+    assert np.array_equal(host(fq.w8a8_block_gemm_ws(*args)), host(fq.w8a8_block_gemm(*args)))
+
+
+def test_split_writes_exactly_its_strided_extent_and_nan_rows_stay_out():
+    """Strided output (ldc > n): nothing outside the (m - 1) * ldc + n extent changes; NaN
+    bytes in activation rows >= m (device memory beyond the rows passed) never leak in."""
+    m, n, k, ldc = 6, 1024, 5120, 1100
+    q, s, wq, ws = _operands(m, n, k, 41)
+    qd = torch.full((16, k), 0x7F, dtype=torch.uint8, device=DEV)
+    qd[:m] = u8_dev(q)
+    buf = torch.full((m * ldc + 32,), 5.0, dtype=torch.bfloat16, device=DEV)
+    fq.w8a8_block_gemm_ws(qd[:m], f32_dev(s), u8_dev(wq), f32_dev(ws), out=buf, ldc=ldc)
+    got = host(buf)
+    mask = np.zeros(got.size, dtype=bool)
+    for r in range(m):
+        mask[r * ldc:r * ldc + n] = True
+    assert np.all(bf16_host_to_f64(got[~mask]) == 5.0)
+    vals = np.stack([got[r * ldc:r * ldc + n] for r in range(m)])
+    ok, worst = gemm_tolerance_ok(vals, oracle.gemm(q, s, wq, ws))
+    assert ok, worst
+
+
+def test_workspace_errors_before_launch():
+    import ctypes
+    lib = fq.load()
+    m, n, k = 16, 1024, 5120
+    need = fq.w8a8_block_gemm_workspace_size(m, n, k)
+    p = ctypes.c_void_p(1 << 20)
+    assert lib.w8a8_block_gemm_ws(p, p, p, p, p, m, n, k, n, None, need, None) == -2
+    assert lib.w8a8_block_gemm_ws(p, p, p, p, p, m, n, k, n, p, need - 1, None) == -1
+    assert lib.w8a8_block_gemm_ws(p, p, p, p, p, m, n, k, n, ctypes.c_void_p((1 << 20) + 16),
+                                  need, None) == -3
