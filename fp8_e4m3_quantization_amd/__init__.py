@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     strerror,
     gemm_workspace,
     w8a8_block_gemm,
+    w8a8_block_gemm_noalloc,
     w8a8_block_gemm_workspace_size,
     w8a8_block_gemm_ws,
     w8a8_block_gemm_prefill,

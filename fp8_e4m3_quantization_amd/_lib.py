@@ -23,6 +23,7 @@ EXPORTS = (
     "fp8q_strerror", "fp8q_version", "fp8q_time_next_launch", "fp8q_reference_empty",
     "fp8q_reference_stream", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
     "w8a8_block_gemm", "w8a8_block_gemm_workspace_size", "w8a8_block_gemm_ws",
+    "w8a8_block_gemm_noalloc",
     "w8a8_block_gemm_prefill", "w8a8_block_gemm_grouped",
     "fp8_quant_w8a8_gemm_grouped", "w8a16_block_gemv", "w8a16_block_gemv_grouped",
     "fp8_kv_write", "fp8_kv_write_amax", "fp8_kv_read", "fp8_kv_amax",
@@ -112,6 +113,7 @@ def load() -> ctypes.CDLL:
                                                           ctypes.POINTER(ctypes.c_uint64)]),
         "w8a8_block_gemm_ws": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, P,
                                               ctypes.c_uint64, P]),
+        "w8a8_block_gemm_noalloc": (ctypes.c_int, [P, P, P, P, P, I32, I32, I32, I32, P]),
         "w8a8_block_gemm_grouped": (ctypes.c_int, [P, P, ctypes.POINTER(GemmProj), I32, I32,
                                                    I32, P]),
         "fp8_quant_w8a8_gemm_grouped": (ctypes.c_int, [P, P, P, ctypes.POINTER(GemmProj), I32,
@@ -314,6 +316,16 @@ def w8a8_block_gemm_ws(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tens
                                    _dev(out, "out", _BF16), m, n, k, ldc, wp or None, wb, st_)
     check("w8a8_block_gemm_ws", st)
     return out
+
+
+def w8a8_block_gemm_noalloc(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tensor,
+                            w_scale: torch.Tensor, out: torch.Tensor,
+                            ldc: int | None = None, stream: int | None = None) -> torch.Tensor:
+    """w8a8_block_gemm_ws with its split scratch in the library's static device array: the
+    call allocates nothing (out must be given).  Calls overlapping on one GPU race."""
+    if out is None:
+        raise ValueError("w8a8_block_gemm_noalloc writes into a given out tensor")
+    return _w8a8("w8a8_block_gemm_noalloc", a_q, a_scale, w_q, w_scale, out, ldc, stream)
 
 
 def w8a8_block_gemm_prefill(a_q: torch.Tensor, a_scale: torch.Tensor, w_q: torch.Tensor,

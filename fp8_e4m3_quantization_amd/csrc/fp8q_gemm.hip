@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fp8q.h"
 #include "fp8q_device.h"
 #include "fp8q_gemm_common.h"
@@ -545,10 +547,11 @@ int ws_parts(int32_t n, int32_t k) {
   return split_parts(n / 16, k / 128, num_cus());
 }
 
-// One projection with K split in `parts` over the workspace (counts, then tiles).
+// One projection with K split in `parts`: counts [n/16] (zero on entry, zero again on
+// exit) and part tiles [n/16][parts][256] fp32.
 int run_split(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
               const float* w_scale, uint16_t* out, int32_t m, int32_t n, int32_t k,
-              int32_t ldc, void* workspace, int parts, hipStream_t stream) {
+              int32_t ldc, uint32_t* counts, float* tiles, int parts, hipStream_t stream) {
   ProjSet ps = {};
   ps.w[0] = w_q;
   ps.ws[0] = w_scale;
@@ -557,10 +560,53 @@ int run_split(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
   ps.strip_end[0] = n / 16;
   ps.count = 1;
   const ActSrc act = {a_q, a_scale, nullptr, nullptr, nullptr};
-  uint8_t* base = static_cast<uint8_t*>(workspace);
-  const SplitK sk = {reinterpret_cast<float*>(base + split_counts_bytes(n / 16)),
-                     reinterpret_cast<uint32_t*>(base), parts};
+  const SplitK sk = {tiles, counts, parts};
   return run_persistent<false, true>(act, ps, m, k, stream, sk);
+}
+
+// ---------------------------------------------------------- allocation-free K split
+// w8a8_block_gemm_noalloc keeps the split's counts and part tiles in `scratch`, a static
+// array of every device the library runs on (each device holds its own copy at its own
+// address).  Host code never uses the array's name as an address: the device address is
+// looked up once per device with hipGetSymbolAddress and kept in scratch_ptr.
+constexpr uint64_t kScratchCountBytes = 4096;        // counts of up to 1024 strips
+constexpr uint64_t kScratchTileBytes = 1u << 20;     // up to 1024 strips x parts of 1 KB
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchCountBytes + kScratchTileBytes];
+
+namespace {
+
+std::mutex scratch_mu;
+uint8_t* scratch_ptr[kMaxDevices] = {};
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, int n) {
+  for (int i = int(blockIdx.x) * 256 + int(threadIdx.x); i < n; i += int(gridDim.x) * 256)
+    p[i] = 0u;
+}
+
+// The current device's scratch address.  The first call on a device looks it up and
+// enqueues a fill that zeroes the counts on `stream` (a kernel, so that a captured graph
+// holds no memset node; the array also starts zeroed when the code object is loaded).
+int scratch_on_device(hipStream_t stream, uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8Q_EHIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP8Q_EHIP;
+    const LaunchEvents timed = g_next_launch_events;  // the fill is not the timed kernel
+    g_next_launch_events = LaunchEvents();
+    launch(zero_words_kernel, dim3(4), dim3(256), 0, stream, static_cast<uint32_t*>(p),
+           int(kScratchCountBytes / 4));
+    g_next_launch_events = timed;
+    if (launch_status() != FP8Q_OK) return FP8Q_ELAUNCH;
+    scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = scratch_ptr[dev];
+  return FP8Q_OK;
 }
 }  // namespace
 
@@ -587,7 +633,30 @@ extern "C" int w8a8_block_gemm_ws(const uint8_t* a_q, const float* a_scale,
   if (!workspace) return FP8Q_ENULL;
   if (workspace_bytes < split_workspace_bytes(n / 16, parts)) return FP8Q_EINVAL;
   if (!aligned(workspace, 256)) return FP8Q_EALIGN;
-  return run_split(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, workspace, parts, stream);
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  return run_split(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc,
+                   reinterpret_cast<uint32_t*>(base),
+                   reinterpret_cast<float*>(base + split_counts_bytes(n / 16)), parts, stream);
+}
+
+extern "C" int w8a8_block_gemm_noalloc(const uint8_t* a_q, const float* a_scale,
+                                       const uint8_t* w_q, const float* w_scale, uint16_t* out,
+                                       int32_t m, int32_t n, int32_t k, int32_t ldc,
+                                       hipStream_t stream) {
+  int rc = check_gemm_common(a_q, a_scale, m, k);
+  if (rc == FP8Q_OK) rc = check_proj(w_q, w_scale, out, n, ldc);
+  if (rc != FP8Q_OK) return rc;
+  const int parts = ws_parts(n, k);
+  if (parts <= 1) return w8a8_block_gemm(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, stream);
+  const uint64_t strips = uint64_t(n / 16);
+  if (strips * 4 > kScratchCountBytes || strips * uint64_t(parts) * 1024 > kScratchTileBytes)
+    return FP8Q_EINVAL;
+  uint8_t* base = nullptr;
+  rc = scratch_on_device(stream, &base);
+  if (rc != FP8Q_OK) return rc;
+  return run_split(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc,
+                   reinterpret_cast<uint32_t*>(base),
+                   reinterpret_cast<float*>(base + kScratchCountBytes), parts, stream);
 }
 
 extern "C" int w8a8_block_gemm_grouped(const uint8_t* a_q, const float* a_scale,

@@ -155,6 +155,22 @@ int w8a8_block_gemm_ws(const uint8_t* a_q, const float* a_scale, const uint8_t* 
                        int32_t ldc, void* workspace, uint64_t workspace_bytes,
                        hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving
+ * loops that forbid allocation): w8a8_block_gemm_ws without the workspace argument.  Same
+ * arguments as w8a8_block_gemm and exactly w8a8_block_gemm_ws's result (the same split and
+ * summation order), with the split's counts and part tiles in a static device array of
+ * 4 KiB + 1 MiB that the library holds on every GPU it runs on until the process ends.
+ * Allocates nothing.  The first call on a device looks the array's address up and enqueues
+ * a fill that zeroes its counts on `stream`; every call leaves them zero.  All calls on one
+ * GPU share the array: calls that overlap in time on one GPU (e.g. on two streams) race;
+ * calls on one stream never overlap.  A shape whose split needs more than the array (more
+ * than 1024 strips, or strips x parts above 1024) is refused with FP8Q_EINVAL before
+ * anything is enqueued; shapes that run unsplit use no scratch.
+ * Errors: as w8a8_block_gemm, and FP8Q_EHIP (the array's address could not be looked up). */
+int w8a8_block_gemm_noalloc(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
+                            const float* w_scale, uint16_t* out, int32_t m, int32_t n,
+                            int32_t k, int32_t ldc, hipStream_t stream);
+
 /* ------------------------------------------------ W8A8 GEMM at prefill widths
  * [resid] DenseFp8Inputs::w8a8_kernels (the W8A8 prefill arm: per-token group quant, then
  * a block-scaled FP8 GEMM); [actq] module doc (a 4593-token prefill).  The arithmetic and
