@@ -81,9 +81,11 @@ class KvCalibOps(ctypes.Structure):
     READ = ctypes.CFUNCTYPE(ctypes.c_int, _P, _P, _P, _U64, _P)
     REPLAY = ctypes.CFUNCTYPE(ctypes.c_int, _P, _P, _P, _P, _P, _I32, _I32,
                               ctypes.POINTER(KvTarget), _F32, _F32, _P)
+    STAGE = ctypes.CFUNCTYPE(ctypes.c_int, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _P,
+                             _P, _P)
     _fields_ = [("ctx", _P), ("device", DEVICE), ("alloc", ALLOC), ("release", RELEASE),
                 ("zero", ZERO), ("amax_rows", AMAX_ROWS), ("copy2d", COPY2D), ("read", READ),
-                ("replay", REPLAY)]
+                ("replay", REPLAY), ("stage", STAGE)]
 
 
 _lib = None

@@ -19,13 +19,15 @@
 // backed by host memory.
 //
 // Differences from the pages: the pages synchronize the stream on every observe inside
-// the window to read the batch's absmax back.  Here the running maximum is
-// max-accumulated on the device across the whole window and read once, at the freeze;
+// the window to read the batch's absmax back, and stage with separate copies.  Here the
+// running maximum is max-accumulated on the device across the whole window and read once,
+// at the freeze;
 // max is order-free, so the frozen scales are bit-identical.  The pages replay one write
 // per staged batch, in order; the HIP table's replay is one write of all staged tokens
 // after dropping every token a later staged token overwrites (last writer wins either
-// way, so the pool bytes are the same).  The staging is allocated and released in stream
-// order, so the freeze blocks only for the 8-byte read.
+// way, so the pool bytes are the same).  The staging is one stream-ordered allocation,
+// released in stream order, so the freeze blocks only for the 8-byte read; an in-window
+// observe is one kernel (the batch's absmax and its staging copy in one pass).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -109,6 +111,12 @@ int hip_copy2d(void*, void* dst, const void* src, int64_t src_pitch, int64_t row
   return e == hipSuccess ? FP8Q_OK : FP8Q_EHIP;
 }
 
+int hip_stage(void*, const uint16_t* k, const uint16_t* v, const int64_t* slots, int64_t rows,
+              int64_t elems, int64_t ks, int64_t vs, uint16_t* dk, uint16_t* dv, int64_t* dslots,
+              float* amax2, hipStream_t stream) {
+  return fp8q::kv_stage(k, v, slots, rows, elems, ks, vs, dk, dv, dslots, amax2, stream);
+}
+
 int hip_read(void*, void* host_dst, const void* src, uint64_t bytes, hipStream_t stream) {
   if (hipMemcpyAsync(host_dst, src, size_t(bytes), hipMemcpyDeviceToHost, stream) !=
           hipSuccess ||
@@ -146,7 +154,9 @@ struct fp8q_kv_calib {
   float k_amax = 0.0f, v_amax = 0.0f;
   int32_t device = -1;
   float* d_amax = nullptr;  // device float[2]: running max |K|, |V| over the window
-  // staging: packed bf16 rows and int64 slots of every staged batch, in order
+  // staging: packed bf16 rows and int64 slots of every staged batch, in order, carved from
+  // one allocation (base)
+  void* base = nullptr;
   uint16_t* sk = nullptr;
   uint16_t* sv = nullptr;
   int64_t* sslots = nullptr;
@@ -165,19 +175,26 @@ int decide_locked(const fp8q_kv_calib* c, int64_t n, int64_t e) {
   return FP8Q_CALIB_STAGE;
 }
 
-// Releases the staging buffers (staging.rs page, KvStaging::release; idempotent).
+// Releases the staging (staging.rs page, KvStaging::release; idempotent).
 int release_staging(fp8q_kv_calib* c, hipStream_t stream, int32_t at_destroy) {
-  int rc = FP8Q_OK;
-  for (void* p : {static_cast<void*>(c->sk), static_cast<void*>(c->sv),
-                  static_cast<void*>(c->sslots), static_cast<void*>(c->rslots)}) {
-    const int r = c->ops.release(c->ops.ctx, p, stream, at_destroy);
-    if (r != FP8Q_OK) rc = r;
-  }
+  const int rc = c->base ? c->ops.release(c->ops.ctx, c->base, stream, at_destroy) : FP8Q_OK;
+  c->base = nullptr;
   c->sk = c->sv = nullptr;
   c->sslots = c->rslots = nullptr;
   c->capacity = c->elems = c->used = 0;
   c->batches.clear();
   return rc;
+}
+
+// Byte offsets of the four staging regions for `rows` tokens of `e` elements, each 256-byte
+// aligned: K rows, V rows, slots, replay scratch; [4] is the total.
+void staging_layout(uint64_t rows, uint64_t e, uint64_t off[5]) {
+  const auto up = [](uint64_t b) { return (b + 255) & ~uint64_t(255); };
+  off[0] = 0;
+  off[1] = off[0] + up(rows * e * 2);
+  off[2] = off[1] + up(rows * e * 2);
+  off[3] = off[2] + up(rows * 8);
+  off[4] = off[3] + up(rows * 8);
 }
 
 float freeze_scale(float amax, float headroom) {
@@ -200,8 +217,9 @@ int create(int32_t window_tokens, float headroom, float provisional_scale,
   if (ops) {
     c->ops = *ops;
   } else {
-    c->ops = fp8q_kv_calib_ops{&c->hip,      hip_device,    hip_alloc,  hip_release, hip_zero,
-                               hip_amax_rows, hip_copy2d,   hip_read,   hip_replay};
+    c->ops = fp8q_kv_calib_ops{&c->hip,       hip_device, hip_alloc, hip_release,
+                               hip_zero,       hip_amax_rows, hip_copy2d, hip_read,
+                               hip_replay,     hip_stage};
   }
   c->requested = window_tokens;
   c->window = window_tokens < kMaxStagedTokens ? window_tokens : kMaxStagedTokens;
@@ -272,34 +290,37 @@ extern "C" int fp8q_kv_calib_observe(fp8q_kv_calib* c, const uint16_t* k, const 
   const int step = decide_locked(c, n, e);
   // allocate before touching any state, so a failure leaves the calibrator unchanged
   if (step == FP8Q_CALIB_STAGE && c->capacity == 0) {
-    const uint64_t rows = uint64_t(c->window);
-    void* p[4] = {nullptr, nullptr, nullptr, nullptr};
-    const uint64_t bytes[4] = {rows * uint64_t(e) * 2, rows * uint64_t(e) * 2, rows * 8,
-                               rows * 8};
-    for (int i = 0; i < 4 && rc == FP8Q_OK; ++i) rc = ops.alloc(ops.ctx, bytes[i], &p[i], stream);
-    if (rc != FP8Q_OK) {
-      for (void* q : p) (void)ops.release(ops.ctx, q, stream, 0);
-      return rc;
-    }
-    c->sk = static_cast<uint16_t*>(p[0]);
-    c->sv = static_cast<uint16_t*>(p[1]);
-    c->sslots = static_cast<int64_t*>(p[2]);
-    c->rslots = static_cast<int64_t*>(p[3]);
+    uint64_t off[5];
+    staging_layout(uint64_t(c->window), uint64_t(e), off);
+    void* p = nullptr;
+    rc = ops.alloc(ops.ctx, off[4], &p, stream);
+    if (rc != FP8Q_OK) return rc;
+    uint8_t* b = static_cast<uint8_t*>(p);
+    c->base = p;
+    c->sk = reinterpret_cast<uint16_t*>(b + off[0]);
+    c->sv = reinterpret_cast<uint16_t*>(b + off[1]);
+    c->sslots = reinterpret_cast<int64_t*>(b + off[2]);
+    c->rslots = reinterpret_cast<int64_t*>(b + off[3]);
     c->capacity = c->window;
     c->elems = e;
   }
 
-  rc = ops.amax_rows(ops.ctx, k, v, n, e, t->key_stride, t->value_stride, c->d_amax, stream);
-  if (rc != FP8Q_OK) return rc;
-
   if (step == FP8Q_CALIB_STAGE) {
-    rc = ops.copy2d(ops.ctx, c->sk + c->used * c->elems, k, int64_t(t->key_stride) * 2, e * 2,
-                    n, stream);
-    if (rc == FP8Q_OK)
-      rc = ops.copy2d(ops.ctx, c->sv + c->used * c->elems, v, int64_t(t->value_stride) * 2,
-                      e * 2, n, stream);
-    if (rc == FP8Q_OK)
-      rc = ops.copy2d(ops.ctx, c->sslots + c->used, t->slot_mapping, n * 8, n * 8, 1, stream);
+    uint16_t* dk = c->sk + c->used * c->elems;
+    uint16_t* dv = c->sv + c->used * c->elems;
+    if (ops.stage) {
+      rc = ops.stage(ops.ctx, k, v, t->slot_mapping, n, e, t->key_stride, t->value_stride, dk,
+                     dv, c->sslots + c->used, c->d_amax, stream);
+    } else {
+      rc = ops.amax_rows(ops.ctx, k, v, n, e, t->key_stride, t->value_stride, c->d_amax,
+                         stream);
+      if (rc == FP8Q_OK)
+        rc = ops.copy2d(ops.ctx, dk, k, int64_t(t->key_stride) * 2, e * 2, n, stream);
+      if (rc == FP8Q_OK)
+        rc = ops.copy2d(ops.ctx, dv, v, int64_t(t->value_stride) * 2, e * 2, n, stream);
+      if (rc == FP8Q_OK)
+        rc = ops.copy2d(ops.ctx, c->sslots + c->used, t->slot_mapping, n * 8, n * 8, 1, stream);
+    }
     if (rc != FP8Q_OK) return rc;
     c->tokens_seen += n;
     c->batches.emplace_back(c->used, int32_t(n));
@@ -307,6 +328,9 @@ extern "C" int fp8q_kv_calib_observe(fp8q_kv_calib* c, const uint16_t* k, const 
     c->used += n;
     return FP8Q_OK;
   }
+
+  rc = ops.amax_rows(ops.ctx, k, v, n, e, t->key_stride, t->value_stride, c->d_amax, stream);
+  if (rc != FP8Q_OK) return rc;
   if (step == FP8Q_CALIB_DECLINE) {
     c->tokens_seen += n;
     c->unstaged += n;

@@ -389,7 +389,65 @@ __global__ __launch_bounds__(kKvBlock) void amax_rows_kernel(const uint16_t* __r
   fold_block_max<kKvBlock>(m, amax2, blockIdx.y, seen);
 }
 
+// Staging of a calibration batch in one pass: `rows` rows of e = 8 * ce bf16 at strides
+// ks / vs (elements) are copied packed to dk / dv (row t at t * e), their |K| / |V| maxima
+// folded into amax2 (as amax_rows_kernel would), and the batch's int64 slots copied to
+// dslots.  Work item = the same 16-byte chunk of one row of K and of V: item i -> row i / ce,
+// chunk i % ce, so consecutive lanes read and write contiguous bytes.
+constexpr int kStageBlock = 256;
+__global__ __launch_bounds__(kStageBlock) void kv_stage_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int64_t* __restrict__ slots, int64_t rows, int64_t ce, int64_t ks, int64_t vs,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int64_t* __restrict__ dslots,
+    float* __restrict__ amax2) {
+  const float seen = threadIdx.x < 2 ? seen_max(amax2, int(threadIdx.x)) : 0.0f;
+  const int64_t items = rows * ce;
+  const int64_t stride = int64_t(gridDim.x) * kStageBlock;
+  const int64_t first = int64_t(blockIdx.x) * kStageBlock + threadIdx.x;
+  float mk = 0.0f, mv = 0.0f;
+  for (int64_t i = first; i < items; i += stride) {
+    const int64_t t = i / ce, c = i - t * ce;
+    const uint4 a = *reinterpret_cast<const uint4*>(k + t * ks + c * 8);
+    const uint4 b = *reinterpret_cast<const uint4*>(v + t * vs + c * 8);
+    *reinterpret_cast<uint4*>(dk + i * 8) = a;
+    *reinterpret_cast<uint4*>(dv + i * 8) = b;
+    mk = fmaxf(mk, absmax8(a));
+    mv = fmaxf(mv, absmax8(b));
+  }
+  for (int64_t i = first; i < rows; i += stride) dslots[i] = slots[i];
+  fold_block_max2<kStageBlock>(mk, mv, amax2, seen);
+}
+
 }  // namespace
+
+int kv_stage(const uint16_t* k, const uint16_t* v, const int64_t* slots, int64_t rows,
+             int64_t e, int64_t key_stride, int64_t value_stride, uint16_t* dk, uint16_t* dv,
+             int64_t* dslots, float* amax2, hipStream_t stream) {
+  if (rows <= 0) return FP8Q_OK;
+  const bool vec = e % 8 == 0 && key_stride % 8 == 0 && value_stride % 8 == 0 &&
+                   aligned(k, 16) && aligned(v, 16) && aligned(dk, 16) && aligned(dv, 16) &&
+                   aligned(slots, 8) && aligned(dslots, 8);
+  if (vec) {
+    const int64_t items = rows * (e / 8);
+    int64_t blocks = (items + kStageBlock - 1) / kStageBlock;
+    if (blocks > 1024) blocks = 1024;
+    launch(kv_stage_kernel, dim3(unsigned(blocks)), dim3(kStageBlock), 0, stream, k, v, slots,
+           rows, e / 8, key_stride, value_stride, dk, dv, dslots, amax2);
+    return launch_status();
+  }
+  // other geometries: the absmax pass, then the row and slot copies
+  int rc = kv_amax_rows(k, v, rows, e, key_stride, value_stride, amax2, stream);
+  if (rc != FP8Q_OK) return rc;
+  const size_t row = size_t(e) * 2;
+  if (hipMemcpy2DAsync(dk, row, k, size_t(key_stride) * 2, row, size_t(rows),
+                       hipMemcpyDeviceToDevice, stream) != hipSuccess ||
+      hipMemcpy2DAsync(dv, row, v, size_t(value_stride) * 2, row, size_t(rows),
+                       hipMemcpyDeviceToDevice, stream) != hipSuccess ||
+      hipMemcpyAsync(dslots, slots, size_t(rows) * 8, hipMemcpyDeviceToDevice, stream) !=
+          hipSuccess)
+    return FP8Q_EHIP;
+  return FP8Q_OK;
+}
 
 int kv_amax_rows(const uint16_t* k, const uint16_t* v, int64_t rows, int64_t row_elems,
                  int64_t key_stride, int64_t value_stride, float* amax2, hipStream_t stream) {

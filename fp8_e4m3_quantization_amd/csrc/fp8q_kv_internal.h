@@ -38,6 +38,13 @@ int kv_write(const uint16_t* k, const uint16_t* v, uint8_t* k_cache, uint8_t* v_
 // pools exactly as writing the list's tokens one after another would.
 int kv_last_writer_slots(const int64_t* slots, int64_t* out, int32_t n, hipStream_t stream);
 
+// A calibration batch staged in one pass: rows copied packed to dk / dv, slots to dslots,
+// the rows' |K| / |V| maxima folded into amax2 (one kernel for 16-byte aligned geometries,
+// else the absmax pass and copies).
+int kv_stage(const uint16_t* k, const uint16_t* v, const int64_t* slots, int64_t rows,
+             int64_t e, int64_t key_stride, int64_t value_stride, uint16_t* dk, uint16_t* dv,
+             int64_t* dslots, float* amax2, hipStream_t stream);
+
 int kv_amax_rows(const uint16_t* k, const uint16_t* v, int64_t rows, int64_t row_elems,
                  int64_t key_stride, int64_t value_stride, float* amax2, hipStream_t stream);
 

@@ -411,7 +411,10 @@ typedef struct fp8q_kv_calib_info {
  *   replay      write n staged packed rows (`elems` bf16 each, K and V) to the target's pools
  *               at (k_scale, v_scale) as fp8_kv_write would write them one after another in
  *               staging order (a slot staged twice keeps its later row); scratch_slots is
- *               int64 [n] of device scratch the callback may use; stream-ordered */
+ *               int64 [n] of device scratch the callback may use; stream-ordered
+ *   stage       optional (NULL: amax_rows, then copy2d of the K rows, V rows and slots): the
+ *               same in one call -- amax_rows over the batch, its rows copied packed to
+ *               dst_k / dst_v (row t at t * elems) and its `rows` slots to dst_slots */
 typedef struct fp8q_kv_calib_ops {
   void* ctx;
   int (*device)(void* ctx, int32_t* dev);
@@ -427,6 +430,10 @@ typedef struct fp8q_kv_calib_ops {
   int (*replay)(void* ctx, const uint16_t* k, const uint16_t* v, const int64_t* slots,
                 int64_t* scratch_slots, int32_t n, int32_t elems, const fp8q_kv_target* target,
                 float k_scale, float v_scale, hipStream_t stream);
+  int (*stage)(void* ctx, const uint16_t* k, const uint16_t* v, const int64_t* slots,
+               int64_t rows, int64_t elems, int64_t key_stride, int64_t value_stride,
+               uint16_t* dst_k, uint16_t* dst_v, int64_t* dst_slots, float* amax2,
+               hipStream_t stream);
 } fp8q_kv_calib_ops;
 
 /* window_tokens > 0 (window 0 means no calibrator: FP8Q_EINVAL); headroom finite and
@@ -437,14 +444,16 @@ typedef struct fp8q_kv_calib_ops {
 int fp8q_kv_calib_create(int32_t window_tokens, float headroom, float provisional_scale,
                          fp8q_kv_calib** out);
 /* As fp8q_kv_calib_create, with the device work going through `ops` (copied; every
- * callback must be set; the table's ctx must outlive the calibrator). */
+ * callback but stage must be set; the table's ctx must outlive the calibrator). */
 int fp8q_kv_calib_create_with_ops(int32_t window_tokens, float headroom,
                                   float provisional_scale, const fp8q_kv_calib_ops* ops,
                                   fp8q_kv_calib** out);
 /* Fold one batch in (see above).  k, v: device bf16 [num_tokens] rows at the target's
  * key/value strides.  Enqueues work on `stream`; blocks only at the freeze, to read the
- * 8-byte running maximum back.  The first staged batch allocates the staging (window * H *
- * D * 2 * 2 + window * 16 bytes, stream-ordered), the freeze releases it in stream order.
+ * 8-byte running maximum back.  The first staged batch allocates the staging in one piece
+ * (window * H * D * 2 * 2 + window * 16 bytes, stream-ordered); the freeze releases it in
+ * stream order.  With the library's HIP table an in-window observe is one kernel (absmax
+ * and staging copy in one pass).
  * A frozen scale outside [2^-64, 2^64] (the write's scale range) fails the freezing
  * observe with FP8Q_EINVAL and leaves the calibrator as it was (the batch's absmax may
  * already be folded into the running maximum; folding the same batch again changes

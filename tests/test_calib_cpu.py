@@ -39,7 +39,7 @@ class HostOps:
     a read of memory the calibrator never initialized shows), the absmax and the replay's
     write are the oracle's, the replay writes the staged tokens one after another."""
 
-    def __init__(self, pools):
+    def __init__(self, pools, with_stage=False):
         self.bufs = {}
         self.pools = pools  # address -> numpy pool the target points at
         self.reads = 0
@@ -51,7 +51,8 @@ class HostOps:
             None, ops.DEVICE(self._guard(self.device)), ops.ALLOC(self._guard(self.alloc)),
             ops.RELEASE(self._guard(self.release)), ops.ZERO(self._guard(self.zero)),
             ops.AMAX_ROWS(self._guard(self.amax_rows)), ops.COPY2D(self._guard(self.copy2d)),
-            ops.READ(self._guard(self.read)), ops.REPLAY(self._guard(self.replay)))
+            ops.READ(self._guard(self.read)), ops.REPLAY(self._guard(self.replay)),
+            ops.STAGE(self._guard(self.stage)) if with_stage else ops.STAGE())
 
     def _guard(self, fn):
         def call(*a):
@@ -95,6 +96,17 @@ class HostOps:
             ctypes.memmove(dst + r * row_bytes, src + r * src_pitch, row_bytes)
         return 0
 
+    def stage(self, ctx, k, v, slots, rows, elems, ks, vs, dk, dv, dslots, amax2, stream):
+        """The optional one-call staging: absmax, packed rows, slots."""
+        self.amax_rows(ctx, k, v, rows, elems, ks, vs, amax2, stream)
+        packed_k = np.ascontiguousarray(_rows(k, rows, elems, ks))  # held until copied
+        packed_v = np.ascontiguousarray(_rows(v, rows, elems, vs))
+        ctypes.memmove(dk, packed_k.ctypes.data, packed_k.nbytes)
+        ctypes.memmove(dv, packed_v.ctypes.data, packed_v.nbytes)
+        ctypes.memmove(dslots, slots, rows * 8)
+        self.staged_calls = getattr(self, "staged_calls", 0) + 1
+        return 0
+
     def read(self, ctx, host_dst, src, nbytes, stream):
         self.reads += 1
         ctypes.memmove(host_dst, src, nbytes)
@@ -120,9 +132,10 @@ def _batch_input(b, narrow):
     return b.k, b.v, H
 
 
-def _run_library(batches, window, headroom=1.0, provisional=2.0, decline_at=None):
+def _run_library(batches, window, headroom=1.0, provisional=2.0, decline_at=None,
+                 with_stage=False):
     kc, vc = _pools()
-    ops = HostOps({kc.ctypes.data: kc, vc.ctypes.data: vc})
+    ops = HostOps({kc.ctypes.data: kc, vc.ctypes.data: vc}, with_stage)
     lib = fq.load()
     cal = fq.KvCalibrator(window, headroom, provisional, ops=ops.table)
     steps = []
@@ -179,12 +192,17 @@ def _same(lib_run, ora_run):
 
 @pytest.mark.parametrize("window,headroom,seed", [(256, 1.0, 5000), (256, 1.5, 5001),
                                                   (1, 1.0, 5002), (100, 0.5, 5003)])
-def test_library_calibrator_equals_oracle(window, headroom, seed):
+@pytest.mark.parametrize("with_stage", [False, True])
+def test_library_calibrator_equals_oracle(window, headroom, seed, with_stage):
+    """With and without the optional one-call staging callback."""
     batches, reuse = synth.kv_batches(num_tokens_total=synth.KV_WINDOW + 96, seed=seed)
     if window == 256 and seed == 5000:  # the configuration's own run rewrites a freed slot
         cross = int(np.searchsorted(np.cumsum([len(b.slots) for b in batches]), window))
         assert any(bi <= cross for bi, _ in reuse)
-    _same(_run_library(batches, window, headroom), _run_oracle(batches, window, headroom))
+    run = _run_library(batches, window, headroom, with_stage=with_stage)
+    _same(run, _run_oracle(batches, window, headroom))
+    if with_stage and window > 1:
+        assert run[4].staged_calls == run[2]["staged_batches"]
 
 
 def test_window_one_freezes_on_the_first_observe_and_stages_nothing():

@@ -159,6 +159,38 @@ def test_calibration_matches_oracle(window, headroom, seed):
     assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
 
 
+@pytest.mark.parametrize("k_pad,v_pad", [(64, 8), (3, 1)])
+def test_calibration_from_strided_rows_matches_oracle(k_pad, v_pad):
+    """K / V rows inside wider buffers: strides that keep 16-byte rows take the one-kernel
+    staging (absmax + packed copy + slots), odd strides the absmax pass and 2-D copies; both
+    stage the same packed rows, so the pools and scales equal the oracle's on packed input."""
+    batches, _ = synth.kv_batches(num_tokens_total=synth.KV_WINDOW + 96, seed=5030 + k_pad)
+    ks, vs = E + k_pad, E + v_pad
+    _, _, kcd, vcd = _pools()
+    cal = fq.KvCalibrator(synth.KV_WINDOW)
+    for b in batches:
+        n = len(b.slots)
+        # padding of bf16 2^127: a read past a row would show in the maxima and the codes
+        kw = torch.full((n, ks), 0x7F00, dtype=torch.int16, device=DEV)
+        vw = torch.full((n, vs), 0x7F00, dtype=torch.int16, device=DEV)
+        kw[:, :E] = torch.from_numpy(b.k.view(np.int16)).to(DEV)
+        vw[:, :E] = torch.from_numpy(b.v.view(np.int16)).to(DEV)
+        kd, vd = kw.view(torch.bfloat16)[:, :E], vw.view(torch.bfloat16)[:, :E]
+        sd = i64_dev(b.slots)
+        cal.observe(kd, vd, H, D, kcd, vcd, sd, BS, key_stride=ks, value_stride=vs,
+                    cache_stride=CS)
+        k_scale, v_scale = cal.scales()
+        fq.fp8_kv_write(kd, vd, kcd, vcd, sd, H, D, BS, k_scale, v_scale, key_stride=ks,
+                        value_stride=vs, cache_stride=CS)
+    info = cal.info()
+    cal.close()
+    kc_ref, vc_ref, ref = _calibrate_oracle(batches, synth.KV_WINDOW)
+    assert info["frozen"] == 1 and info["replayed_tokens"] == ref["replayed_tokens"] > 0
+    for key in ("k_scale", "v_scale", "k_amax", "v_amax"):
+        assert np.float32(info[key]) == ref[key.replace("amax", "max")], key
+    assert np.array_equal(host(kcd), kc_ref) and np.array_equal(host(vcd), vc_ref)
+
+
 def test_calibration_with_a_declined_batch_matches_oracle():
     batches, _ = synth.kv_batches(num_tokens_total=synth.KV_WINDOW + 96, seed=5004)
     kc, vc, info = _calibrate_on_gpu(batches, synth.KV_WINDOW, decline_at=1)
