@@ -127,25 +127,27 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
   if (wave == 7 && (lane == 32 || lane == 33))
     gsp = w_scale + int64_t(min((n0 + kWaveCols * (lane - 32)) >> 7, (n >> 7) - 1)) * groups;
 
-  // The copies of group g; outside [0, groups) they read a zero-size buffer (zeros written,
-  // no memory traffic) and repeat a valid scale.  Every copy is unconditional: a branch
-  // here would split the step and let the compiler sink its FMAs past the next barrier.
-  auto copy_group = [&](uint8_t* sa, uint8_t* sb, float* ss, int g) {
+  // The copies of group g, in pieces: j < 4 the activation blocks, then the kBBlocks weight
+  // blocks, then the scales.  Outside [0, groups) they read a zero-size buffer (zeros
+  // written, no memory traffic) and repeat a valid scale.  Every copy is unconditional: a
+  // branch here would split the step and let the compiler sink its FMAs past the next
+  // barrier.
+  constexpr int kPieces = 4 + kBBlocks + 1;
+  auto copy_piece = [&](uint8_t* sa, uint8_t* sb, float* ss, int g, int j) {
     const bool live = g >= 0 && g < groups;
-    const __amdgpu_buffer_rsrc_t ra = live ? ra_rsrc : none_rsrc;
-    const __amdgpu_buffer_rsrc_t rb = live ? rb_rsrc : none_rsrc;
     const int goff = live ? g * 128 : 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(sa + (wave + 8 * q) * 1024), 16,
-                                               voff[q], goff, 0, 0);
-#pragma unroll
-    for (int q = 0; q < kBBlocks; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(sb + (wave + 8 * q) * 1024), 16,
-                                               voff[q], goff, 0, 0);
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(gsp + min(max(g, 0), groups - 1)),
-        (lds_void*)(ss + 32 * wave), 4, 0, 0);
+    if (j < 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? ra_rsrc : none_rsrc,
+                                               (lds_void*)(sa + (wave + 8 * j) * 1024), 16,
+                                               voff[j], goff, 0, 0);
+    else if (j < 4 + kBBlocks)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rb_rsrc : none_rsrc,
+                                               (lds_void*)(sb + (wave + 8 * (j - 4)) * 1024),
+                                               16, voff[j - 4], goff, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(gsp + min(max(g, 0), groups - 1)),
+          (lds_void*)(ss + 32 * wave), 4, 0, 0);
   };
 
   v4f acc[4][kCols];
@@ -175,11 +177,14 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
   };
 
   // Group g from stage (sa, sb, ss); the copies of group g + 1 go to (na, nbs, ns), which
-  // held group g - 1 (read by everyone before the barrier).
+  // held group g - 1 (read by everyone before the barrier).  The copies are dealt out over
+  // the first half of the step's MFMAs, one piece after each, rather than issued in one
+  // burst ahead of them (the burst queues in the address unit and holds back the MFMAs
+  // that follow it in the wave's instruction stream).
   auto step = [&](int g, const uint8_t* sa, const uint8_t* sb, const float* ss, uint8_t* na,
                   uint8_t* nbs, float* ns) {
     __syncthreads();  // everyone's copies of group g landed (the fence drains them)
-    copy_group(na, nbs, ns, g + 1);
+    copy_piece(na, nbs, ns, g + 1, 0);
     // Column 0 starts once B_0, A_0 and A_1 are in: each later fragment is read one MFMA
     // ahead of its use, the scales last (their first use is column 0's FMAs, in column 1).
     v8i af[4];
@@ -191,13 +196,19 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
     __builtin_amdgcn_sched_barrier(0);
     pcur[0] = mfma_group(af[0], bcur);
     __builtin_amdgcn_sched_barrier(0);
+    copy_piece(na, nbs, ns, g + 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
     af[2] = ld32(sa + 2 * 2048, a_lo, a_hi);
     __builtin_amdgcn_sched_barrier(0);
     pcur[1] = mfma_group(af[1], bcur);
     __builtin_amdgcn_sched_barrier(0);
+    copy_piece(na, nbs, ns, g + 1, 2);
+    __builtin_amdgcn_sched_barrier(0);
     af[3] = ld32(sa + 3 * 2048, a_lo, a_hi);
     __builtin_amdgcn_sched_barrier(0);
     pcur[2] = mfma_group(af[2], bcur);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_piece(na, nbs, ns, g + 1, 3);
     __builtin_amdgcn_sched_barrier(0);
     v8i bnxt = ld32(sb + 2048, b_lo, b_hi);
 #pragma unroll
@@ -218,6 +229,8 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
     bcur = bnxt;
 #pragma unroll
     for (int c = 1; c <= kCols; ++c) {
+      if (3 + c < kPieces) copy_piece(na, nbs, ns, g + 1, 3 + c);
+      __builtin_amdgcn_sched_barrier(0);
       bnxt = bcur;
       if (c + 1 < kCols) bnxt = ld32(sb + (c + 1) * 2048, b_lo, b_hi);
 #pragma unroll
@@ -249,7 +262,8 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
   // An odd group count starts with one step over a zero group, so that steps come in
   // pairs and each step's stage is fixed at compile time.
   const int odd = groups & 1;
-  copy_group(st.a0, st.b0, st.s0, -odd);
+#pragma unroll
+  for (int j = 0; j < kPieces; ++j) copy_piece(st.a0, st.b0, st.s0, -odd, j);
   for (int g = -odd; g < groups; g += 2) {
     step(g, st.a0, st.b0, st.s0, st.a1, st.b1, st.s1);
     step(g + 1, st.a1, st.b1, st.s1, st.a0, st.b0, st.s0);
