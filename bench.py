@@ -94,6 +94,23 @@ def kv_amax_bytes(t, e=KV_H * KV_D):
     return 2 * t * e * 2
 
 
+def prefill_copy_bytes(m, n, k, cus):
+    """Bytes the prefill GEMM moves from global memory into LDS per launch: every output tile
+    copies its activation and weight tile of each 128-wide group plus 1 KB of scales (the
+    launch rule of w8a8_block_gemm_prefill: 256 x 256 tiles, the last round's tiles split
+    into two 256 x 128 halves when it would leave half the CUs idle; else 128 x 128 tiles)."""
+    g = k // 128
+    big_m, big_n = -(-m // 256), -(-n // 256)
+    big = big_m * big_n
+    if 2 * big >= cus:
+        tail = big % cus
+        split = tail if (tail and 2 * tail <= cus) else 0
+        whole = big - split
+        return g * (whole * (2 * 256 * 128 + 1024) + split * 2 * (256 * 128 + 128 * 128 + 1024))
+    tiles = -(-m // 128) * -(-n // 128)
+    return g * tiles * (2 * 128 * 128 + 512)
+
+
 def grouped_gemm_bytes(m, ns, k):
     """Several projections of one activation in one launch: the activation is read once."""
     return sum(gemm_bytes(m, n, k) for n in ns) - (len(ns) - 1) * (m * k + m * (k // 128) * 4)
@@ -414,8 +431,36 @@ def main():
                                 rotation_sets=nset)
             log(f"prefill gemm m={m} n={n}: {mean_us:.1f} us {kernels[key]['tflops']} TFLOP/s "
                 f"({kernels[key]['frac_mfma_fp8']:.3f} of fp8 MFMA peak, {nset} operand sets)")
+            kernels[key]["copy_bytes"] = prefill_copy_bytes(
+                m, n, K_DECODE, torch.cuda.get_device_properties(0).multi_processor_count)
             del ps, launches
         del q0, s0
+        # The copy path alone (global -> LDS, the GEMM's own copy instructions and slices, no
+        # MFMA) moving the N = 16384 launch's operand bytes, from an L2-resident span and from
+        # HBM, beside the launch's MFMA time at the fp8 peak: the floors the GEMM is read
+        # against (overlapped perfectly it takes the larger, serialized their sum).
+        lib = fq.load()
+        stream = torch.cuda.current_stream().cuda_stream
+        key = f"w8a8_gemm_prefill_m{m}_n16384_k5120"
+        total = kernels[key]["copy_bytes"] // 65536 * 65536
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        path = {}
+        for name, span in (("l2_2MB", 2 << 20), ("hbm_1GB", 1 << 30)):
+            mean_us, med_us = timer.kernel_us(
+                [lambda sp=span: lib.fp8q_reference_lds_stream(src.data_ptr(), sp, total, stream)],
+                10)
+            path[name] = dict(us=round(mean_us, 2), us_median=round(med_us, 2),
+                              gbs=round(total / (mean_us * 1e-6) / 1e9, 1))
+            log(f"reference global->LDS copy of {total / 1e9:.2f} GB from {name}: {mean_us:.1f} us "
+                f"({path[name]['gbs']:.0f} GB/s)")
+        mfma_us = 2.0 * m * 16384 * K_DECODE / (FP8_MFMA_PEAK_TFLOPS * 1e12) * 1e6
+        path["mfma_at_peak_us"] = round(mfma_us, 2)
+        path["gemm_us"] = kernels[key]["us"]
+        path["floor_overlapped_us"] = round(max(mfma_us, path["l2_2MB"]["us"]), 2)
+        path["floor_serialized_us"] = round(mfma_us + path["l2_2MB"]["us"], 2)
+        path["bytes"] = total
+        kernels["prefill_copy_path_n16384"] = path
+        del src
 
     # ----------------------------------------------------------- width sweep
     if "sweep" in only:

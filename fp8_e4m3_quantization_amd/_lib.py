@@ -21,7 +21,7 @@ FP8Q_CALIB_STAGE, FP8Q_CALIB_DECLINE, FP8Q_CALIB_FREEZE, FP8Q_CALIB_FROZEN = 0, 
 # Every symbol include/fp8q.h declares.
 EXPORTS = (
     "fp8q_strerror", "fp8q_version", "fp8q_time_next_launch", "fp8q_reference_empty",
-    "fp8q_reference_stream", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
+    "fp8q_reference_stream", "fp8q_reference_lds_stream", "fp8_group_quant", "fp8_block_quant", "fp8_e4m3_encode",
     "w8a8_block_gemm", "w8a8_block_gemm_workspace_size", "w8a8_block_gemm_ws",
     "w8a8_block_gemm_noalloc",
     "w8a8_block_gemm_prefill", "w8a8_block_gemm_grouped",
@@ -107,6 +107,7 @@ def load() -> ctypes.CDLL:
         "fp8q_time_next_launch": (ctypes.c_int, [P, P]),
         "fp8q_reference_empty": (ctypes.c_int, [P]),
         "fp8q_reference_stream": (ctypes.c_int, [P, P, I64, P]),
+        "fp8q_reference_lds_stream": (ctypes.c_int, [P, I64, I64, P]),
         "fp8_group_quant": (ctypes.c_int, [P, P, P, I64, I32, P]),
         "fp8_block_quant": (ctypes.c_int, [P, P, P, I32, I32, P]),
         "fp8_e4m3_encode": (ctypes.c_int, [P, P, I64, P]),

@@ -60,9 +60,17 @@ int fp8q_time_next_launch(hipEvent_t start, hipEvent_t stop);
  * src_bytes (a multiple of 16) from src and writes src_bytes / 2 to dst -- the 2:1
  * read/write mix of the group quantizer and the KV write, with no arithmetic -- over a grid
  * of 4 blocks per CU.  src 16-byte and dst 8-byte aligned device memory.
+ * fp8q_reference_lds_stream moves total_bytes from src into LDS the way the prefill GEMM
+ * moves its operand tiles (16-byte buffer_load ... lds, 64 KB slices, one 512-thread
+ * workgroup per CU, one slice landing while the next is issued, a barrier per slice) and
+ * nothing else; slice s reads src bytes [(s * 65536) % span_bytes, + 65536).  span_bytes
+ * and total_bytes are multiples of 65536, 65536 <= span_bytes <= 0x7FFF0000; src holds
+ * span_bytes of device memory, 16-byte aligned.
  * Errors: FP8Q_EINVAL, FP8Q_ENULL, FP8Q_EALIGN, FP8Q_ELAUNCH. */
 int fp8q_reference_empty(hipStream_t stream);
 int fp8q_reference_stream(const void* src, void* dst, int64_t src_bytes, hipStream_t stream);
+int fp8q_reference_lds_stream(const void* src, int64_t span_bytes, int64_t total_bytes,
+                              hipStream_t stream);
 
 /* ------------------------------------------------ per-token 1x128 group quant
  * [actq] module doc: one FP32 scale per 128-wide K-group of one token row;

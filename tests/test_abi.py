@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = fq.load()
-    assert lib.fp8q_version() == 10100
+    assert lib.fp8q_version() == 10200
     for code in (0, -1, -2, -3, -4, -5, -6):
         assert fq.strerror(code) and fq.strerror(code) != "unknown status"
     assert fq.strerror(-99) == "unknown status"
@@ -84,6 +84,12 @@ def test_workspace_gemm_and_reference_argument_checks():
     assert lib.fp8q_reference_stream(None, FAKE, 32, None) == ENULL
     assert lib.fp8q_reference_stream(FAKE + 8, FAKE, 32, None) == EALIGN
     assert lib.fp8q_reference_stream(None, None, 0, None) == 0
+    assert lib.fp8q_reference_lds_stream(FAKE, 65536 + 16, 65536, None) == EINVAL
+    assert lib.fp8q_reference_lds_stream(FAKE, 65536, 1000, None) == EINVAL
+    assert lib.fp8q_reference_lds_stream(FAKE, 0x7FFF0000 + 65536, 65536, None) == EINVAL
+    assert lib.fp8q_reference_lds_stream(None, 65536, 65536, None) == ENULL
+    assert lib.fp8q_reference_lds_stream(FAKE + 8, 65536, 65536, None) == EALIGN
+    assert lib.fp8q_reference_lds_stream(None, 65536, 0, None) == 0
 
 
 def test_kv_write_argument_checks():
