@@ -186,7 +186,7 @@ struct SplitK {
 
 template <int kGpw, int kDepth, int kAux, int kRound, bool kQuant, bool kSplit>
 __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
-    ActSrc act, ProjSet ps, int m, int k, int total_strips, SplitK sk) {
+    ActSrc act, ProjSet ps, int m, int k, int total_strips, int half_from, SplitK sk) {
   static_assert(kRound % (kDepth + 1) == 0, "buffer index must be static within a round");
   static_assert(kRound * 256 == kPWaves * 64 * 2, "reduce: two outputs per lane");
   static_assert(!(kQuant && kSplit), "the fused quantizer runs unsplit");
@@ -210,11 +210,16 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
 #pragma unroll
   for (int u = 0; u < kGpw; ++u) goff[u] = (g0 + max(0, min(u, cnt - 1))) * 128;
 
+  // work items: strips, the last round's halved (never in a K split, whose parts' tiles
+  // are summed per strip)
+  const int total_items = kSplit ? total_strips : item_count(total_strips, half_from);
   auto fetch = [&](int s, Slice<kGpw>& sl) {
-    const bool valid = s < total_strips;
+    const bool valid = s < total_items;
+    const StripItem it = strip_item(valid ? s : total_items - 1, kSplit ? total_strips : half_from);
     int p, n0;
-    locate_strip(ps, valid ? s : total_strips - 1, &p, &n0);
-    const __amdgpu_buffer_rsrc_t r = make_strip_rsrc(ps.w[p] + int64_t(n0) * k, k, valid);
+    locate_strip(ps, it.strip, &p, &n0);
+    const __amdgpu_buffer_rsrc_t r =
+        make_strip_rsrc(ps.w[p] + int64_t(n0 + it.col0) * k, k, valid, it.cols);
     const_float* wsp = (const_float*)(ps.ws[p] + int64_t(n0 >> 7) * groups);
 #pragma unroll
     for (int u = 0; u < kGpw; ++u) sl.b[u] = buffer_load32<kAux>(r, row * k + koff + goff[u]);
@@ -224,7 +229,7 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
 
   const int stride = set_size;
   const int first = first_strip(in_set, stride);
-  const int nit = (total_strips - first + stride - 1) / stride;
+  const int nit = (total_items - first + stride - 1) / stride;
   if (nit <= 0) return;
 
   // 1) raw activation loads, 2) the first weight prefetch, 3) activation fragments: the
@@ -373,14 +378,15 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_persistent_kernel(
           __hip_atomic_store(dst, sum[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(dst + 64, sum[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
+          const StripItem it = strip_item(strip, half_from);  // `strip` is an item here
           int p, n0;
-          locate_strip(ps, strip, &p, &n0);
-          uint16_t* o = ps.out[p] + n0 + (lane & 15);
+          locate_strip(ps, it.strip, &p, &n0);
+          uint16_t* o = ps.out[p] + n0 + it.col0 + (lane & 15);
           const int ldc = ps.ldc[p];
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
             const int r = 4 * (lane >> 4) + q0 + x;
-            if (r < m) o[int64_t(r) * ldc] = f32_to_bf16_rne(sum[x]);
+            if (r < m && (lane & 15) < it.cols) o[int64_t(r) * ldc] = f32_to_bf16_rne(sum[x]);
           }
         }
       }
@@ -446,8 +452,9 @@ int launch_persistent(const ActSrc& act, const ProjSet& ps, int m, int k, int to
   // a short slice per wave (split K) keeps more strips in flight to cover the latency
   constexpr int kDepth = (kSplit && kGpw <= 2) ? 3 : 1;
   constexpr int kRound = 4;
+  const int half_from = kSplit ? total : halved_from(total, grid);
   launch((w8a8_persistent_kernel<kGpw, kDepth, kGemmAux, kRound, kQuant, kSplit>),
-         dim3(grid), dim3(64 * kPWaves), 0, stream, act, ps, m, k, total, sk);
+         dim3(grid), dim3(64 * kPWaves), 0, stream, act, ps, m, k, total, half_from, sk);
   return launch_status();
 }
 

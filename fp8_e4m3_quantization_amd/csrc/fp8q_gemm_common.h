@@ -46,10 +46,37 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr uint32_t kBufferDword3 = 0x00020000;  // raw 32-bit buffer format (gfx9 family)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_strip_rsrc(const uint8_t* base, int k,
-                                                                  bool valid) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, valid ? 16 * k : 0,
+                                                                  bool valid, int rows = 16) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, valid ? rows * k : 0,
                                            kBufferDword3);
 }
+
+// ---------------------------------------------------------------------------------
+// Work items of a persistent launch.  Strips [0, half_from) are whole items; every later
+// strip is two items of 8 columns (item half_from + 2 (s - half_from) + h covers columns
+// 8h .. 8h + 7 of strip s).  When the strips leave a last round at most half full, its
+// strips are halved so that every workgroup takes one half: each then streams the same
+// bytes, instead of half the workgroups streaming a whole extra strip while the rest idle.
+// A half item reads its 8 weight rows through a descriptor 8 rows long, so the other 8
+// rows of the MFMA's weight operand read as zeros and only the item's own 8 output
+// columns are stored: the products of the stored columns are the whole strip's.
+struct StripItem {
+  int strip;  // strip index
+  int col0;   // first column of the item within the strip (0 or 8)
+  int cols;   // 16, or 8 for a half
+};
+__device__ __forceinline__ StripItem strip_item(int item, int half_from) {
+  if (item < half_from) return StripItem{item, 0, 16};
+  const int h = item - half_from;
+  return StripItem{half_from + (h >> 1), 8 * (h & 1), 8};
+}
+
+// First halved strip for `strips` strips over `grid` workgroups (strips: none halved).
+__host__ __device__ inline int halved_from(int strips, int grid) {
+  const int rest = strips % grid;
+  return (rest != 0 && 2 * rest <= grid) ? strips - rest : strips;
+}
+__host__ __device__ inline int item_count(int strips, int half_from) { return half_from + 2 * (strips - half_from); }
 
 // Weight block scales are read-only for the whole launch and uniform per wave: reading
 // them through the constant address space makes them scalar loads (counted apart from

@@ -64,7 +64,7 @@ struct GemvSlice {
 // m <= 4 only lanes 0..15 carry stored rows.
 template <int kGpw>
 __global__ __launch_bounds__(64 * kPWaves) void w8a16_persistent_kernel(
-    const uint16_t* __restrict__ a, ProjSet ps, int m, int k, int total_strips) {
+    const uint16_t* __restrict__ a, ProjSet ps, int m, int k, int total_strips, int half_from) {
   __shared__ float s_part[2][kGemvRound * kPWaves * 64];
   __shared__ uint4 s_tile[kPWaves * ActTile<16>::kUints];
   const int lane = threadIdx.x & 63;
@@ -78,11 +78,14 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a16_persistent_kernel(
 #pragma unroll
   for (int u = 0; u < kGpw; ++u) goff[u] = (g0 + max(0, min(u, cnt - 1))) * 128;
 
+  const int total_items = item_count(total_strips, half_from);  // see StripItem
   auto fetch = [&](int s, GemvSlice<kGpw>& sl) {
-    const bool valid = s < total_strips;
+    const bool valid = s < total_items;
+    const StripItem it = strip_item(valid ? s : total_items - 1, half_from);
     int p, n0;
-    locate_strip(ps, valid ? s : total_strips - 1, &p, &n0);
-    const __amdgpu_buffer_rsrc_t r = make_strip_rsrc(ps.w[p] + int64_t(n0) * k, k, valid);
+    locate_strip(ps, it.strip, &p, &n0);
+    const __amdgpu_buffer_rsrc_t r =
+        make_strip_rsrc(ps.w[p] + int64_t(n0 + it.col0) * k, k, valid, it.cols);
     const_float* wsp = (const_float*)(ps.ws[p] + int64_t(n0 >> 7) * groups);
 #pragma unroll
     for (int u = 0; u < kGpw; ++u) sl.b[u] = buffer_load32<0>(r, row * k + koff + goff[u]);
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a16_persistent_kernel(
 
   const int stride = int(gridDim.x);
   const int first = first_strip(int(blockIdx.x), stride);
-  const int nit = (total_strips - first + stride - 1) / stride;
+  const int nit = (total_items - first + stride - 1) / stride;
   if (nit <= 0) return;
 
   // activation tiles first, then the first weight prefetch, then the fragments (through
@@ -161,9 +164,10 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a16_persistent_kernel(
 #pragma unroll
       for (int w = 0; w < kPWaves; ++w) sum += part[((j * kPWaves + w) * 4 + q) * 16 + c];
       if (i + j < nit && q < m) {
+        const StripItem it = strip_item(first + (i + j) * stride, half_from);
         int p, n0;
-        locate_strip(ps, first + (i + j) * stride, &p, &n0);
-        ps.out[p][int64_t(q) * ps.ldc[p] + n0 + c] = f32_to_bf16_rne(sum);
+        locate_strip(ps, it.strip, &p, &n0);
+        if (c < it.cols) ps.out[p][int64_t(q) * ps.ldc[p] + n0 + it.col0 + c] = f32_to_bf16_rne(sum);
       }
     }
     par ^= 1;
@@ -240,7 +244,7 @@ int launch_gemv(const uint16_t* a, const ProjSet& ps, int m, int k, int total,
                 hipStream_t stream) {
   const int grid = total < num_cus() ? total : num_cus();
   launch(w8a16_persistent_kernel<kGpw>, dim3(grid), dim3(64 * kPWaves), 0, stream, a, ps, m,
-         k, total);
+         k, total, halved_from(total, grid));
   return launch_status();
 }
 
