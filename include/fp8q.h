@@ -57,9 +57,9 @@ int fp8q_time_next_launch(hipEvent_t start, hipEvent_t stop);
 /* Measurement references (not steps of the path): kernels that the path's timings are read
  * against, launched through the same hook.  fp8q_reference_empty enqueues one empty
  * 256-thread block (what a launch costs before any work).  fp8q_reference_stream reads
- * src_bytes (a multiple of 16) from src and writes src_bytes / 2 to dst -- the 2:1
- * read/write mix of the group quantizer and the KV write, with no arithmetic -- over a grid
- * of 4 blocks per CU.  src 16-byte and dst 8-byte aligned device memory.
+ * src_bytes (a multiple of 16) from src (non-temporal 16-byte loads) and writes
+ * src_bytes / 2 to dst -- the 2:1 read/write mix of the group quantizer and the KV write,
+ * with no arithmetic -- over a grid of 4 blocks per CU.  src 16-byte and dst 8-byte aligned device memory.
  * fp8q_reference_lds_stream moves total_bytes from src into LDS the way the prefill GEMM
  * moves its operand tiles (16-byte buffer_load ... lds, 64 KB slices, one 512-thread
  * workgroup per CU, one slice landing while the next is issued, a barrier per slice) and
