@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 #include <new>
@@ -54,6 +55,17 @@ bool scale_in_range(float s) { return s >= 0x1p-64f && s <= 0x1p64f; }
 struct HipCtx {
   int device = -1;
 };
+
+// 64 bytes of page-locked host memory for the freezes' reads, shared by every calibrator of
+// the process (allocated at the first freeze, kept until the process ends; reads take turns).
+std::mutex g_pinned_mu;
+void* g_pinned = nullptr;
+
+// Clears `n` bytes with a kernel rather than a memset node, so that the calibrator's device
+// work holds no memset if a caller ever captures it.
+__global__ __launch_bounds__(64) void zero_bytes_kernel(uint8_t* p, uint64_t n) {
+  for (uint64_t i = threadIdx.x; i < n; i += 64) p[i] = 0;
+}
 
 int hip_device(void* ctx, int32_t* dev) {
   int d = 0;
@@ -89,7 +101,10 @@ int hip_release(void* ctx, void* p, hipStream_t stream, int32_t at_destroy) {
 }
 
 int hip_zero(void*, void* p, uint64_t bytes, hipStream_t stream) {
-  return hipMemsetAsync(p, 0, size_t(bytes), stream) == hipSuccess ? FP8Q_OK : FP8Q_EHIP;
+  if (bytes == 0) return FP8Q_OK;
+  fp8q::launch(zero_bytes_kernel, dim3(1), dim3(64), 0, stream, static_cast<uint8_t*>(p),
+               bytes);
+  return fp8q::launch_status();
 }
 
 int hip_amax_rows(void*, const uint16_t* k, const uint16_t* v, int64_t rows, int64_t elems,
@@ -117,11 +132,17 @@ int hip_stage(void*, const uint16_t* k, const uint16_t* v, const int64_t* slots,
   return fp8q::kv_stage(k, v, slots, rows, elems, ks, vs, dk, dv, dslots, amax2, stream);
 }
 
+// The one blocking read: into page-locked memory (a direct copy, where pageable memory is
+// staged through the runtime's own buffer), then to the caller's memory.
 int hip_read(void*, void* host_dst, const void* src, uint64_t bytes, hipStream_t stream) {
-  if (hipMemcpyAsync(host_dst, src, size_t(bytes), hipMemcpyDeviceToHost, stream) !=
-          hipSuccess ||
+  std::lock_guard<std::mutex> lock(g_pinned_mu);
+  if (bytes <= 64 && !g_pinned && hipHostMalloc(&g_pinned, 64, hipHostMallocDefault) != hipSuccess)
+    g_pinned = nullptr;
+  void* dst = (bytes <= 64 && g_pinned) ? g_pinned : host_dst;
+  if (hipMemcpyAsync(dst, src, size_t(bytes), hipMemcpyDeviceToHost, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)
     return FP8Q_EHIP;
+  if (dst != host_dst) memcpy(host_dst, dst, size_t(bytes));
   return FP8Q_OK;
 }
 
