@@ -458,7 +458,9 @@ int fp8q_kv_calib_create_with_ops(int32_t window_tokens, float headroom,
                                   fp8q_kv_calib** out);
 /* Fold one batch in (see above).  k, v: device bf16 [num_tokens] rows at the target's
  * key/value strides.  Enqueues work on `stream`; blocks only at the freeze, to read the
- * 8-byte running maximum back.  The first staged batch allocates the staging in one piece
+ * 8-byte running maximum back (through 64 bytes of page-locked host memory that the first
+ * freeze of the process allocates and every later one reuses; concurrent freezes take
+ * turns).  The first staged batch allocates the staging in one piece
  * (window * H * D * 2 * 2 + window * 16 bytes, stream-ordered); the freeze releases it in
  * stream order.  With the library's HIP table an in-window observe is one kernel (absmax
  * and staging copy in one pass).
