@@ -54,7 +54,7 @@ def test_split_matches_oracle_deterministic_and_leaves_counts_zero(m, n, k):
 
 
 def test_decode_projection_n1024_with_the_bindings_own_workspace():
-    """The configuration's N = 1024 projection (M = 16, K = 5120) through the workspace the
+    """The decode step's N = 1024 projection (M = 16, K = 5120) through the workspace the
     binding keeps per stream, over several calls with other shapes in between."""
     q, s, wq, ws = _operands(16, 1024, 5120, 2000)
     args = (u8_dev(q), f32_dev(s), u8_dev(wq), f32_dev(ws))
