@@ -352,7 +352,9 @@ __device__ __forceinline__ void fold_block_max(float m, float* amax2, int which,
 }
 
 // max |x| over a packed run of n8 16-byte words; blockIdx.y picks K (0) or V (1).  Four
-// independent 16-byte loads per thread per step keep enough bytes in flight.
+// independent 16-byte loads per thread per step keep enough bytes in flight; the loads carry
+// the non-temporal hint (read once: measured 3-4 % faster than plain loads on the whole pool,
+// where 256- and 512-thread blocks and persistent grids were slower).
 constexpr int kAmaxBlock = 1024;
 constexpr int64_t kAmaxMaxBlocks = 4096;  // per tensor
 __global__ __launch_bounds__(kAmaxBlock) void amax_flat_kernel(const uint4* __restrict__ k,
@@ -364,11 +366,17 @@ __global__ __launch_bounds__(kAmaxBlock) void amax_flat_kernel(const uint4* __re
   const int64_t stride = int64_t(gridDim.x) * kAmaxBlock;
   float m = 0.0f;
   int64_t i = int64_t(blockIdx.x) * kAmaxBlock + threadIdx.x;
+  typedef unsigned v4u_nt __attribute__((ext_vector_type(4)));
+  const v4u_nt* xv = reinterpret_cast<const v4u_nt*>(x);
+  auto ld = [&](int64_t j) {
+    const v4u_nt t = __builtin_nontemporal_load(xv + j);
+    return make_uint4(t[0], t[1], t[2], t[3]);
+  };
   for (; i + 3 * stride < n8; i += 4 * stride) {
-    const uint4 a = x[i], b = x[i + stride], c = x[i + 2 * stride], d = x[i + 3 * stride];
+    const uint4 a = ld(i), b = ld(i + stride), c = ld(i + 2 * stride), d = ld(i + 3 * stride);
     m = fmaxf(m, fmaxf(fmaxf(absmax8(a), absmax8(b)), fmaxf(absmax8(c), absmax8(d))));
   }
-  for (; i < n8; i += stride) m = fmaxf(m, absmax8(x[i]));
+  for (; i < n8; i += stride) m = fmaxf(m, absmax8(ld(i)));
   fold_block_max<kAmaxBlock>(m, amax2, blockIdx.y, seen);
 }
 
