@@ -267,6 +267,48 @@ def test_calibrator_frozen_scale_out_of_range_is_refused_on_the_gpu():
     assert np.array_equal(host(kcd), kc) and np.array_equal(host(vcd), vc)
 
 
+def test_calibrators_freezing_concurrently_on_two_streams_match_the_oracle():
+    """Two calibrators driven from two host threads, each on its own stream, over different
+    batch sequences: their freezes share the process's page-locked read buffer and must each
+    read their own running maximum (scales, counters and pools equal the oracle's)."""
+    import threading
+
+    seqs = [synth.kv_batches(num_tokens_total=synth.KV_WINDOW + 64, seed=seed)[0]
+            for seed in (5040, 5041)]
+    results, errors = [None, None], []
+
+    def drive(idx):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                _, _, kcd, vcd = _pools()
+                cal = fq.KvCalibrator(synth.KV_WINDOW)
+                for b in seqs[idx]:
+                    kd, vd, sd = bf16_dev(b.k), bf16_dev(b.v), i64_dev(b.slots)
+                    cal.observe(kd, vd, H, D, kcd, vcd, sd, BS, cache_stride=CS)
+                    ks, vs = cal.scales()
+                    fq.fp8_kv_write(kd, vd, kcd, vcd, sd, H, D, BS, ks, vs, cache_stride=CS)
+                stream.synchronize()
+                results[idx] = (host(kcd), host(vcd), cal.info())
+                cal.close()
+        except Exception as exc:  # reported by the main thread
+            errors.append(exc)
+
+    threads = [threading.Thread(target=drive, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    for idx in range(2):
+        kc, vc, info = results[idx]
+        kc_ref, vc_ref, ref = _calibrate_oracle(seqs[idx], synth.KV_WINDOW)
+        assert info["frozen"] == 1 and info["replayed_tokens"] == ref["replayed_tokens"]
+        for key in ("k_scale", "v_scale", "k_amax", "v_amax"):
+            assert np.float32(info[key]) == ref[key.replace("amax", "max")], (idx, key)
+        assert np.array_equal(kc, kc_ref) and np.array_equal(vc, vc_ref)
+
+
 # ------------------------------------------------------------------ dequantizing read
 
 
