@@ -135,6 +135,29 @@ def test_grouped_and_strided_match_single_calls_bit_for_bit():
     assert np.all(bf16_host_to_f64(got[:, 6144:]) == -7.0)  # columns past both outputs
 
 
+@pytest.mark.parametrize("m", [1, 4])
+def test_grouped_four_decode_projections_match_single_calls_and_oracle(m):
+    """The four decode projections (2176 strips: the last round runs as 8-column halves on
+    a 256-CU part) in one launch: every output equals its single call bit for bit and the
+    oracle within the bound."""
+    k = synth.DECODE_K
+    a = synth.decode_activation(m, seed=2300 + m)
+    ad = bf16_dev(a)
+    projs, singles = [], []
+    for n in synth.DECODE_N:
+        wq, ws = _weights(n, k, 2100 + n)
+        wq_d, ws_d = u8_dev(wq), f32_dev(ws)
+        projs.append((wq_d, ws_d, None))
+        singles.append((host(fq.w8a16_block_gemv(ad, wq_d, ws_d)), wq, ws))
+    outs = fq.w8a16_block_gemv_grouped(ad, projs)
+    for out, (single, wq, ws) in zip(outs, singles):
+        got = host(out)
+        assert np.array_equal(got, single)
+        ref, mag = oracle.gemm_w8a16(a, wq, ws)
+        ok, worst = _within(got, ref, mag, k)
+        assert ok, f"worst error / bound = {worst:.3f}"
+
+
 def test_strided_output_writes_exactly_its_extent():
     import torch
     k, n, m, ldc = 256, 256, 3, 300
