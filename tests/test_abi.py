@@ -65,6 +65,23 @@ def test_gemm_argument_checks():
     assert lib.w8a8_block_gemm(FAKE, FAKE, FAKE, FAKE, FAKE + 1, 4, 128, 128, 128, None) == EALIGN
 
 
+def test_grouped_launches_take_one_to_eight_projections():
+    """count outside [1, 8] is refused before anything is read or launched, by all three
+    grouped entry points; a NULL projection table is ENULL."""
+    lib = fq.load()
+    projs = (_lib.GemmProj * 9)(*[_lib.GemmProj(FAKE, FAKE, FAKE, 128, 128) for _ in range(9)])
+    for count in (0, 9, -1):
+        assert lib.w8a8_block_gemm_grouped(FAKE, FAKE, projs, count, 4, 128, None) == EINVAL
+        assert lib.fp8_quant_w8a8_gemm_grouped(FAKE, FAKE, FAKE, projs, count, 4, 128,
+                                               None) == EINVAL
+        assert lib.w8a16_block_gemv_grouped(FAKE, projs, count, 2, 128, None) == EINVAL
+    assert lib.w8a8_block_gemm_grouped(FAKE, FAKE, None, 2, 4, 128, None) == ENULL
+    assert lib.w8a16_block_gemv_grouped(FAKE, None, 2, 2, 128, None) == ENULL
+    bad = (_lib.GemmProj * 2)(_lib.GemmProj(FAKE, FAKE, FAKE, 128, 128),
+                              _lib.GemmProj(FAKE, FAKE, FAKE, 100, 128))
+    assert lib.w8a8_block_gemm_grouped(FAKE, FAKE, bad, 2, 4, 128, None) == EINVAL
+
+
 def test_workspace_gemm_and_reference_argument_checks():
     lib = fq.load()
     b = ctypes.c_uint64(7)

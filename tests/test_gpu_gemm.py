@@ -211,6 +211,36 @@ def test_grouped_matches_single_calls_bit_for_bit():
         assert ok, worst
 
 
+def test_eight_projections_in_one_launch_match_single_calls():
+    """The largest grouped launch: 8 projections (288 strips; on a 256-CU part the halved last
+    round spans the last two of them). W8A8 grouped, the fused quantize + GEMM and the W8A16
+    grouped launch each equal their single calls bit for bit; the W8A8 outputs are within
+    tolerance of the oracle."""
+    widths = (1024, 1024, 512, 512, 512, 512, 256, 256)
+    k, m = synth.DECODE_K, 4
+    a = synth.decode_activation(m, seed=2400)
+    ad = bf16_dev(a)
+    q, s = fq.fp8_group_quant(ad)
+    q_ref, s_ref = oracle.group_quant(a)
+    ws_all, singles, singles16 = [], [], []
+    for i, n in enumerate(widths):
+        wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=2500 + i))
+        wq_d, ws_d = u8_dev(wq), f32_dev(ws)
+        ws_all.append((wq, ws, wq_d, ws_d))
+        singles.append(host(fq.w8a8_block_gemm(q, s, wq_d, ws_d)))
+        singles16.append(host(fq.w8a16_block_gemv(ad, wq_d, ws_d)))
+    projs = [(wq_d, ws_d, None) for _, _, wq_d, ws_d in ws_all]
+    grouped = [host(o) for o in fq.w8a8_block_gemm_grouped(q, s, projs)]
+    fused = [host(o) for o in fq.fp8_quant_w8a8_gemm_grouped(ad, projs)]
+    g16 = [host(o) for o in fq.w8a16_block_gemv_grouped(ad, projs)]
+    for i, (wq, ws, _, _) in enumerate(ws_all):
+        assert np.array_equal(grouped[i], singles[i]), i
+        assert np.array_equal(fused[i], singles[i]), i
+        assert np.array_equal(g16[i], singles16[i]), i
+        ok, worst = gemm_tolerance_ok(grouped[i], oracle.gemm(q_ref, s_ref, wq, ws))
+        assert ok, (i, worst)
+
+
 def test_grouped_strided_outputs_into_one_buffer():
     """Q/K/V-style: three projections written side by side into one [m, ldc] buffer."""
     m, k = 9, 1024
