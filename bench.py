@@ -96,9 +96,11 @@ def kv_amax_bytes(t, e=KV_H * KV_D):
 
 def prefill_copy_bytes(m, n, k, cus):
     """Bytes the prefill GEMM moves from global memory into LDS per launch: every output tile
-    copies its activation and weight tile of each 128-wide group plus 1 KB of scales (the
-    launch rule of w8a8_block_gemm_prefill: 256 x 256 tiles, the last round's tiles split
-    into two 256 x 128 halves when it would leave half the CUs idle; else 128 x 128 tiles)."""
+    copies its activation and weight tile of each 128-wide group, plus 1 KB of scales when
+    the scales go through LDS (the launch rule of w8a8_block_gemm_prefill: 256 x 256 tiles,
+    the last round's tiles split into two 256 x 128 halves when it would leave half the CUs
+    idle, the scales loaded into registers when the group count is a multiple of eight;
+    else 128 x 128 tiles)."""
     g = k // 128
     big_m, big_n = -(-m // 256), -(-n // 256)
     big = big_m * big_n
@@ -106,7 +108,8 @@ def prefill_copy_bytes(m, n, k, cus):
         tail = big % cus
         split = tail if (tail and 2 * tail <= cus) else 0
         whole = big - split
-        return g * (whole * (2 * 256 * 128 + 1024) + split * 2 * (256 * 128 + 128 * 128 + 1024))
+        scales = 0 if g % 8 == 0 else 1024
+        return g * (whole * (2 * 256 * 128 + scales) + split * 2 * (256 * 128 + 128 * 128 + scales))
     tiles = -(-m // 128) * -(-n // 128)
     return g * tiles * (2 * 128 * 128 + 512)
 

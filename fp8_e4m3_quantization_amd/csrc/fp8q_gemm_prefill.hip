@@ -7,12 +7,12 @@
 // (E4M3 activations with per-token 1x128 FP32 scales times E4M3 weights with 128x128 FP32
 // block scales, FP32 epilogue).
 //
-// Both kernels walk K one 128-wide group at a time; one v_mfma_f32_16x16x128_f8f6f4 covers
+// The kernels walk K one 128-wide group at a time; one v_mfma_f32_16x16x128_f8f6f4 covers
 // one group of a 16 x 16 output tile, so every instruction's result is one group's partial
 // and takes its scale a_scale[row, g] * w_scale[col/128, g] in one FMA per element.  The
 // operand tiles of each group are copied global -> LDS by the buffer unit itself
-// (buffer_load ... lds: no staging registers, no LDS store instructions) into one of two
-// stages, the next group's copies landing while the current group multiplies.
+// (buffer_load ... lds: no staging registers, no LDS store instructions), the next groups'
+// copies landing while the current group multiplies.
 //
 // tile256 (the large shapes): one 512-thread workgroup per CU owns a 256 x 256 output tile,
 // wave (wm, wn) of the 4 x 2 grid 64 x 128 of it (4 x 8 MFMA tiles).  A 256 x 256 tile
@@ -22,11 +22,16 @@
 // weight fragment is read and column c - 1's products are scaled while column c
 // multiplies, one group of four FMAs between MFMAs; after each group's barrier only B_0
 // and the first two activation fragments are read before the first MFMA, each later
-// fragment an MFMA ahead of its use.
-// Both scales come from LDS (the weight block scale rides in the activation-scale copy),
-// so no scalar load shares the LDS reads' wait counter.  When the tile count leaves the last
-// round of workgroups at most half full, each of those last tiles is split into two
-// 256 x 128 halves (wave tiles 64 x 64): twice as many work items, each half as long.
+// fragment an MFMA ahead of its use.  When the tile count leaves the last round of
+// workgroups at most half full, each of those last tiles is split into two 256 x 128 halves
+// (wave tiles 64 x 64): twice as many work items, each half as long.  Two forms:
+//  - ring (group count a multiple of eight): five 32 KB LDS slots in rotation, each weight
+//    tile copied two groups ahead and each activation tile one; the scales go to
+//    registers (no LDS is left), the weight scale by a scalar load issued after the
+//    step's last LDS read.  It hides the copies that miss L2 better than two stages.
+//  - two_stage (any group count): two stages of both operand tiles and the scales (the
+//    weight block scale rides in the activation-scale copy), one group ahead.
+// Results are the same bit for bit: the same products, scaled and summed in the same order.
 //
 // tile128 (fewer than half a round of 256 x 256 tiles, e.g. a 1024-column projection):
 // 256-thread workgroups, two per CU, each a 128 x 128 tile (2 x 2 waves of 64 x 64).
@@ -71,26 +76,393 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base,
 namespace tile256 {
 
 constexpr int kBM = 256, kBN = 256, kThreads = 512;
-constexpr int kCPitch = kBN + 8;          // bf16 elements per staged output row
-constexpr int kSlab = 64 * kCPitch * 2;   // 64 staged output rows (bytes)
-static_assert(kSlab >= kBM * 128, "a stage array holds one operand tile of one group");
+constexpr int kArr = kBM * 128;           // one operand tile of one group (bytes)
+constexpr int kCPitch = kBN;              // bf16 elements per staged output row
+static_assert(64 * kCPitch * 2 == kArr, "an operand array holds 64 staged output rows");
 constexpr int kGroupM = 4;                // row tiles per column tile in the walk order
 
-// Two LDS stages.  The operand arrays are padded to kSlab so that the four of them also
-// hold the four 64-row slabs of the staged bf16 output tile.  They are separate objects:
-// the compiler can then see that a stage's operand reads never alias the copies landing
-// in the other stage, and keeps those copies in flight.
-struct Stages {
-  uint8_t (&a0)[kSlab];
-  uint8_t (&a1)[kSlab];
-  uint8_t (&b0)[kSlab];
-  uint8_t (&b1)[kSlab];
-  float (&s0)[kBM + 32];
-  float (&s1)[kBM + 32];
+// Work item -> output tile origin.  Items [0, n_full) are whole tiles, the rest the two
+// halves (half 0 or 1: columns n0 .. n0 + 127) of each of the last tiles of the walk order;
+// half is -1 for a whole tile.  The walk takes kGroupM consecutive row tiles per column
+// tile, and each XCD (workgroup ids are dealt to the 8 XCDs round-robin) a contiguous
+// stretch of it.
+struct TileOrigin {
+  int m0, n0, half;
+};
+__device__ __forceinline__ TileOrigin walk_tile(int item, int tiles_m, int tiles_n, int n_full) {
+  int tile = item, half = -1;
+  if (item < n_full) {
+    const int even = n_full - n_full % kXcds;
+    if (item < even) tile = (item % kXcds) * (even / kXcds) + item / kXcds;
+  } else {
+    tile = n_full + (item - n_full) / 2;
+    half = (item - n_full) & 1;
+  }
+  const int band = kGroupM * tiles_n;
+  const int first_m = (tile / band) * kGroupM;
+  const int band_m = min(kGroupM, tiles_m - first_m);
+  const int tm = first_m + (tile % band) % band_m;
+  const int tn = (tile % band) / band_m;
+  return {tm * kBM, tn * kBN + (half > 0 ? 128 : 0), half};
+}
+
+// Staged 128-byte operand row r keeps its 16-byte chunk c at slot c ^ (r & 7) ^ (bit 3 of
+// r): an operand read takes one chunk from 16 consecutive rows per 16 lanes, which land on
+// 16 distinct bank groups.  Fragment row 64 wm + 16 i + orow (or kWaveCols wn + 16 c +
+// orow) has the swizzle of row orow, so every read is one of four lane offsets plus a
+// constant.  A 1 KB copy block (8 rows) is one copy instruction: lane L of block b loads
+// row 8b + L/8, chunk (L % 8) ^ (L / 8) ^ (b & 1), which the swizzle places at byte
+// b * 1024 + 16 L.
+struct Frag {
+  int a_lo, a_hi, b_lo, b_hi;
+};
+__device__ __forceinline__ Frag frag_offsets(int lane, int wm, int wn, int wave_cols) {
+  const int orow = lane & 15, oh = lane >> 4;
+  const int sw = (orow & 7) ^ ((orow >> 3) & 1);
+  return {(wm * 64 + orow) * 128 + (((2 * oh) ^ sw) << 4),
+          (wm * 64 + orow) * 128 + (((2 * oh + 1) ^ sw) << 4),
+          (wn * wave_cols + orow) * 128 + (((2 * oh) ^ sw) << 4),
+          (wn * wave_cols + orow) * 128 + (((2 * oh + 1) ^ sw) << 4)};
+}
+
+// The 32 operand bytes of one MFMA fragment: chunks at byte offsets lo and hi of p.
+__device__ __forceinline__ v8i ld32(const uint8_t* p, int lo, int hi) {
+  const v4u x = *reinterpret_cast<const v4u*>(p + lo);
+  const v4u y = *reinterpret_cast<const v4u*>(p + hi);
+  v8i r;
+  r[0] = int(x[0]); r[1] = int(x[1]); r[2] = int(x[2]); r[3] = int(x[3]);
+  r[4] = int(y[0]); r[5] = int(y[1]); r[6] = int(y[2]); r[7] = int(y[3]);
+  return r;
+}
+
+// Each MFMA takes the weight fragment as its first operand, so its 16 x 16 result is the
+// transposed tile: element j of lane (oh, orow) in row tile i is row 16 i + orow of the
+// wave's 64 and column 4 oh + j of the 16 -- one activation scale per lane and row tile.
+//
+// The bf16 output tile is staged through four operand arrays (rows 64 s .. 64 s + 63 in
+// array s; row r's 8-column blocks XOR-permuted by bits 0..3 of r, so that the 16 rows one
+// 8-byte store instruction writes land on distinct bank groups), then written out in
+// 16-byte row pieces.  Called after a barrier that ends every operand read.
+template <int kCols>
+__device__ __forceinline__ void store_tile(const v4f (&acc)[4][kCols], uint8_t* s0, uint8_t* s1,
+                                           uint8_t* s2, uint8_t* s3, uint16_t* __restrict__ out,
+                                           int m, int n, int ldc, int vec_out, int m0, int n0) {
+  constexpr int kWaveCols = 16 * kCols, kTileCols = 2 * kWaveCols;
+  const int t = int(threadIdx.x), lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int orow = lane & 15, oh = lane >> 4;
+  auto slab = [&](int s) -> uint8_t* { return s == 0 ? s0 : s == 1 ? s1 : s == 2 ? s2 : s3; };
+  {
+    uint16_t* so = reinterpret_cast<uint16_t*>(slab(wm));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < kCols; ++c) {
+        const int r = i * 16 + orow;
+        const int col = (wn * kWaveCols + c * 16 + 4 * oh) ^ (orow << 3);
+        const uint32_t lo = uint32_t(f32_to_bf16_rne(acc[i][c][0])) |
+                            (uint32_t(f32_to_bf16_rne(acc[i][c][1])) << 16);
+        const uint32_t hi = uint32_t(f32_to_bf16_rne(acc[i][c][2])) |
+                            (uint32_t(f32_to_bf16_rne(acc[i][c][3])) << 16);
+        *reinterpret_cast<uint2*>(so + r * kCPitch + col) = make_uint2(lo, hi);
+      }
+  }
+  __syncthreads();
+  constexpr int kRowChunks = kTileCols / 8;  // 16-byte chunks per output row
+#pragma unroll 4
+  for (int q = 0; q < kBM * kRowChunks / kThreads; ++q) {
+    const int ch = t + kThreads * q, r = ch / kRowChunks, cc = (ch % kRowChunks) * 8;
+    const int gm = m0 + r, gn = n0 + cc;
+    if (gm < m && gn < n) {
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(slab(r >> 6)) +
+                            (r & 63) * kCPitch + (cc ^ ((r & 15) << 3));
+      uint16_t* dst = out + int64_t(gm) * ldc + gn;
+      if (vec_out) {
+        *reinterpret_cast<v4u*>(dst) = *reinterpret_cast<const v4u*>(src);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[e] = src[e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Five-slot ring (group counts that are a multiple of eight).
+//
+// LDS: five 32 KB slots, each a separate array (160 KB, all of it).  Step g multiplies the
+// activation tile and the weight tile of group g from two slots while the weight tile of
+// group g + 1 lands in a third, and copies the activation tile of group g + 1 and the
+// weight tile of group g + 2 into the two slots that group g - 1 used: a weight copy has
+// two steps to land, an activation copy one.  The slots rotate with a period of eight
+// steps: activation groups 8t + j sit in slots 4 3 4 1 4 0 4 2 and weight groups in slots
+// 0 1 2 0 3 2 1 3, so that the two activation groups and three weight groups of any step
+// sit in five distinct slots.  Separate objects let the compiler see that a slot's operand
+// reads never alias the copies landing in the others, so it keeps those copies in flight.
+// The scales have no LDS left: each wave loads them into registers.
+namespace ring {
+
+// One group's scales as one lane holds them: the activation scale of row 64 wm + lane of
+// the tile and the weight block scale of the wave's column block (uniform: a scalar).
+struct Scales {
+  float row, w;
+};
+
+struct Slots {
+  uint8_t (&x0)[kArr];
+  uint8_t (&x1)[kArr];
+  uint8_t (&x2)[kArr];
+  uint8_t (&x3)[kArr];
+  uint8_t (&x4)[kArr];
 };
 
 // One output tile: rows [m0, m0 + 256) x columns [n0, n0 + 32 kCols), kCols = 8 (256
 // columns, wave tiles 64 x 128) or 4 (128 columns, wave tiles 64 x 64).
+template <int kCols>
+__device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
+                                             const float* __restrict__ a_scale,
+                                             const uint8_t* __restrict__ w_q,
+                                             const float* __restrict__ w_scale,
+                                             uint16_t* __restrict__ out, int m, int n, int k,
+                                             int ldc, int vec_out, int m0, int n0,
+                                             const Slots& st) {
+  constexpr int kWaveCols = 16 * kCols;   // columns per wave
+  constexpr int kTileCols = 2 * kWaveCols;
+  constexpr int kBBlocks = kTileCols / 8 / 8;  // 1 KB weight copy blocks per wave per group
+  const int t = int(threadIdx.x), lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1;  // rows 64 wm .., columns kWaveCols * wn ..
+  const int groups = k >> 7;
+
+  const __amdgpu_buffer_rsrc_t ra_rsrc = tile_rsrc(a_q, m0, m, k, kBM);
+  const __amdgpu_buffer_rsrc_t rb_rsrc = tile_rsrc(w_q, n0, n, k, kTileCols);
+  const __amdgpu_buffer_rsrc_t none_rsrc = tile_rsrc(a_q, 0, 0, k, 0);
+  // Scales: the wave's 64 activation rows (rows past m read as zeros) as a [rows, groups]
+  // FP32 matrix, and the weight block row of its columns.  (readfirstlane: the descriptor
+  // must be seen as uniform, or each load becomes a loop.)
+  const int srow0 = __builtin_amdgcn_readfirstlane(min(m0 + 64 * wm, m));
+  const int srows = __builtin_amdgcn_readfirstlane(min(m - srow0, 64));
+  const __amdgpu_buffer_rsrc_t rs_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(a_scale + int64_t(srow0) * groups), 0, srows * groups * 4,
+      kBufferDword3);
+  const int rs_off = lane * groups * 4;
+  const int wrow =
+      __builtin_amdgcn_readfirstlane(min((n0 + kWaveCols * wn) >> 7, (n >> 7) - 1));
+  const float* __restrict__ wsp = w_scale + int64_t(wrow) * groups;
+  // Copy block w + 8q of an operand is block w's offset plus 64 q rows; the sum is formed
+  // at each copy from an opaque copy of block w's, so it costs one add, not a live register.
+  const int voff0 =
+      (8 * wave + (lane >> 3)) * k + (((lane & 7) ^ (lane >> 3) ^ (wave & 1)) << 4);
+  auto voff = [&](int q) {
+    int v = voff0;
+    asm volatile("" : "+v"(v));
+    return v + q * 64 * k;
+  };
+
+  // The copies of a step, in pieces: j < 4 the activation blocks of group ga, then its
+  // row scales, then the kBBlocks weight blocks of group gb, then the weight scale of group
+  // ga (a scalar load, issued where the step has no LDS read left to wait for: scalar and
+  // LDS loads share a wait counter).  Past the last group the operand copies read a
+  // zero-size buffer (zeros written, no memory traffic) and the scale loads repeat the last
+  // group.  Every copy is unconditional: a branch here would split the step and let the
+  // compiler sink its FMAs past the next barrier.
+  constexpr int kPieces = 4 + 1 + kBBlocks + 1;
+  auto copy_piece = [&](uint8_t* sa, uint8_t* sb, Scales& sc, int ga, int gb, int j) {
+    if (j < 4) {
+      const bool live = ga < groups;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? ra_rsrc : none_rsrc,
+                                               (lds_void*)(sa + (wave + 8 * j) * 1024), 16,
+                                               voff(j), live ? ga * 128 : 0, 0, 0);
+    } else if (j == 4) {
+      sc.row = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(rs_rsrc, rs_off,
+                                                      min(ga, groups - 1) * 4, 0));
+    } else if (j < 5 + kBBlocks) {
+      const bool live = gb < groups;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rb_rsrc : none_rsrc,
+                                               (lds_void*)(sb + (wave + 8 * (j - 5)) * 1024),
+                                               16, voff(j - 5), live ? gb * 128 : 0, 0, 0);
+    } else {
+      sc.w = wsp[min(ga, groups - 1)];
+    }
+  };
+
+  v4f acc[4][kCols];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) acc[i][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const Frag fo = frag_offsets(lane, wm, wn, kWaveCols);
+  const int sel = (lane & 15) * 4;  // lane 16 i + orow holds row 16 i + orow's scale
+
+  // Wait for this wave's copies of group g and its scales (everything but the previous
+  // step's weight copies of group g + 1), then the barrier: everyone's copies of group g
+  // landed and everyone is done reading the slots the next copies go to.  No fence: it
+  // would drain the copies still in flight.  (vmcnt in bits 3:0 and 15:14, lgkmcnt 0,
+  // expcnt not waited for.)
+  constexpr int kWait = (kBBlocks & 15) | (7 << 4) | ((kBBlocks >> 4) << 14);
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWait);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Group g from slots (sa, sb) with scales sc; the activation copies and scales of group
+  // g + 1 go to (na, nsc) and the weight copies of group g + 2 to nb, slots that held group
+  // g - 1 (read by everyone before the barrier).  The copies are dealt out over the first
+  // half of the step's MFMAs, one piece after each, rather than issued in one burst ahead
+  // of them (the burst queues in the address unit and holds back the MFMAs that follow it
+  // in the wave's instruction stream).  Column 0 starts once B_0, A_0 and A_1 are in: each
+  // later fragment is read one MFMA ahead of its use; the column loop is software-
+  // pipelined (column c + 1's weight fragment read and column c - 1's products scaled
+  // while column c multiplies, MFMA and four FMAs alternating).
+  auto step = [&](int g, const uint8_t* sa, const uint8_t* sb, const Scales& sc, uint8_t* na,
+                  uint8_t* nb, Scales& nsc) {
+    barrier();
+    // Opaque copies of the fragment offsets: the addresses below are formed from them
+    // within the step (one add per slot, the rest in the instruction's offset field)
+    // instead of being hoisted out of the loop as one live register per slot and fragment.
+    int alo = fo.a_lo, ahi = fo.a_hi, blo = fo.b_lo, bhi = fo.b_hi;
+    asm volatile("" : "+v"(alo), "+v"(ahi), "+v"(blo), "+v"(bhi));
+    copy_piece(na, nb, nsc, g + 1, g + 2, 0);
+    v8i af[4];
+    v4f pcur[4], pprev[4];
+    v8i bcur = ld32(sb, blo, bhi);
+    af[0] = ld32(sa, alo, ahi);
+    af[1] = ld32(sa + 2048, alo, ahi);
+    __builtin_amdgcn_sched_barrier(0);
+    pcur[0] = mfma_group(bcur, af[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_piece(na, nb, nsc, g + 1, g + 2, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    af[2] = ld32(sa + 2 * 2048, alo, ahi);
+    __builtin_amdgcn_sched_barrier(0);
+    pcur[1] = mfma_group(bcur, af[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_piece(na, nb, nsc, g + 1, g + 2, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    af[3] = ld32(sa + 3 * 2048, alo, ahi);
+    __builtin_amdgcn_sched_barrier(0);
+    pcur[2] = mfma_group(bcur, af[2]);
+    __builtin_amdgcn_sched_barrier(0);
+    copy_piece(na, nb, nsc, g + 1, g + 2, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    v8i bnxt = ld32(sb + 2048, blo, bhi);
+    // the four row scales of this lane, times the weight scale (one product per row and
+    // group, as the definition scales each group's partial)
+    const int rsw = __builtin_bit_cast(int, sc.row * sc.w);
+    int sel_here = sel;  // (opaque: one address register, the rest in the offset field)
+    asm volatile("" : "+v"(sel_here));
+    float f[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f[i] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(sel_here + 64 * i, rsw));
+    __builtin_amdgcn_sched_barrier(0);
+    pcur[3] = mfma_group(bcur, af[3]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pprev[i] = pcur[i];
+    bcur = bnxt;
+#pragma unroll
+    for (int c = 1; c <= kCols; ++c) {
+      // (the last piece, the scalar load, waits for the last column: every LDS read of the
+      // step is issued and waited for by then)
+      if (3 + c < kPieces - 1) copy_piece(na, nb, nsc, g + 1, g + 2, 3 + c);
+      if (c == kCols) copy_piece(na, nb, nsc, g + 1, g + 2, kPieces - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      bnxt = bcur;
+      if (c + 1 < kCols) bnxt = ld32(sb + (c + 1) * 2048, blo, bhi);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (c < kCols) pcur[i] = mfma_group(bcur, af[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][c - 1][j] = __builtin_fmaf(pprev[i][j], f[i], acc[i][c - 1][j]);
+      }
+      if (c < kCols) {  // MFMA, its neighbour's four FMAs, MFMA, ...
+        if (c + 1 < kCols) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pprev[i] = pcur[i];
+      bcur = bnxt;
+    }
+  };
+
+  // Prologue: the activation copies and scales of group 0 and the weight copies of groups
+  // 0 and 1, in issue order (the barrier's wait count assumes it, so no load may move).
+  Scales s0, s1;
+#pragma unroll
+  for (int j = 0; j < kPieces; ++j) {
+    copy_piece(st.x4, st.x0, s0, 0, 0, j);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int j = 5; j < 5 + kBBlocks; ++j) {
+    copy_piece(st.x4, st.x1, s0, 0, 1, j);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int g = 0;
+  do {  // (do-while: a guard before the first trip would let the prologue's loads sink)
+    step(g, st.x4, st.x0, s0, st.x3, st.x2, s1);
+    step(g + 1, st.x3, st.x1, s1, st.x4, st.x0, s0);
+    step(g + 2, st.x4, st.x2, s0, st.x1, st.x3, s1);
+    step(g + 3, st.x1, st.x0, s1, st.x4, st.x2, s0);
+    step(g + 4, st.x4, st.x3, s0, st.x0, st.x1, s1);
+    step(g + 5, st.x0, st.x2, s1, st.x4, st.x3, s0);
+    step(g + 6, st.x4, st.x1, s0, st.x2, st.x0, s1);
+    step(g + 7, st.x2, st.x3, s1, st.x4, st.x1, s0);
+    g += 8;
+  } while (g < groups);
+  __syncthreads();  // every copy landed and every wave is done reading the slots
+  store_tile<kCols>(acc, st.x0, st.x1, st.x2, st.x3, out, m, n, ldc, vec_out, m0, n0);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void w8a8_prefill_ring_kernel(
+    const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale,
+    const uint8_t* __restrict__ w_q, const float* __restrict__ w_scale,
+    uint16_t* __restrict__ out, int m, int n, int k, int ldc, int tiles_m, int tiles_n,
+    int n_full, int vec_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t x0[kArr], x1[kArr], x2[kArr], x3[kArr],
+      x4[kArr];
+  const Slots st{x0, x1, x2, x3, x4};
+  const TileOrigin o = walk_tile(int(blockIdx.x), tiles_m, tiles_n, n_full);
+  if (o.half < 0)
+    prefill_tile<8>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0, o.n0, st);
+  else
+    prefill_tile<4>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0, o.n0, st);
+}
+
+}  // namespace ring
+
+// ---------------------------------------------------------------------------------------
+// Two stages (any group count).
+//
+// Each stage holds one group's activation and weight tiles and its scales; group g
+// multiplies from one while the copies of group g + 1 land in the other.  The operand
+// arrays are separate objects: the compiler can then see that a stage's operand reads
+// never alias the copies landing in the other stage, and keeps those copies in flight.
+namespace two_stage {
+
+struct Stages {
+  uint8_t (&a0)[kArr];
+  uint8_t (&a1)[kArr];
+  uint8_t (&b0)[kArr];
+  uint8_t (&b1)[kArr];
+  float (&s0)[kBM + 32];
+  float (&s1)[kBM + 32];
+};
+
 template <int kCols>
 __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
                                              const float* __restrict__ a_scale,
@@ -110,9 +482,7 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
   const __amdgpu_buffer_rsrc_t ra_rsrc = tile_rsrc(a_q, m0, m, k, kBM);
   const __amdgpu_buffer_rsrc_t rb_rsrc = tile_rsrc(w_q, n0, n, k, kTileCols);
   const __amdgpu_buffer_rsrc_t none_rsrc = tile_rsrc(a_q, 0, 0, k, 0);
-  // 1 KB copy blocks (8 rows each): wave w fills blocks w + 8q of each operand; lane L of
-  // block b loads row 8b + L/8, chunk (L % 8) ^ (L / 8) ^ (b & 1), which the swizzle below
-  // places at byte b * 1024 + 16 L
+  // wave w fills copy blocks w + 8q of each operand
   int voff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -156,74 +526,52 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
 #pragma unroll
     for (int c = 0; c < kCols; ++c) acc[i][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Staged 128-byte row r keeps its 16-byte chunk c at slot c ^ (r & 7) ^ (bit 3 of r): an
-  // operand read takes one chunk from 16 consecutive rows per 16 lanes, which land on 16
-  // distinct bank groups.  Fragment row 64 wm + 16 i + orow (or kWaveCols wn + 16 c + orow)
-  // has the swizzle of row orow, so every read is one of four lane offsets plus a constant.
-  const int orow = lane & 15, oh = lane >> 4;
-  const int sw = (orow & 7) ^ ((orow >> 3) & 1);
-  const int a_lo = (wm * 64 + orow) * 128 + (((2 * oh) ^ sw) << 4);
-  const int a_hi = (wm * 64 + orow) * 128 + (((2 * oh + 1) ^ sw) << 4);
-  const int b_lo = (wn * kWaveCols + orow) * 128 + (((2 * oh) ^ sw) << 4);
-  const int b_hi = (wn * kWaveCols + orow) * 128 + (((2 * oh + 1) ^ sw) << 4);
-  const int s_off = (wm * 64 + oh * 4) * 4;
-  auto ld32 = [&](const uint8_t* p, int lo, int hi) {
-    const v4u x = *reinterpret_cast<const v4u*>(p + lo);
-    const v4u y = *reinterpret_cast<const v4u*>(p + hi);
-    v8i r;
-    r[0] = int(x[0]); r[1] = int(x[1]); r[2] = int(x[2]); r[3] = int(x[3]);
-    r[4] = int(y[0]); r[5] = int(y[1]); r[6] = int(y[2]); r[7] = int(y[3]);
-    return r;
-  };
+  const Frag fo = frag_offsets(lane, wm, wn, kWaveCols);
+  const int s_off = (wm * 64 + (lane & 15)) * 4;  // row 64 wm + orow's scale slot
 
   // Group g from stage (sa, sb, ss); the copies of group g + 1 go to (na, nbs, ns), which
   // held group g - 1 (read by everyone before the barrier).  The copies are dealt out over
-  // the first half of the step's MFMAs, one piece after each, rather than issued in one
-  // burst ahead of them (the burst queues in the address unit and holds back the MFMAs
-  // that follow it in the wave's instruction stream).
+  // the first half of the step's MFMAs, one piece after each, as in the ring.
   auto step = [&](int g, const uint8_t* sa, const uint8_t* sb, const float* ss, uint8_t* na,
                   uint8_t* nbs, float* ns) {
     __syncthreads();  // everyone's copies of group g landed (the fence drains them)
     copy_piece(na, nbs, ns, g + 1, 0);
-    // Column 0 starts once B_0, A_0 and A_1 are in: each later fragment is read one MFMA
-    // ahead of its use, the scales last (their first use is column 0's FMAs, in column 1).
     v8i af[4];
-    float4 as[4];
+    float as[4];
     v4f pcur[4], pprev[4];
-    v8i bcur = ld32(sb, b_lo, b_hi);
-    af[0] = ld32(sa, a_lo, a_hi);
-    af[1] = ld32(sa + 2048, a_lo, a_hi);
+    v8i bcur = ld32(sb, fo.b_lo, fo.b_hi);
+    af[0] = ld32(sa, fo.a_lo, fo.a_hi);
+    af[1] = ld32(sa + 2048, fo.a_lo, fo.a_hi);
     __builtin_amdgcn_sched_barrier(0);
-    pcur[0] = mfma_group(af[0], bcur);
+    pcur[0] = mfma_group(bcur, af[0]);
     __builtin_amdgcn_sched_barrier(0);
     copy_piece(na, nbs, ns, g + 1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    af[2] = ld32(sa + 2 * 2048, a_lo, a_hi);
+    af[2] = ld32(sa + 2 * 2048, fo.a_lo, fo.a_hi);
     __builtin_amdgcn_sched_barrier(0);
-    pcur[1] = mfma_group(af[1], bcur);
+    pcur[1] = mfma_group(bcur, af[1]);
     __builtin_amdgcn_sched_barrier(0);
     copy_piece(na, nbs, ns, g + 1, 2);
     __builtin_amdgcn_sched_barrier(0);
-    af[3] = ld32(sa + 3 * 2048, a_lo, a_hi);
+    af[3] = ld32(sa + 3 * 2048, fo.a_lo, fo.a_hi);
     __builtin_amdgcn_sched_barrier(0);
-    pcur[2] = mfma_group(af[2], bcur);
+    pcur[2] = mfma_group(bcur, af[2]);
     __builtin_amdgcn_sched_barrier(0);
     copy_piece(na, nbs, ns, g + 1, 3);
     __builtin_amdgcn_sched_barrier(0);
-    v8i bnxt = ld32(sb + 2048, b_lo, b_hi);
+    v8i bnxt = ld32(sb + 2048, fo.b_lo, fo.b_hi);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      as[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(ss) + s_off +
-                                               i * 64);
+      as[i] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(ss) + s_off +
+                                              i * 64);
     const float ws = ss[kBM + wn];
     __builtin_amdgcn_sched_barrier(0);
-    pcur[3] = mfma_group(af[3], bcur);
+    pcur[3] = mfma_group(bcur, af[3]);
     __builtin_amdgcn_sched_barrier(0);
-    float f[4][4];
+    float f[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      f[i][0] = as[i].x * ws; f[i][1] = as[i].y * ws; f[i][2] = as[i].z * ws;
-      f[i][3] = as[i].w * ws;
+      f[i] = as[i] * ws;
       pprev[i] = pcur[i];
     }
     bcur = bnxt;
@@ -232,24 +580,20 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
       if (3 + c < kPieces) copy_piece(na, nbs, ns, g + 1, 3 + c);
       __builtin_amdgcn_sched_barrier(0);
       bnxt = bcur;
-      if (c + 1 < kCols) bnxt = ld32(sb + (c + 1) * 2048, b_lo, b_hi);
+      if (c + 1 < kCols) bnxt = ld32(sb + (c + 1) * 2048, fo.b_lo, fo.b_hi);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (c < kCols) pcur[i] = mfma_group(af[i], bcur);
-        acc[i][c - 1][0] = __builtin_fmaf(pprev[i][0], f[i][0], acc[i][c - 1][0]);
-        acc[i][c - 1][1] = __builtin_fmaf(pprev[i][1], f[i][1], acc[i][c - 1][1]);
-        acc[i][c - 1][2] = __builtin_fmaf(pprev[i][2], f[i][2], acc[i][c - 1][2]);
-        acc[i][c - 1][3] = __builtin_fmaf(pprev[i][3], f[i][3], acc[i][c - 1][3]);
+        if (c < kCols) pcur[i] = mfma_group(bcur, af[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][c - 1][j] = __builtin_fmaf(pprev[i][j], f[i], acc[i][c - 1][j]);
       }
       if (c < kCols) {  // MFMA, its neighbour's four FMAs, MFMA, ...
         if (c + 1 < kCols) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (c == 1)
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-          else
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -269,75 +613,25 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
     step(g + 1, st.a1, st.b1, st.s1, st.a0, st.b0, st.s0);
   }
   __syncthreads();  // every copy landed and every wave is done reading the stages
-
-  // output rows 64 s .. 64 s + 63 are staged in operand array s
-  auto slab = [&](int s) -> uint8_t* {
-    return s == 0 ? st.a0 : s == 1 ? st.a1 : s == 2 ? st.b0 : st.b1;
-  };
-  {
-    uint16_t* sc = reinterpret_cast<uint16_t*>(slab(wm));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int c = 0; c < kCols; ++c)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = i * 16 + oh * 4 + j;
-          const int col = wn * kWaveCols + c * 16 + (lane & 15);
-          sc[r * kCPitch + col] = f32_to_bf16_rne(acc[i][c][j]);
-        }
-  }
-  __syncthreads();
-  constexpr int kRowChunks = kTileCols / 8;  // 16-byte chunks per output row
-#pragma unroll 4
-  for (int q = 0; q < kBM * kRowChunks / kThreads; ++q) {
-    const int ch = t + kThreads * q, r = ch / kRowChunks, cc = (ch % kRowChunks) * 8;
-    const int gm = m0 + r, gn = n0 + cc;
-    if (gm < m && gn < n) {
-      const uint16_t* src =
-          reinterpret_cast<const uint16_t*>(slab(r >> 6)) + (r & 63) * kCPitch + cc;
-      uint16_t* dst = out + int64_t(gm) * ldc + gn;
-      if (vec_out) {
-        *reinterpret_cast<v4u*>(dst) = *reinterpret_cast<const v4u*>(src);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dst[e] = src[e];
-      }
-    }
-  }
+  store_tile<kCols>(acc, st.a0, st.a1, st.b0, st.b1, out, m, n, ldc, vec_out, m0, n0);
 }
 
-// Work item b: items [0, n_full) are whole tiles, the rest are the two halves of each of
-// the last tiles of the walk order.
 __global__ __launch_bounds__(kThreads, 1) void w8a8_prefill_kernel(
     const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale,
     const uint8_t* __restrict__ w_q, const float* __restrict__ w_scale,
     uint16_t* __restrict__ out, int m, int n, int k, int ldc, int tiles_m, int tiles_n,
     int n_full, int vec_out) {
-  __shared__ __attribute__((aligned(16))) uint8_t a0[kSlab], a1[kSlab], b0[kSlab], b1[kSlab];
+  __shared__ __attribute__((aligned(16))) uint8_t a0[kArr], a1[kArr], b0[kArr], b1[kArr];
   __shared__ __attribute__((aligned(16))) float s0[kBM + 32], s1[kBM + 32];
   const Stages st{a0, a1, b0, b1, s0, s1};
-
-  int item = int(blockIdx.x), tile = item, half = -1;
-  if (item < n_full) {
-    const int even = n_full - n_full % kXcds;
-    if (item < even) tile = (item % kXcds) * (even / kXcds) + item / kXcds;
-  } else {
-    tile = n_full + (item - n_full) / 2;
-    half = (item - n_full) & 1;
-  }
-  const int band = kGroupM * tiles_n;
-  const int first_m = (tile / band) * kGroupM;
-  const int band_m = min(kGroupM, tiles_m - first_m);
-  const int tm = first_m + (tile % band) % band_m;
-  const int tn = (tile % band) / band_m;
-  const int m0 = tm * kBM, n0 = tn * kBN;
-  if (half < 0)
-    prefill_tile<8>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, m0, n0, st);
+  const TileOrigin o = walk_tile(int(blockIdx.x), tiles_m, tiles_n, n_full);
+  if (o.half < 0)
+    prefill_tile<8>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0, o.n0, st);
   else
-    prefill_tile<4>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, m0, n0 + 128 * half,
-                    st);
+    prefill_tile<4>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0, o.n0, st);
 }
+
+}  // namespace two_stage
 
 }  // namespace tile256
 
@@ -528,9 +822,12 @@ extern "C" int w8a8_block_gemm_prefill(const uint8_t* a_q, const float* a_scale,
     const int64_t tail = big % cus;
     const int64_t split = (tail != 0 && 2 * tail <= cus) ? tail : 0;
     const int64_t n_full = big - split;
-    launch(tile256::w8a8_prefill_kernel, dim3(unsigned(n_full + 2 * split)),
-           dim3(tile256::kThreads), 0, stream, a_q, a_scale, w_q, w_scale, out, m, n, k, ldc,
-           int(big_m), int(big_n), int(n_full), vec_out);
+    // the five-slot ring's rotation repeats every eight groups
+    const auto kernel = (k / 128) % 8 == 0 ? tile256::ring::w8a8_prefill_ring_kernel
+                                            : tile256::two_stage::w8a8_prefill_kernel;
+    launch(kernel, dim3(unsigned(n_full + 2 * split)), dim3(tile256::kThreads), 0, stream, a_q,
+           a_scale, w_q, w_scale, out, m, n, k, ldc, int(big_m), int(big_n), int(n_full),
+           vec_out);
     return launch_status();
   }
   const int64_t tiles_m = (int64_t(m) + 127) / 128, tiles_n = (int64_t(n) + 127) / 128;

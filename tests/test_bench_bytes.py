@@ -54,12 +54,19 @@ def test_more_than_one_gpu_is_refused_before_touching_a_device():
 def test_prefill_copy_bytes_follow_the_launch_rule():
     # 4593 x 16384 on 256 CUs: 18 x 64 = 1152 tiles of 256 x 256, a last round of 128 tiles
     # (half the CUs) split into 256 x 128 halves; per 128-wide group a whole tile copies its
-    # two 32 KB operand tiles and 1 KB of scales, a half 32 KB + 16 KB + 1 KB
+    # two 32 KB operand tiles, a half 32 KB + 16 KB (40 groups, a multiple of eight: the
+    # scales go to registers, not LDS)
     g = 5120 // 128
     whole, split = 1152 - 128, 128
     assert bench.prefill_copy_bytes(4593, 16384, 5120, 256) == g * (
+        whole * 2 * 32768 + split * 2 * (32768 + 16384))
+    # with a group count that is not a multiple of eight 1 KB of scales per tile goes
+    # through LDS too
+    g = 5248 // 128
+    assert bench.prefill_copy_bytes(4593, 16384, 5248, 256) == g * (
         whole * (2 * 32768 + 1024) + split * 2 * (32768 + 16384 + 1024))
     # a last round more than half full (712 = 2 x 256 + 200 tiles) is not split
     assert bench.prefill_copy_bytes(256 * 4, 256 * 178, 128, 256) == 712 * (2 * 32768 + 1024)
+    g = 5120 // 128
     # fewer tiles than half the CUs: 128 x 128 tiles, 16 KB per operand + 512 B of scales
     assert bench.prefill_copy_bytes(4593, 1024, 5120, 256) == g * 36 * 8 * (2 * 16384 + 512)

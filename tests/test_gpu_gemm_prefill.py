@@ -9,8 +9,9 @@ scales.
 
 The library picks the 256 x 256 tiling once a problem has at least half a round of such
 tiles (128 on the 256-CU MI355X) and splits the tiles of a last round that is at most half
-full into 256 x 128 halves; the large-tile cases below are sized to take each of those
-paths, the smaller ones the 128 x 128 tiling."""
+full into 256 x 128 halves; with a group count (K / 128) that is a multiple of eight those
+tiles run on the five-slot ring, else on two stages.  The large-tile cases below are sized
+to take each of those paths, the smaller ones the 128 x 128 tiling."""
 import numpy as np
 import pytest
 import torch
@@ -50,6 +51,9 @@ def test_ragged_shapes_in_full(m, n, k):
     (4096, 2560, 384),   # 160 tiles: whole tiles only; three K-groups (odd: a zero step first)
     (4096, 1920, 256),   # 128 tiles, split; the last column tile's second half is empty
     (4000, 2304, 384),   # 144 tiles, whole; ragged last row tile, half-empty last column tile
+    (4096, 2048, 1024),  # ring (8 groups: one trip of its rotation), every tile in halves
+    (4096, 1920, 1024),  # ring, split; the last column tile's second half is empty
+    (4000, 2304, 2048),  # ring (16 groups: two trips), whole tiles; ragged rows and columns
 ])
 def test_large_tile_shapes_in_full(m, n, k):
     a = synth.prefill_activation(k, m=m, seed=m + 3 * n + k)
@@ -96,17 +100,37 @@ def test_rows_past_two_to_the_32_bytes_of_codes():
     assert ok, f"worst error / bound = {worst:.3f}"
 
 
-def test_split_halves_match_whole_tiles_bit_for_bit():
+@pytest.mark.parametrize("k", [256, 1024])  # two stages; the ring
+def test_split_halves_match_whole_tiles_bit_for_bit(k):
     # 4096 x 2048 runs as 256 x 128 halves, 4096 x 2560 as whole 256 x 256 tiles; both sum
     # the same scaled group partials in the same order, so the shared columns agree exactly
-    m, k = 4096, 256
-    a = synth.prefill_activation(k, m=m, seed=515)
-    wq, ws = oracle.block_quant(synth.decode_weight(2560, k, seed=516))
+    m = 4096
+    a = synth.prefill_activation(k, m=m, seed=515 + k)
+    wq, ws = oracle.block_quant(synth.decode_weight(2560, k, seed=516 + k))
     q, s = _quant(a)
     halves = host(fq.w8a8_block_gemm_prefill(q, s, u8_dev(wq[:2048].copy()),
                                              f32_dev(ws[:16].copy())))
     whole = host(fq.w8a8_block_gemm_prefill(q, s, u8_dev(wq), f32_dev(ws)))
     assert np.array_equal(halves, whole[:, :2048])
+
+
+@pytest.mark.parametrize("n", [2048, 2560])  # tiles split in halves; whole tiles
+def test_ring_matches_two_stages_bit_for_bit(n):
+    # K = 1024 (8 groups) runs on the five-slot ring; the same problem with a ninth group of
+    # zero codes (unit scales) runs on two stages.  The zero group adds exactly zero to every
+    # sum, and both sum the same scaled partials in the same order, so the outputs agree bit
+    # for bit.
+    m, k = 4096, 1024
+    a = synth.prefill_activation(k, m=m, seed=520 + n)
+    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=521 + n))
+    q, s = _quant(a)
+    ring = host(fq.w8a8_block_gemm_prefill(q, s, u8_dev(wq), f32_dev(ws)))
+    q9 = torch.cat([q, torch.zeros((m, 128), dtype=torch.uint8, device=DEV)], 1).contiguous()
+    s9 = torch.cat([s, torch.ones((m, 1), dtype=torch.float32, device=DEV)], 1).contiguous()
+    wq9 = np.ascontiguousarray(np.concatenate([wq, np.zeros((n, 128), np.uint8)], 1))
+    ws9 = np.ascontiguousarray(np.concatenate([ws, np.ones((n // 128, 1), np.float32)], 1))
+    two = host(fq.w8a8_block_gemm_prefill(q9, s9, u8_dev(wq9), f32_dev(ws9)))
+    assert np.array_equal(ring, two)
 
 
 def test_small_integer_sums_are_exact():
