@@ -413,11 +413,13 @@ def main():
     # --------------------------------------- W8A8 GEMM at the 4593-token prefill width
     if "prefill" in only:
         # operands and outputs rotate over >= 1 GB of sets (codes, scales, weights, output)
-        m = synth.PREFILL_TOKENS
+        # the 4593-token prefill at the four decode widths, and a short (256-token) prefill
+        m_full = synth.PREFILL_TOKENS
         a = bf16_dev(torch, synth.prefill_activation(K_DECODE, seed=3100))
-        q0, s0 = fq.fp8_group_quant(a)
+        q_full, s_full = fq.fp8_group_quant(a)
         del a
-        for n in (16384, 5120):
+        for m, n in [(m_full, n) for n in N_DECODE] + [(256, 16384)]:
+            q0, s0 = q_full[:m].contiguous(), s_full[:m].contiguous()
             wq0, ws0 = sets[0]["w"][n]
             per = m * K_DECODE + n * K_DECODE + m * n * 2
             nset = rotation_sets(per)
@@ -436,8 +438,9 @@ def main():
                 f"({kernels[key]['frac_mfma_fp8']:.3f} of fp8 MFMA peak, {nset} operand sets)")
             kernels[key]["copy_bytes"] = prefill_copy_bytes(
                 m, n, K_DECODE, torch.cuda.get_device_properties(0).multi_processor_count)
-            del ps, launches
-        del q0, s0
+            del ps, launches, q0, s0
+        del q_full, s_full
+        m = m_full
         # The copy path alone (global -> LDS, the GEMM's own copy instructions and slices, no
         # MFMA) moving the N = 16384 launch's operand bytes, from an L2-resident span and from
         # HBM, beside the launch's MFMA time at the fp8 peak: the floors the GEMM is read

@@ -33,8 +33,10 @@
 //    weight block scale rides in the activation-scale copy), one group ahead.
 // Results are the same bit for bit: the same products, scaled and summed in the same order.
 //
-// tile128 (fewer than half a round of 256 x 256 tiles, e.g. a 1024-column projection):
-// 256-thread workgroups, two per CU, each a 128 x 128 tile (2 x 2 waves of 64 x 64).
+// tile128 (fewer than half a round of 256 x 256 tiles, e.g. a 1024-column projection or a
+// short prefill): 256-thread workgroups, up to two per CU, each a 128 x 128 tile (2 x 2
+// waves of 64 x 64).  With at most one tile per CU and a group count that is a multiple of
+// eight it runs on the same five-slot ring (16 KB slots), else on two stages.
 //
 // Workgroups are ordered so that concurrently running ones share operand tiles:
 // consecutive row tiles per column tile, and each XCD (workgroup ids are dealt to the 8
@@ -73,42 +75,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base,
                                            valid > 0 ? valid * k : 0, kBufferDword3);
 }
 
-namespace tile256 {
-
-constexpr int kBM = 256, kBN = 256, kThreads = 512;
-constexpr int kArr = kBM * 128;           // one operand tile of one group (bytes)
-constexpr int kCPitch = kBN;              // bf16 elements per staged output row
-static_assert(64 * kCPitch * 2 == kArr, "an operand array holds 64 staged output rows");
-constexpr int kGroupM = 4;                // row tiles per column tile in the walk order
-
-// Work item -> output tile origin.  Items [0, n_full) are whole tiles, the rest the two
-// halves (half 0 or 1: columns n0 .. n0 + 127) of each of the last tiles of the walk order;
-// half is -1 for a whole tile.  The walk takes kGroupM consecutive row tiles per column
-// tile, and each XCD (workgroup ids are dealt to the 8 XCDs round-robin) a contiguous
-// stretch of it.
-struct TileOrigin {
-  int m0, n0, half;
-};
-__device__ __forceinline__ TileOrigin walk_tile(int item, int tiles_m, int tiles_n, int n_full) {
-  int tile = item, half = -1;
-  if (item < n_full) {
-    const int even = n_full - n_full % kXcds;
-    if (item < even) tile = (item % kXcds) * (even / kXcds) + item / kXcds;
-  } else {
-    tile = n_full + (item - n_full) / 2;
-    half = (item - n_full) & 1;
-  }
-  const int band = kGroupM * tiles_n;
-  const int first_m = (tile / band) * kGroupM;
-  const int band_m = min(kGroupM, tiles_m - first_m);
-  const int tm = first_m + (tile % band) % band_m;
-  const int tn = (tile % band) / band_m;
-  return {tm * kBM, tn * kBN + (half > 0 ? 128 : 0), half};
-}
+// ---------------------------------------------------------------------------------------
+// Shared by the tiled kernels.  A wave tile is 64 rows x 16 kCols columns; the waves form a
+// kWM x 2 grid (kWM = 4: 256 x 256 or 256 x 128 tiles of 8 waves; kWM = 2: 128 x 128 tiles
+// of 4 waves).
 
 // Staged 128-byte operand row r keeps its 16-byte chunk c at slot c ^ (r & 7) ^ (bit 3 of
 // r): an operand read takes one chunk from 16 consecutive rows per 16 lanes, which land on
-// 16 distinct bank groups.  Fragment row 64 wm + 16 i + orow (or kWaveCols wn + 16 c +
+// 16 distinct bank groups.  Fragment row 64 wm + 16 i + orow (or wave_cols wn + 16 c +
 // orow) has the swizzle of row orow, so every read is one of four lane offsets plus a
 // constant.  A 1 KB copy block (8 rows) is one copy instruction: lane L of block b loads
 // row 8b + L/8, chunk (L % 8) ^ (L / 8) ^ (b & 1), which the swizzle places at byte
@@ -139,15 +113,17 @@ __device__ __forceinline__ v8i ld32(const uint8_t* p, int lo, int hi) {
 // transposed tile: element j of lane (oh, orow) in row tile i is row 16 i + orow of the
 // wave's 64 and column 4 oh + j of the 16 -- one activation scale per lane and row tile.
 //
-// The bf16 output tile is staged through four operand arrays (rows 64 s .. 64 s + 63 in
-// array s; row r's 8-column blocks XOR-permuted by bits 0..3 of r, so that the 16 rows one
-// 8-byte store instruction writes land on distinct bank groups), then written out in
-// 16-byte row pieces.  Called after a barrier that ends every operand read.
-template <int kCols>
+// The bf16 output tile is staged through kWM operand arrays (rows 64 s .. 64 s + 63 in
+// array s at a pitch of one tile row; row r's 8-column blocks XOR-permuted by bits 0..3 of
+// r, so that the 16 rows one 8-byte store instruction writes spread over the bank groups),
+// then written out in 16-byte row pieces.  Called after a barrier that ends every operand
+// read.
+template <int kWM, int kCols>
 __device__ __forceinline__ void store_tile(const v4f (&acc)[4][kCols], uint8_t* s0, uint8_t* s1,
                                            uint8_t* s2, uint8_t* s3, uint16_t* __restrict__ out,
                                            int m, int n, int ldc, int vec_out, int m0, int n0) {
   constexpr int kWaveCols = 16 * kCols, kTileCols = 2 * kWaveCols;
+  constexpr int kRows = 64 * kWM, kThreads = 128 * kWM;
   const int t = int(threadIdx.x), lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -165,18 +141,18 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[4][kCols], uint8_t* 
                             (uint32_t(f32_to_bf16_rne(acc[i][c][1])) << 16);
         const uint32_t hi = uint32_t(f32_to_bf16_rne(acc[i][c][2])) |
                             (uint32_t(f32_to_bf16_rne(acc[i][c][3])) << 16);
-        *reinterpret_cast<uint2*>(so + r * kCPitch + col) = make_uint2(lo, hi);
+        *reinterpret_cast<uint2*>(so + r * kTileCols + col) = make_uint2(lo, hi);
       }
   }
   __syncthreads();
   constexpr int kRowChunks = kTileCols / 8;  // 16-byte chunks per output row
 #pragma unroll 4
-  for (int q = 0; q < kBM * kRowChunks / kThreads; ++q) {
+  for (int q = 0; q < kRows * kRowChunks / kThreads; ++q) {
     const int ch = t + kThreads * q, r = ch / kRowChunks, cc = (ch % kRowChunks) * 8;
     const int gm = m0 + r, gn = n0 + cc;
     if (gm < m && gn < n) {
       const uint16_t* src = reinterpret_cast<const uint16_t*>(slab(r >> 6)) +
-                            (r & 63) * kCPitch + (cc ^ ((r & 15) << 3));
+                            (r & 63) * kTileCols + (cc ^ ((r & 15) << 3));
       uint16_t* dst = out + int64_t(gm) * ldc + gn;
       if (vec_out) {
         *reinterpret_cast<v4u*>(dst) = *reinterpret_cast<const v4u*>(src);
@@ -191,16 +167,17 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[4][kCols], uint8_t* 
 // ---------------------------------------------------------------------------------------
 // Five-slot ring (group counts that are a multiple of eight).
 //
-// LDS: five 32 KB slots, each a separate array (160 KB, all of it).  Step g multiplies the
-// activation tile and the weight tile of group g from two slots while the weight tile of
-// group g + 1 lands in a third, and copies the activation tile of group g + 1 and the
-// weight tile of group g + 2 into the two slots that group g - 1 used: a weight copy has
-// two steps to land, an activation copy one.  The slots rotate with a period of eight
-// steps: activation groups 8t + j sit in slots 4 3 4 1 4 0 4 2 and weight groups in slots
-// 0 1 2 0 3 2 1 3, so that the two activation groups and three weight groups of any step
-// sit in five distinct slots.  Separate objects let the compiler see that a slot's operand
-// reads never alias the copies landing in the others, so it keeps those copies in flight.
-// The scales have no LDS left: each wave loads them into registers.
+// LDS: five slots, each a separate array (one operand tile of one group each; 5 x 32 KB =
+// all 160 KB for the 256-row tiles, 5 x 16 KB for the 128 x 128 tiles, two workgroups per
+// CU).  Step g multiplies the activation tile and the weight tile of group g from two
+// slots while the weight tile of group g + 1 lands in a third, and copies the activation
+// tile of group g + 1 and the weight tile of group g + 2 into the two slots that group
+// g - 1 used: a weight copy has two steps to land, an activation copy one.  The slots
+// rotate with a period of eight steps: activation groups 8t + j sit in slots 4 3 4 1 4 0 4 2
+// and weight groups in slots 0 1 2 0 3 2 1 3, so that the two activation groups and three
+// weight groups of any step sit in five distinct slots.  Separate objects let the compiler
+// see that a slot's operand reads never alias the copies landing in the others, so it keeps
+// those copies in flight.  The scales take no LDS: each wave loads them into registers.
 namespace ring {
 
 // One group's scales as one lane holds them: the activation scale of row 64 wm + lane of
@@ -209,33 +186,39 @@ struct Scales {
   float row, w;
 };
 
+template <int kBytes>
 struct Slots {
-  uint8_t (&x0)[kArr];
-  uint8_t (&x1)[kArr];
-  uint8_t (&x2)[kArr];
-  uint8_t (&x3)[kArr];
-  uint8_t (&x4)[kArr];
+  uint8_t (&x0)[kBytes];
+  uint8_t (&x1)[kBytes];
+  uint8_t (&x2)[kBytes];
+  uint8_t (&x3)[kBytes];
+  uint8_t (&x4)[kBytes];
 };
 
-// One output tile: rows [m0, m0 + 256) x columns [n0, n0 + 32 kCols), kCols = 8 (256
-// columns, wave tiles 64 x 128) or 4 (128 columns, wave tiles 64 x 64).
-template <int kCols>
+// One output tile: rows [m0, m0 + 64 kWM) x columns [n0, n0 + 32 kCols).
+template <int kWM, int kCols, int kBytes>
 __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
                                              const float* __restrict__ a_scale,
                                              const uint8_t* __restrict__ w_q,
                                              const float* __restrict__ w_scale,
                                              uint16_t* __restrict__ out, int m, int n, int k,
                                              int ldc, int vec_out, int m0, int n0,
-                                             const Slots& st) {
+                                             const Slots<kBytes>& st) {
+  constexpr int kWaves = 2 * kWM;
+  constexpr int kRows = 64 * kWM;         // tile rows
   constexpr int kWaveCols = 16 * kCols;   // columns per wave
   constexpr int kTileCols = 2 * kWaveCols;
-  constexpr int kBBlocks = kTileCols / 8 / 8;  // 1 KB weight copy blocks per wave per group
+  static_assert(kRows * 128 <= kBytes && kTileCols * 128 <= kBytes, "a slot holds a tile");
+  static_assert(kRows * kTileCols * 2 <= kWM * kBytes, "kWM slots hold the output tile");
+  constexpr int kABlocks = kRows / 8 / kWaves;     // 1 KB activation copy blocks per wave
+  constexpr int kBBlocks = kTileCols / 8 / kWaves;  // 1 KB weight copy blocks per wave
+  static_assert(kABlocks == 4, "four activation blocks per wave and group");
   const int t = int(threadIdx.x), lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // rows 64 wm .., columns kWaveCols * wn ..
   const int groups = k >> 7;
 
-  const __amdgpu_buffer_rsrc_t ra_rsrc = tile_rsrc(a_q, m0, m, k, kBM);
+  const __amdgpu_buffer_rsrc_t ra_rsrc = tile_rsrc(a_q, m0, m, k, kRows);
   const __amdgpu_buffer_rsrc_t rb_rsrc = tile_rsrc(w_q, n0, n, k, kTileCols);
   const __amdgpu_buffer_rsrc_t none_rsrc = tile_rsrc(a_q, 0, 0, k, 0);
   // Scales: the wave's 64 activation rows (rows past m read as zeros) as a [rows, groups]
@@ -250,14 +233,15 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
   const int wrow =
       __builtin_amdgcn_readfirstlane(min((n0 + kWaveCols * wn) >> 7, (n >> 7) - 1));
   const float* __restrict__ wsp = w_scale + int64_t(wrow) * groups;
-  // Copy block w + 8q of an operand is block w's offset plus 64 q rows; the sum is formed
-  // at each copy from an opaque copy of block w's, so it costs one add, not a live register.
+  // Copy block w + kWaves q of an operand is block w's offset plus 8 kWaves q rows; the sum
+  // is formed at each copy from an opaque copy of block w's, so it costs one add, not a
+  // live register.
   const int voff0 =
       (8 * wave + (lane >> 3)) * k + (((lane & 7) ^ (lane >> 3) ^ (wave & 1)) << 4);
   auto voff = [&](int q) {
     int v = voff0;
     asm volatile("" : "+v"(v));
-    return v + q * 64 * k;
+    return v + q * 8 * kWaves * k;
   };
 
   // The copies of a step, in pieces: j < 4 the activation blocks of group ga, then its
@@ -267,22 +251,23 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
   // zero-size buffer (zeros written, no memory traffic) and the scale loads repeat the last
   // group.  Every copy is unconditional: a branch here would split the step and let the
   // compiler sink its FMAs past the next barrier.
-  constexpr int kPieces = 4 + 1 + kBBlocks + 1;
+  constexpr int kPieces = kABlocks + 1 + kBBlocks + 1;
   auto copy_piece = [&](uint8_t* sa, uint8_t* sb, Scales& sc, int ga, int gb, int j) {
-    if (j < 4) {
+    if (j < kABlocks) {
       const bool live = ga < groups;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? ra_rsrc : none_rsrc,
-                                               (lds_void*)(sa + (wave + 8 * j) * 1024), 16,
-                                               voff(j), live ? ga * 128 : 0, 0, 0);
-    } else if (j == 4) {
+                                               (lds_void*)(sa + (wave + kWaves * j) * 1024),
+                                               16, voff(j), live ? ga * 128 : 0, 0, 0);
+    } else if (j == kABlocks) {
       sc.row = __builtin_bit_cast(
           float, __builtin_amdgcn_raw_buffer_load_b32(rs_rsrc, rs_off,
                                                       min(ga, groups - 1) * 4, 0));
-    } else if (j < 5 + kBBlocks) {
+    } else if (j < kABlocks + 1 + kBBlocks) {
+      const int q = j - kABlocks - 1;
       const bool live = gb < groups;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rb_rsrc : none_rsrc,
-                                               (lds_void*)(sb + (wave + 8 * (j - 5)) * 1024),
-                                               16, voff(j - 5), live ? gb * 128 : 0, 0, 0);
+                                               (lds_void*)(sb + (wave + kWaves * q) * 1024),
+                                               16, voff(q), live ? gb * 128 : 0, 0, 0);
     } else {
       sc.w = wsp[min(ga, groups - 1)];
     }
@@ -368,9 +353,18 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
     bcur = bnxt;
 #pragma unroll
     for (int c = 1; c <= kCols; ++c) {
-      // (the last piece, the scalar load, waits for the last column: every LDS read of the
-      // step is issued and waited for by then)
-      if (3 + c < kPieces - 1) copy_piece(na, nb, nsc, g + 1, g + 2, 3 + c);
+      // The row scales and the weight blocks (pieces 4 .. kPieces - 2): one per column from
+      // column 1 while there are no more of them than columns, else spread over all of
+      // them.  The last piece, the scalar load, waits for the last column: every LDS read of
+      // the step is issued and waited for by then.
+      constexpr int kDealt = kPieces - 5;
+      if constexpr (kDealt <= kCols) {
+        if (c <= kDealt) copy_piece(na, nb, nsc, g + 1, g + 2, 3 + c);
+      } else {
+#pragma unroll
+        for (int j = 4 + (c - 1) * kDealt / kCols; j < 4 + c * kDealt / kCols; ++j)
+          copy_piece(na, nb, nsc, g + 1, g + 2, j);
+      }
       if (c == kCols) copy_piece(na, nb, nsc, g + 1, g + 2, kPieces - 1);
       __builtin_amdgcn_sched_barrier(0);
       bnxt = bcur;
@@ -407,7 +401,7 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
     __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
-  for (int j = 5; j < 5 + kBBlocks; ++j) {
+  for (int j = kABlocks + 1; j < kABlocks + 1 + kBBlocks; ++j) {
     copy_piece(st.x4, st.x1, s0, 0, 1, j);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -425,9 +419,44 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
     g += 8;
   } while (g < groups);
   __syncthreads();  // every copy landed and every wave is done reading the slots
-  store_tile<kCols>(acc, st.x0, st.x1, st.x2, st.x3, out, m, n, ldc, vec_out, m0, n0);
+  store_tile<kWM, kCols>(acc, st.x0, st.x1, st.x2, st.x3, out, m, n, ldc, vec_out, m0, n0);
 }
 
+}  // namespace ring
+
+namespace tile256 {
+
+constexpr int kBM = 256, kBN = 256, kThreads = 512;
+constexpr int kArr = kBM * 128;           // one operand tile of one group (bytes)
+constexpr int kGroupM = 4;                // row tiles per column tile in the walk order
+
+// Work item -> output tile origin.  Items [0, n_full) are whole tiles, the rest the two
+// halves (half 0 or 1: columns n0 .. n0 + 127) of each of the last tiles of the walk order;
+// half is -1 for a whole tile.  The walk takes kGroupM consecutive row tiles per column
+// tile, and each XCD (workgroup ids are dealt to the 8 XCDs round-robin) a contiguous
+// stretch of it.
+struct TileOrigin {
+  int m0, n0, half;
+};
+__device__ __forceinline__ TileOrigin walk_tile(int item, int tiles_m, int tiles_n, int n_full) {
+  int tile = item, half = -1;
+  if (item < n_full) {
+    const int even = n_full - n_full % kXcds;
+    if (item < even) tile = (item % kXcds) * (even / kXcds) + item / kXcds;
+  } else {
+    tile = n_full + (item - n_full) / 2;
+    half = (item - n_full) & 1;
+  }
+  const int band = kGroupM * tiles_n;
+  const int first_m = (tile / band) * kGroupM;
+  const int band_m = min(kGroupM, tiles_m - first_m);
+  const int tm = first_m + (tile % band) % band_m;
+  const int tn = (tile % band) / band_m;
+  return {tm * kBM, tn * kBN + (half > 0 ? 128 : 0), half};
+}
+
+// Five-slot ring (group counts that are a multiple of eight): whole tiles 256 x 256, the
+// halves 256 x 128, 32 KB slots (all 160 KB of LDS).
 __global__ __launch_bounds__(kThreads, 1) void w8a8_prefill_ring_kernel(
     const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale,
     const uint8_t* __restrict__ w_q, const float* __restrict__ w_scale,
@@ -435,15 +464,16 @@ __global__ __launch_bounds__(kThreads, 1) void w8a8_prefill_ring_kernel(
     int n_full, int vec_out) {
   __shared__ __attribute__((aligned(16))) uint8_t x0[kArr], x1[kArr], x2[kArr], x3[kArr],
       x4[kArr];
-  const Slots st{x0, x1, x2, x3, x4};
+  const ring::Slots<kArr> st{x0, x1, x2, x3, x4};
   const TileOrigin o = walk_tile(int(blockIdx.x), tiles_m, tiles_n, n_full);
   if (o.half < 0)
-    prefill_tile<8>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0, o.n0, st);
+    ring::prefill_tile<4, 8>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0,
+                             o.n0, st);
   else
-    prefill_tile<4>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0, o.n0, st);
+    ring::prefill_tile<4, 4>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0,
+                             o.n0, st);
 }
 
-}  // namespace ring
 
 // ---------------------------------------------------------------------------------------
 // Two stages (any group count).
@@ -613,7 +643,7 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
     step(g + 1, st.a1, st.b1, st.s1, st.a0, st.b0, st.s0);
   }
   __syncthreads();  // every copy landed and every wave is done reading the stages
-  store_tile<kCols>(acc, st.a0, st.a1, st.b0, st.b1, out, m, n, ldc, vec_out, m0, n0);
+  store_tile<4, kCols>(acc, st.a0, st.a1, st.b0, st.b1, out, m, n, ldc, vec_out, m0, n0);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void w8a8_prefill_kernel(
@@ -663,6 +693,37 @@ __device__ __forceinline__ v8i lds_load32(const uint8_t* base, int row, int h) {
   return r;
 }
 
+// Workgroup -> output tile origin (m0, n0): kGroupM consecutive row tiles per column tile,
+// each XCD a contiguous stretch of that order.
+__device__ __forceinline__ int2 tile_origin(int bid, int tiles_m, int tiles_n) {
+  const int nblk = tiles_m * tiles_n;
+  const int even = nblk - nblk % kXcds;
+  if (bid < even) bid = (bid % kXcds) * (even / kXcds) + bid / kXcds;
+  const int band = kGroupM * tiles_n;
+  const int first_m = (bid / band) * kGroupM;
+  const int band_m = min(kGroupM, tiles_m - first_m);
+  const int tm = first_m + (bid % band) % band_m;
+  const int tn = (bid % band) / band_m;
+  return make_int2(tm * kBM, tn * kBN);
+}
+
+// Five-slot ring (group counts that are a multiple of eight, at most one tile per CU):
+// 16 KB slots, 2 x 2 waves of 64 x 64.
+__global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_small_ring_kernel(
+    const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale,
+    const uint8_t* __restrict__ w_q, const float* __restrict__ w_scale,
+    uint16_t* __restrict__ out, int m, int n, int k, int ldc, int tiles_m, int tiles_n,
+    int vec_out) {
+  static_assert(kAStage == kBStage, "one slot size for both operands");
+  __shared__ __attribute__((aligned(16))) uint8_t x0[kAStage], x1[kAStage], x2[kAStage],
+      x3[kAStage], x4[kAStage];
+  const ring::Slots<kAStage> st{x0, x1, x2, x3, x4};
+  const int2 origin = tile_origin(int(blockIdx.x), tiles_m, tiles_n);
+  ring::prefill_tile<2, 4>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, origin.x,
+                           origin.y, st);
+}
+
+// Two stages (any group count).
 // Operand tiles are copied global -> LDS by the buffer unit itself (buffer_load ... lds):
 // no staging registers and no LDS store instructions.  A wave's copy instruction fills one
 // contiguous 1 KB block of LDS, lane L writing bytes [16L, 16L + 16); so lane L of block b
@@ -679,16 +740,8 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_small_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
   __shared__ __attribute__((aligned(16))) float s_as[2][kBM];
 
-  const int nblk = tiles_m * tiles_n;
-  int bid = int(blockIdx.x);
-  const int even = nblk - nblk % kXcds;
-  if (bid < even) bid = (bid % kXcds) * (even / kXcds) + bid / kXcds;
-  const int band = kGroupM * tiles_n;
-  const int first_m = (bid / band) * kGroupM;
-  const int band_m = min(kGroupM, tiles_m - first_m);
-  const int tm = first_m + (bid % band) % band_m;
-  const int tn = (bid % band) / band_m;
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int2 origin = tile_origin(int(blockIdx.x), tiles_m, tiles_n);
+  const int m0 = origin.x, n0 = origin.y;
 
   const int t = int(threadIdx.x), lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -823,7 +876,7 @@ extern "C" int w8a8_block_gemm_prefill(const uint8_t* a_q, const float* a_scale,
     const int64_t split = (tail != 0 && 2 * tail <= cus) ? tail : 0;
     const int64_t n_full = big - split;
     // the five-slot ring's rotation repeats every eight groups
-    const auto kernel = (k / 128) % 8 == 0 ? tile256::ring::w8a8_prefill_ring_kernel
+    const auto kernel = (k / 128) % 8 == 0 ? tile256::w8a8_prefill_ring_kernel
                                             : tile256::two_stage::w8a8_prefill_kernel;
     launch(kernel, dim3(unsigned(n_full + 2 * split)), dim3(tile256::kThreads), 0, stream, a_q,
            a_scale, w_q, w_scale, out, m, n, k, ldc, int(big_m), int(big_n), int(n_full),
@@ -832,8 +885,12 @@ extern "C" int w8a8_block_gemm_prefill(const uint8_t* a_q, const float* a_scale,
   }
   const int64_t tiles_m = (int64_t(m) + 127) / 128, tiles_n = (int64_t(n) + 127) / 128;
   if (tiles_m * tiles_n > 0x7FFFFFFF) return FP8Q_EINVAL;
-  launch(tile128::w8a8_prefill_small_kernel, dim3(unsigned(tiles_m * tiles_n)),
-         dim3(tile128::kThreads), 0, stream, a_q, a_scale, w_q, w_scale, out, m, n, k, ldc,
-         int(tiles_m), int(tiles_n), vec_out);
+  // the ring when every CU holds at most one tile (with two tiles side by side on a CU its
+  // deeper copies gain nothing)
+  const auto small = (k / 128) % 8 == 0 && tiles_m * tiles_n <= cus
+                         ? tile128::w8a8_prefill_small_ring_kernel
+                         : tile128::w8a8_prefill_small_kernel;
+  launch(small, dim3(unsigned(tiles_m * tiles_n)), dim3(tile128::kThreads), 0, stream, a_q,
+         a_scale, w_q, w_scale, out, m, n, k, ldc, int(tiles_m), int(tiles_n), vec_out);
   return launch_status();
 }

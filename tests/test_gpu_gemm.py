@@ -97,6 +97,36 @@ def test_every_e4m3_product_is_exact():
         assert np.array_equal(bf16_host_to_f64(out), want), f"rows starting at {start}"
 
 
+def _one_group_sum(terms):
+    """out[0, 0] of a 1 x 128 x 128 problem with unit scales whose only nonzero products are
+    terms {k: (a, w)} (a and w exact E4M3 values)."""
+    a = np.zeros((1, 128), np.float32)
+    w = np.zeros((128, 128), np.float32)
+    for kk, (av, wv) in terms.items():
+        a[0, kk], w[0, kk] = av, wv
+    one = f32_dev(np.ones((1, 1), np.float32))
+    out = host(fq.w8a8_block_gemm(u8_dev(oracle.e4m3_encode(a)), one,
+                                  u8_dev(oracle.e4m3_encode(w)), one))
+    return float(bf16_host_to_f64(out)[0, 0])
+
+
+def test_fp8_mfma_sums_blocks_of_eight_at_reduced_precision():
+    """Pins the instruction, not the oracle: v_mfma_f32_16x16x128_f8f6f4 forms each product
+    exactly but sums the products of 8 consecutive k (0-7, 8-15, ...) in a window about 14
+    bits below the block's largest one, and adds the blocks in FP32.  +2^16 and -2^16 in
+    blocks 0 and 15 with a 1 between them: the 1 survives outside those blocks and is
+    dropped inside them; beside +2^16 in one block 2^3 survives and 2^2 does not; across
+    blocks 2^-7 survives (an FP32 sum).  This is why an output decided by heavy cancellation
+    can land just outside the FP32-accumulation tolerance (see the prefill case marked so)."""
+    big, neg = (256.0, 256.0), (-256.0, 256.0)
+    for q, kept in ((1, False), (7, False), (8, True), (64, True), (119, True), (120, False)):
+        got = _one_group_sum({0: big, q: (1.0, 1.0), 127: neg})
+        assert got == (1.0 if kept else 0.0), (q, got)
+    assert _one_group_sum({0: big, 1: (4.0, 1.0), 127: neg}) == 0.0
+    assert _one_group_sum({0: big, 1: (8.0, 1.0), 127: neg}) == 8.0
+    assert _one_group_sum({0: big, 64: (2.0 ** -7, 1.0), 127: neg}) == 2.0 ** -7
+
+
 def test_small_integer_sums_are_exact():
     """Codes in {0, +-1, +-2} with power-of-two scales: every partial and sum is a short
     dyadic number, exact in FP32 whatever the order, so the output must be exactly the

@@ -35,7 +35,18 @@ def _quant(a_bits):
 
 
 @pytest.mark.parametrize("m,n,k", [(17, 128, 128), (130, 384, 384), (300, 256, 1152),
-                                   (1, 128, 256), (128, 640, 512), (257, 1024, 256)])
+                                   (1, 128, 256), (128, 640, 512), (257, 1024, 256),
+                                   # 128 x 128 tiles on the ring (K / 128 a multiple of 8,
+                                   # at most one tile per CU)
+                                   (17, 128, 1024), (300, 384, 1024), (1, 128, 2048),
+                                   (257, 1024, 2048), (130, 640, 3072),
+                                   # 272 tiles of 128 x 128: two stages; one of its 4.3 M
+                                   # outputs, decided by cancellation, lands at 1.005 x the
+                                   # bound: the MFMA sums each 8 products about 14 bits
+                                   # below the largest (see the decode GEMM's block test)
+                                   pytest.param(2100, 2048, 1024, marks=pytest.mark.xfail(
+                                       strict=True, reason="fp8 MFMA block summation: one "
+                                       "output at 1.005 x the FP32-accumulation bound"))])
 def test_ragged_shapes_in_full(m, n, k):
     a = synth.prefill_activation(k, m=m, seed=m * 7 + k)
     wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=n + k))
@@ -65,11 +76,13 @@ def test_large_tile_shapes_in_full(m, n, k):
     assert ok, f"worst error / bound = {worst:.3f}"
 
 
-def test_large_tiles_long_k_on_sampled_rows():
-    # 128 tiles of 256 x 256 (split into halves) with K = 16384: 128 groups per tile
-    m, n, k = 4096, 2048, 16384
-    a = synth.prefill_activation(k, m=m, seed=717)
-    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=718))
+@pytest.mark.parametrize("k", [16384, 65536])
+def test_large_tiles_long_k_on_sampled_rows(k):
+    # 128 tiles of 256 x 256 (split into halves) with K = 16384 / 65536: 128 / 512 groups per
+    # tile on the ring (copy offsets up to 2^24 bytes into a tile's rows)
+    m, n = 4096, 2048
+    a = synth.prefill_activation(k, m=m, seed=717 + k)
+    wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=718 + k))
     q, s = _quant(a)
     got = host(fq.w8a8_block_gemm_prefill(q, s, u8_dev(wq), f32_dev(ws)))
     rows = np.r_[0:4, 254:258, 2047:2051, m - 4:m]
@@ -114,13 +127,13 @@ def test_split_halves_match_whole_tiles_bit_for_bit(k):
     assert np.array_equal(halves, whole[:, :2048])
 
 
-@pytest.mark.parametrize("n", [2048, 2560])  # tiles split in halves; whole tiles
-def test_ring_matches_two_stages_bit_for_bit(n):
+@pytest.mark.parametrize("m,n", [(4096, 2048), (4096, 2560), (300, 384)])  # 256 x 256 tiles
+def test_ring_matches_two_stages_bit_for_bit(m, n):  # split in halves; whole; 128 x 128 tiles
     # K = 1024 (8 groups) runs on the five-slot ring; the same problem with a ninth group of
     # zero codes (unit scales) runs on two stages.  The zero group adds exactly zero to every
     # sum, and both sum the same scaled partials in the same order, so the outputs agree bit
     # for bit.
-    m, k = 4096, 1024
+    k = 1024
     a = synth.prefill_activation(k, m=m, seed=520 + n)
     wq, ws = oracle.block_quant(synth.decode_weight(n, k, seed=521 + n))
     q, s = _quant(a)
