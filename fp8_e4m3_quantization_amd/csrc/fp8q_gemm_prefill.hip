@@ -118,15 +118,16 @@ __device__ __forceinline__ v8i ld32(const uint8_t* p, int lo, int hi) {
 // r, so that the 16 rows one 8-byte store instruction writes spread over the bank groups),
 // then written out in 16-byte row pieces.  Called after a barrier that ends every operand
 // read.
-template <int kWM, int kCols>
+template <int kWM, int kWN, int kCols>
 __device__ __forceinline__ void store_tile(const v4f (&acc)[4][kCols], uint8_t* s0, uint8_t* s1,
                                            uint8_t* s2, uint8_t* s3, uint16_t* __restrict__ out,
                                            int m, int n, int ldc, int vec_out, int m0, int n0) {
-  constexpr int kWaveCols = 16 * kCols, kTileCols = 2 * kWaveCols;
-  constexpr int kRows = 64 * kWM, kThreads = 128 * kWM;
+  constexpr int kWaveCols = 16 * kCols, kTileCols = kWN * kWaveCols;
+  constexpr int kRows = 64 * kWM, kThreads = 64 * kWM * kWN;
+  static_assert(kTileCols == 128 || kTileCols == 256, "the XOR permutation stays in the row");
   const int t = int(threadIdx.x), lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWN, wn = wave % kWN;
   const int orow = lane & 15, oh = lane >> 4;
   auto slab = [&](int s) -> uint8_t* { return s == 0 ? s0 : s == 1 ? s1 : s == 2 ? s2 : s3; };
   {
@@ -196,7 +197,7 @@ struct Slots {
 };
 
 // One output tile: rows [m0, m0 + 64 kWM) x columns [n0, n0 + 32 kCols).
-template <int kWM, int kCols, int kBytes>
+template <int kWM, int kWN, int kCols, int kBytes>
 __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
                                              const float* __restrict__ a_scale,
                                              const uint8_t* __restrict__ w_q,
@@ -204,18 +205,18 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
                                              uint16_t* __restrict__ out, int m, int n, int k,
                                              int ldc, int vec_out, int m0, int n0,
                                              const Slots<kBytes>& st) {
-  constexpr int kWaves = 2 * kWM;
+  constexpr int kWaves = kWM * kWN;
   constexpr int kRows = 64 * kWM;         // tile rows
   constexpr int kWaveCols = 16 * kCols;   // columns per wave
-  constexpr int kTileCols = 2 * kWaveCols;
+  constexpr int kTileCols = kWN * kWaveCols;
   static_assert(kRows * 128 <= kBytes && kTileCols * 128 <= kBytes, "a slot holds a tile");
   static_assert(kRows * kTileCols * 2 <= kWM * kBytes, "kWM slots hold the output tile");
   constexpr int kABlocks = kRows / 8 / kWaves;     // 1 KB activation copy blocks per wave
   constexpr int kBBlocks = kTileCols / 8 / kWaves;  // 1 KB weight copy blocks per wave
-  static_assert(kABlocks == 4, "four activation blocks per wave and group");
+  static_assert(kABlocks >= 1 && kBBlocks >= 1 && kWaves % 2 == 0, "whole copy blocks");
   const int t = int(threadIdx.x), lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave >> 1, wn = wave & 1;  // rows 64 wm .., columns kWaveCols * wn ..
+  const int wm = wave / kWN, wn = wave % kWN;  // rows 64 wm .., columns kWaveCols * wn ..
   const int groups = k >> 7;
 
   const __amdgpu_buffer_rsrc_t ra_rsrc = tile_rsrc(a_q, m0, m, k, kRows);
@@ -419,7 +420,8 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
     g += 8;
   } while (g < groups);
   __syncthreads();  // every copy landed and every wave is done reading the slots
-  store_tile<kWM, kCols>(acc, st.x0, st.x1, st.x2, st.x3, out, m, n, ldc, vec_out, m0, n0);
+  store_tile<kWM, kWN, kCols>(acc, st.x0, st.x1, st.x2, st.x3, out, m, n, ldc, vec_out, m0,
+                              n0);
 }
 
 }  // namespace ring
@@ -467,10 +469,10 @@ __global__ __launch_bounds__(kThreads, 1) void w8a8_prefill_ring_kernel(
   const ring::Slots<kArr> st{x0, x1, x2, x3, x4};
   const TileOrigin o = walk_tile(int(blockIdx.x), tiles_m, tiles_n, n_full);
   if (o.half < 0)
-    ring::prefill_tile<4, 8>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0,
+    ring::prefill_tile<4, 2, 8>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0,
                              o.n0, st);
   else
-    ring::prefill_tile<4, 4>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0,
+    ring::prefill_tile<4, 2, 4>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0,
                              o.n0, st);
 }
 
@@ -643,7 +645,7 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
     step(g + 1, st.a1, st.b1, st.s1, st.a0, st.b0, st.s0);
   }
   __syncthreads();  // every copy landed and every wave is done reading the stages
-  store_tile<4, kCols>(acc, st.a0, st.a1, st.b0, st.b1, out, m, n, ldc, vec_out, m0, n0);
+  store_tile<4, 2, kCols>(acc, st.a0, st.a1, st.b0, st.b1, out, m, n, ldc, vec_out, m0, n0);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void w8a8_prefill_kernel(
@@ -709,7 +711,9 @@ __device__ __forceinline__ int2 tile_origin(int bid, int tiles_m, int tiles_n) {
 
 // Five-slot ring (group counts that are a multiple of eight, at most one tile per CU):
 // 16 KB slots, 2 x 2 waves of 64 x 64.
-__global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_small_ring_kernel(
+constexpr int kRingWN = 2, kRingCols = 4;
+constexpr int kRingThreads = 128 * kRingWN;
+__global__ __launch_bounds__(kRingThreads, 2) void w8a8_prefill_small_ring_kernel(
     const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale,
     const uint8_t* __restrict__ w_q, const float* __restrict__ w_scale,
     uint16_t* __restrict__ out, int m, int n, int k, int ldc, int tiles_m, int tiles_n,
@@ -719,8 +723,8 @@ __global__ __launch_bounds__(kThreads, 2) void w8a8_prefill_small_ring_kernel(
       x3[kAStage], x4[kAStage];
   const ring::Slots<kAStage> st{x0, x1, x2, x3, x4};
   const int2 origin = tile_origin(int(blockIdx.x), tiles_m, tiles_n);
-  ring::prefill_tile<2, 4>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, origin.x,
-                           origin.y, st);
+  ring::prefill_tile<2, kRingWN, kRingCols>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc,
+                                            vec_out, origin.x, origin.y, st);
 }
 
 // Two stages (any group count).
@@ -887,10 +891,10 @@ extern "C" int w8a8_block_gemm_prefill(const uint8_t* a_q, const float* a_scale,
   if (tiles_m * tiles_n > 0x7FFFFFFF) return FP8Q_EINVAL;
   // the ring when every CU holds at most one tile (with two tiles side by side on a CU its
   // deeper copies gain nothing)
-  const auto small = (k / 128) % 8 == 0 && tiles_m * tiles_n <= cus
-                         ? tile128::w8a8_prefill_small_ring_kernel
-                         : tile128::w8a8_prefill_small_kernel;
-  launch(small, dim3(unsigned(tiles_m * tiles_n)), dim3(tile128::kThreads), 0, stream, a_q,
-         a_scale, w_q, w_scale, out, m, n, k, ldc, int(tiles_m), int(tiles_n), vec_out);
+  const bool ring = (k / 128) % 8 == 0 && tiles_m * tiles_n <= cus;
+  launch(ring ? tile128::w8a8_prefill_small_ring_kernel : tile128::w8a8_prefill_small_kernel,
+         dim3(unsigned(tiles_m * tiles_n)),
+         dim3(ring ? tile128::kRingThreads : tile128::kThreads), 0, stream, a_q, a_scale, w_q,
+         w_scale, out, m, n, k, ldc, int(tiles_m), int(tiles_n), vec_out);
   return launch_status();
 }
