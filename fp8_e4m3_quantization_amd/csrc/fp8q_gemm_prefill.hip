@@ -77,8 +77,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base,
 
 // ---------------------------------------------------------------------------------------
 // Shared by the tiled kernels.  A wave tile is 64 rows x 16 kCols columns; the waves form a
-// kWM x 2 grid (kWM = 4: 256 x 256 or 256 x 128 tiles of 8 waves; kWM = 2: 128 x 128 tiles
-// of 4 waves).
+// kWM x kWN grid (4 x 2: 256 x 256 or 256 x 128 tiles of 8 waves; 2 x 2: 128 x 128 tiles of
+// 4 waves).
 
 // Staged 128-byte operand row r keeps its 16-byte chunk c at slot c ^ (r & 7) ^ (bit 3 of
 // r): an operand read takes one chunk from 16 consecutive rows per 16 lanes, which land on
@@ -169,8 +169,7 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[4][kCols], uint8_t* 
 // Five-slot ring (group counts that are a multiple of eight).
 //
 // LDS: five slots, each a separate array (one operand tile of one group each; 5 x 32 KB =
-// all 160 KB for the 256-row tiles, 5 x 16 KB for the 128 x 128 tiles, two workgroups per
-// CU).  Step g multiplies the activation tile and the weight tile of group g from two
+// all 160 KB for the 256-row tiles, 5 x 16 KB for the 128 x 128 tiles).  Step g multiplies the activation tile and the weight tile of group g from two
 // slots while the weight tile of group g + 1 lands in a third, and copies the activation
 // tile of group g + 1 and the weight tile of group g + 2 into the two slots that group
 // g - 1 used: a weight copy has two steps to land, an activation copy one.  The slots
@@ -196,7 +195,7 @@ struct Slots {
   uint8_t (&x4)[kBytes];
 };
 
-// One output tile: rows [m0, m0 + 64 kWM) x columns [n0, n0 + 32 kCols).
+// One output tile: rows [m0, m0 + 64 kWM) x columns [n0, n0 + 16 kWN kCols).
 template <int kWM, int kWN, int kCols, int kBytes>
 __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
                                              const float* __restrict__ a_scale,
