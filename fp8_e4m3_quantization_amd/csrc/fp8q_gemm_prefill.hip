@@ -469,10 +469,10 @@ __global__ __launch_bounds__(kThreads, 1) void w8a8_prefill_ring_kernel(
   const TileOrigin o = walk_tile(int(blockIdx.x), tiles_m, tiles_n, n_full);
   if (o.half < 0)
     ring::prefill_tile<4, 2, 8>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0,
-                             o.n0, st);
+                                o.n0, st);
   else
     ring::prefill_tile<4, 2, 4>(a_q, a_scale, w_q, w_scale, out, m, n, k, ldc, vec_out, o.m0,
-                             o.n0, st);
+                                o.n0, st);
 }
 
 
