@@ -288,6 +288,8 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
   // would drain the copies still in flight.  (vmcnt in bits 3:0 and 15:14, lgkmcnt 0,
   // expcnt not waited for.)
   constexpr int kWait = (kBBlocks & 15) | (7 << 4) | ((kBBlocks >> 4) << 14);
+  constexpr bool kSpread = kCols == 8;
+  static_assert(!kSpread || (kABlocks == 4 && kBBlocks + 2 < kCols), "dealing columns");
   auto barrier = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(kWait);
@@ -298,9 +300,12 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
   // Group g from slots (sa, sb) with scales sc; the activation copies and scales of group
   // g + 1 go to (na, nsc) and the weight copies of group g + 2 to nb, slots that held group
   // g - 1 (read by everyone before the barrier).  The copies are dealt out over the first
-  // half of the step's MFMAs, one piece after each, rather than issued in one burst ahead
-  // of them (the burst queues in the address unit and holds back the MFMAs that follow it
-  // in the wave's instruction stream).  Column 0 starts once B_0, A_0 and A_1 are in: each
+  // half of the step's MFMAs rather than issued in one burst ahead of them (the burst
+  // queues in the address unit and holds back the MFMAs that follow it in the wave's
+  // instruction stream): with eight columns (kSpread) two activation pieces in column 0 and
+  // two before column 1, then the row scales, then one weight piece per column; with four,
+  // the activation pieces one after each of the first MFMAs, then the rest one or two per
+  // column.  Column 0 starts once B_0, A_0 and A_1 are in: each
   // later fragment is read one MFMA ahead of its use; the column loop is software-
   // pipelined (column c + 1's weight fragment read and column c - 1's products scaled
   // while column c multiplies, MFMA and four FMAs alternating).
@@ -327,13 +332,13 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
     __builtin_amdgcn_sched_barrier(0);
     pcur[1] = mfma_group(bcur, af[1]);
     __builtin_amdgcn_sched_barrier(0);
-    copy_piece(na, nb, nsc, g + 1, g + 2, 2);
+    if constexpr (!kSpread) copy_piece(na, nb, nsc, g + 1, g + 2, 2);
     __builtin_amdgcn_sched_barrier(0);
     af[3] = ld32(sa + 3 * 2048, alo, ahi);
     __builtin_amdgcn_sched_barrier(0);
     pcur[2] = mfma_group(bcur, af[2]);
     __builtin_amdgcn_sched_barrier(0);
-    copy_piece(na, nb, nsc, g + 1, g + 2, 3);
+    if constexpr (!kSpread) copy_piece(na, nb, nsc, g + 1, g + 2, 3);
     __builtin_amdgcn_sched_barrier(0);
     v8i bnxt = ld32(sb + 2048, blo, bhi);
     // the four row scales of this lane, times the weight scale (one product per row and
@@ -353,12 +358,21 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
     bcur = bnxt;
 #pragma unroll
     for (int c = 1; c <= kCols; ++c) {
-      // The row scales and the weight blocks (pieces 4 .. kPieces - 2): one per column from
-      // column 1 while there are no more of them than columns, else spread over all of
-      // them.  The last piece, the scalar load, waits for the last column: every LDS read of
-      // the step is issued and waited for by then.
+      // kSpread: activation pieces 2 and 3 before column 1, the row scales before column 2,
+      // weight block q before column 3 + q.  Otherwise the row scales and the weight blocks
+      // (pieces 4 .. kPieces - 2): one per column from column 1 while there are no more of
+      // them than columns, else spread over all of them.  The last piece, the scalar load,
+      // waits for the last column: every LDS read of the step is issued and waited for by
+      // then.
       constexpr int kDealt = kPieces - 5;
-      if constexpr (kDealt <= kCols) {
+      if constexpr (kSpread) {
+        if (c == 1) {
+          copy_piece(na, nb, nsc, g + 1, g + 2, 2);
+          copy_piece(na, nb, nsc, g + 1, g + 2, 3);
+        } else if (c <= kBBlocks + 2) {
+          copy_piece(na, nb, nsc, g + 1, g + 2, c + 2);
+        }
+      } else if constexpr (kDealt <= kCols) {
         if (c <= kDealt) copy_piece(na, nb, nsc, g + 1, g + 2, 3 + c);
       } else {
 #pragma unroll
