@@ -305,10 +305,10 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
   // instruction stream): with eight columns (kSpread) two activation pieces in column 0 and
   // two before column 1, then the row scales, then one weight piece per column; with four,
   // the activation pieces one after each of the first MFMAs, then the rest one or two per
-  // column.  Column 0 starts once B_0, A_0 and A_1 are in: each
-  // later fragment is read one MFMA ahead of its use; the column loop is software-
-  // pipelined (column c + 1's weight fragment read and column c - 1's products scaled
-  // while column c multiplies, MFMA and four FMAs alternating).
+  // column.  Column 0 starts once B_0, A_0 and A_1 are in: each later fragment is read one
+  // MFMA ahead of its use; the column loop is software-pipelined (column c + 1's weight
+  // fragment read and column c - 1's products scaled while column c multiplies, MFMA and
+  // four FMAs alternating).
   auto step = [&](int g, const uint8_t* sa, const uint8_t* sb, const Scales& sc, uint8_t* na,
                   uint8_t* nb, Scales& nsc) {
     barrier();
