@@ -576,7 +576,7 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
 
   // Group g from stage (sa, sb, ss); the copies of group g + 1 go to (na, nbs, ns), which
   // held group g - 1 (read by everyone before the barrier).  The copies are dealt out over
-  // the first half of the step's MFMAs, one piece after each, as in the ring.
+  // the first half of the step's MFMAs, one piece after each.
   auto step = [&](int g, const uint8_t* sa, const uint8_t* sb, const float* ss, uint8_t* na,
                   uint8_t* nbs, float* ns) {
     __syncthreads();  // everyone's copies of group g landed (the fence drains them)
