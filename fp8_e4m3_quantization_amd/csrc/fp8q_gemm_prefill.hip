@@ -195,6 +195,39 @@ struct Slots {
   uint8_t (&x4)[kBytes];
 };
 
+// Where each of a step's kPieces copy pieces is dealt: the column before whose MFMAs it is
+// issued, 0 meaning the first column (piece 0 ahead of its first MFMA, piece j after MFMA
+// j - 1).  With eight columns: activation pieces two in column 0 and two before column 1,
+// the row scales before column 2, weight block q before column 3 + q.  With four: the
+// activation pieces after the first MFMAs, then the row scales and weight blocks one per
+// column from column 1 while there are no more of them than columns, else spread over all
+// of them.  The scalar load goes before the last column: every LDS read of the step is
+// issued and waited for by then (scalar and LDS loads share a wait counter).  The barrier's
+// wait count relies on the issue order: pieces go out in index order, so the row scales
+// precede the weight blocks, the step's last vector loads.
+template <int kCols, int kABlocks, int kPieces>
+struct DealColumns {
+  static constexpr int column(int j) {
+    constexpr int kDealt = kPieces - 5;
+    if (j == kPieces - 1) return kCols;
+    if (kCols == 8) return j < 2 ? 0 : j < 4 ? 1 : j - 2;
+    if (j < kABlocks) return 0;
+    if (kDealt <= kCols) return j - 3;
+    int c = 1;
+    while (j >= 4 + c * kDealt / kCols) ++c;
+    return c;
+  }
+  static constexpr bool valid() {
+    if (kABlocks != 4) return false;
+    for (int j = 0; j < kPieces; ++j) {
+      if (column(j) < 0 || column(j) > kCols) return false;
+      if (j > 0 && column(j) < column(j - 1)) return false;
+      if (column(j) == 0 && j > 3) return false;  // three places after the first MFMAs
+    }
+    return column(0) == 0 && column(kPieces - 1) == kCols;
+  }
+};
+
 // One output tile: rows [m0, m0 + 64 kWM) x columns [n0, n0 + 16 kWN kCols).
 template <int kWM, int kWN, int kCols, int kBytes>
 __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
@@ -288,8 +321,8 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
   // would drain the copies still in flight.  (vmcnt in bits 3:0 and 15:14, lgkmcnt 0,
   // expcnt not waited for.)
   constexpr int kWait = (kBBlocks & 15) | (7 << 4) | ((kBBlocks >> 4) << 14);
-  constexpr bool kSpread = kCols == 8;
-  static_assert(!kSpread || (kABlocks == 4 && kBBlocks + 2 < kCols), "dealing columns");
+  using Deal = DealColumns<kCols, kABlocks, kPieces>;
+  static_assert(Deal::valid(), "copy pieces dealt in index order, the scalar load last");
   auto barrier = [&]() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(kWait);
@@ -300,12 +333,10 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
   // Group g from slots (sa, sb) with scales sc; the activation copies and scales of group
   // g + 1 go to (na, nsc) and the weight copies of group g + 2 to nb, slots that held group
   // g - 1 (read by everyone before the barrier).  The copies are dealt out over the first
-  // half of the step's MFMAs rather than issued in one burst ahead of them (the burst
-  // queues in the address unit and holds back the MFMAs that follow it in the wave's
-  // instruction stream): with eight columns (kSpread) two activation pieces in column 0 and
-  // two before column 1, then the row scales, then one weight piece per column; with four,
-  // the activation pieces one after each of the first MFMAs, then the rest one or two per
-  // column.  Column 0 starts once B_0, A_0 and A_1 are in: each later fragment is read one
+  // half of the step's MFMAs (deal_column) rather than issued in one burst ahead of them
+  // (the burst queues in the address unit and holds back the MFMAs that follow it in the
+  // wave's instruction stream).  Column 0 starts once B_0, A_0 and A_1 are in: each later
+  // fragment is read one
   // MFMA ahead of its use; the column loop is software-pipelined (column c + 1's weight
   // fragment read and column c - 1's products scaled while column c multiplies, MFMA and
   // four FMAs alternating).
@@ -326,19 +357,19 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
     __builtin_amdgcn_sched_barrier(0);
     pcur[0] = mfma_group(bcur, af[0]);
     __builtin_amdgcn_sched_barrier(0);
-    copy_piece(na, nb, nsc, g + 1, g + 2, 1);
+    if constexpr (Deal::column(1) == 0) copy_piece(na, nb, nsc, g + 1, g + 2, 1);
     __builtin_amdgcn_sched_barrier(0);
     af[2] = ld32(sa + 2 * 2048, alo, ahi);
     __builtin_amdgcn_sched_barrier(0);
     pcur[1] = mfma_group(bcur, af[1]);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!kSpread) copy_piece(na, nb, nsc, g + 1, g + 2, 2);
+    if constexpr (Deal::column(2) == 0) copy_piece(na, nb, nsc, g + 1, g + 2, 2);
     __builtin_amdgcn_sched_barrier(0);
     af[3] = ld32(sa + 3 * 2048, alo, ahi);
     __builtin_amdgcn_sched_barrier(0);
     pcur[2] = mfma_group(bcur, af[2]);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!kSpread) copy_piece(na, nb, nsc, g + 1, g + 2, 3);
+    if constexpr (Deal::column(3) == 0) copy_piece(na, nb, nsc, g + 1, g + 2, 3);
     __builtin_amdgcn_sched_barrier(0);
     v8i bnxt = ld32(sb + 2048, blo, bhi);
     // the four row scales of this lane, times the weight scale (one product per row and
@@ -358,28 +389,9 @@ __device__ __forceinline__ void prefill_tile(const uint8_t* __restrict__ a_q,
     bcur = bnxt;
 #pragma unroll
     for (int c = 1; c <= kCols; ++c) {
-      // kSpread: activation pieces 2 and 3 before column 1, the row scales before column 2,
-      // weight block q before column 3 + q.  Otherwise the row scales and the weight blocks
-      // (pieces 4 .. kPieces - 2): one per column from column 1 while there are no more of
-      // them than columns, else spread over all of them.  The last piece, the scalar load,
-      // waits for the last column: every LDS read of the step is issued and waited for by
-      // then.
-      constexpr int kDealt = kPieces - 5;
-      if constexpr (kSpread) {
-        if (c == 1) {
-          copy_piece(na, nb, nsc, g + 1, g + 2, 2);
-          copy_piece(na, nb, nsc, g + 1, g + 2, 3);
-        } else if (c <= kBBlocks + 2) {
-          copy_piece(na, nb, nsc, g + 1, g + 2, c + 2);
-        }
-      } else if constexpr (kDealt <= kCols) {
-        if (c <= kDealt) copy_piece(na, nb, nsc, g + 1, g + 2, 3 + c);
-      } else {
 #pragma unroll
-        for (int j = 4 + (c - 1) * kDealt / kCols; j < 4 + c * kDealt / kCols; ++j)
-          copy_piece(na, nb, nsc, g + 1, g + 2, j);
-      }
-      if (c == kCols) copy_piece(na, nb, nsc, g + 1, g + 2, kPieces - 1);
+      for (int j = 1; j < kPieces; ++j)
+        if (Deal::column(j) == c) copy_piece(na, nb, nsc, g + 1, g + 2, j);
       __builtin_amdgcn_sched_barrier(0);
       bnxt = bcur;
       if (c + 1 < kCols) bnxt = ld32(sb + (c + 1) * 2048, blo, bhi);
