@@ -144,7 +144,8 @@ int w8a8_block_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q
  * writes its part's FP32 16x16 tile sums to the workspace, and the workgroup that completes
  * a strip adds the parts in a fixed order (p = 0, 1, ...), so the result is deterministic
  * (it may differ from w8a8_block_gemm's in the last bits: another FP32 summation order).
- * Shapes that do not benefit run w8a8_block_gemm's kernel and touch no workspace.
+ * Shapes that do not benefit run w8a8_block_gemm's kernel and touch no workspace; K a
+ * multiple of 1024 never splits (w8a8_block_gemm's staged form is faster there).
  *
  * w8a8_block_gemm_workspace_size: *bytes = the workspace this shape needs on the current
  *   device (0: no split).  Errors: FP8Q_ENULL, FP8Q_EINVAL (shape as w8a8_block_gemm).

@@ -1,5 +1,8 @@
 """GPU parity: the K-split decode GEMM (w8a8_block_gemm_ws) against the FP64 oracle.
 
+The split applies to few output strips at K not a multiple of 1024 (K a multiple of 1024 runs
+unsplit in the staged form), so the split cases here take K = 41, 39, 31 or 63 groups.
+
 Same bar as w8a8_block_gemm: |gpu - ref| <= 1e-2 |ref| + 1e-3 rms(ref) per bf16 output.
 Beyond it: the split is deterministic (repeated calls give the same bits), the workspace's
 counts are back at zero after every call, only the documented output extent is written,
@@ -32,9 +35,9 @@ def _counts_bytes(n):
     return -(-(n // 16) * 4 // 256) * 256
 
 
-@pytest.mark.parametrize("m,n,k", [(16, 1024, 5120), (5, 1024, 5120), (1, 128, 5120),
-                                   (16, 256, 4096), (12, 128, 8192), (3, 384, 5120),
-                                   (7, 512, 8192)])
+@pytest.mark.parametrize("m,n,k", [(16, 1024, 5248), (5, 1024, 5248), (1, 128, 5248),
+                                   (16, 256, 3968), (12, 128, 8064), (3, 384, 4992),
+                                   (7, 512, 8064)])
 def test_split_matches_oracle_deterministic_and_leaves_counts_zero(m, n, k):
     q, s, wq, ws = _operands(m, n, k, 7000 + n + k + m)
     need = fq.w8a8_block_gemm_workspace_size(m, n, k)
@@ -53,10 +56,11 @@ def test_split_matches_oracle_deterministic_and_leaves_counts_zero(m, n, k):
         2.0 ** -7 * np.max(np.abs(ref))
 
 
-def test_decode_projection_n1024_with_the_bindings_own_workspace():
-    """The decode step's N = 1024 projection (M = 16, K = 5120) through the workspace the
-    binding keeps per stream, over several calls with other shapes in between."""
-    q, s, wq, ws = _operands(16, 1024, 5120, 2000)
+def test_split_with_the_bindings_own_workspace():
+    """A split shape (M = 16, N = 1024, K = 5248) through the workspace the binding keeps per
+    stream, over several calls with other shapes in between."""
+    q, s, wq, ws = _operands(16, 1024, 5248, 2000)
+    assert fq.w8a8_block_gemm_workspace_size(16, 1024, 5248) > 0
     args = (u8_dev(q), f32_dev(s), u8_dev(wq), f32_dev(ws))
     ref = oracle.gemm(q, s, wq, ws)
     first = host(fq.w8a8_block_gemm_ws(*args))
@@ -66,6 +70,18 @@ def test_decode_projection_n1024_with_the_bindings_own_workspace():
     again = host(fq.w8a8_block_gemm_ws(*args))
     assert np.array_equal(first, again)
     assert gemm_tolerance_ok(first, ref)[0]
+
+
+def test_decode_projection_n1024_runs_unsplit():
+    """The decode step's N = 1024 projection (M = 16, K = 5120): K a multiple of 1024 takes the
+    staged form unsplit, so the workspace entry needs no workspace and gives the plain call's
+    bits."""
+    q, s, wq, ws = _operands(16, 1024, 5120, 2000)
+    assert fq.w8a8_block_gemm_workspace_size(16, 1024, 5120) == 0
+    args = (u8_dev(q), f32_dev(s), u8_dev(wq), f32_dev(ws))
+    got = host(fq.w8a8_block_gemm_ws(*args))
+    assert np.array_equal(got, host(fq.w8a8_block_gemm(*args)))
+    assert gemm_tolerance_ok(got, oracle.gemm(q, s, wq, ws))[0]
 
 
 def test_unsplit_shapes_equal_w8a8_block_gemm_bit_for_bit():
@@ -79,7 +95,8 @@ def test_unsplit_shapes_equal_w8a8_block_gemm_bit_for_bit():
 def test_split_writes_exactly_its_strided_extent_and_nan_rows_stay_out():
     """Strided output (ldc > n): nothing outside the (m - 1) * ldc + n extent changes; NaN
     bytes in activation rows >= m (device memory beyond the rows passed) never leak in."""
-    m, n, k, ldc = 6, 1024, 5120, 1100
+    m, n, k, ldc = 6, 1024, 5248, 1100
+    assert fq.w8a8_block_gemm_workspace_size(m, n, k) > 0
     q, s, wq, ws = _operands(m, n, k, 41)
     qd = torch.full((16, k), 0x7F, dtype=torch.uint8, device=DEV)
     qd[:m] = u8_dev(q)
@@ -98,8 +115,9 @@ def test_split_writes_exactly_its_strided_extent_and_nan_rows_stay_out():
 def test_workspace_errors_before_launch():
     import ctypes
     lib = fq.load()
-    m, n, k = 16, 1024, 5120
+    m, n, k = 16, 1024, 5248
     need = fq.w8a8_block_gemm_workspace_size(m, n, k)
+    assert need > 0
     p = ctypes.c_void_p(1 << 20)
     assert lib.w8a8_block_gemm_ws(p, p, p, p, p, m, n, k, n, None, need, None) == -2
     assert lib.w8a8_block_gemm_ws(p, p, p, p, p, m, n, k, n, p, need - 1, None) == -1

@@ -37,7 +37,7 @@ def _noalloc(args, out, m, n, k):
 
 def test_noalloc_equals_the_workspace_entry_point_on_consecutive_calls():
     results = []
-    for m, n, k, seed in [(16, 1024, 5120, 7100), (5, 128, 5120, 7200), (16, 1024, 5120, 7100)]:
+    for m, n, k, seed in [(16, 1024, 5248, 7100), (5, 128, 5248, 7200), (16, 1024, 5248, 7100)]:
         assert fq.w8a8_block_gemm_workspace_size(m, n, k) > 0, "shape takes the split path"
         q, s, wq, ws = _operands(m, n, k, seed)
         args = (u8_dev(q), f32_dev(s), u8_dev(wq), f32_dev(ws))
