@@ -665,7 +665,7 @@ def main():
         roof = dict(bound="hbm", achieved=dom["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(dom["gbs"] / HBM_PEAK_GBS, 4),
                     traffic=profiled_traffic(dom_name),
-                    kernel="w8a8_persistent_kernel<5,...,quant> (group quant + 4 decode "
+                    kernel="w8a8_staged_kernel<5, quant, 3> (group quant + 4 decode "
                            "projections, one launch)",
                     bytes_per_launch=dom["bytes"], us_per_launch=dom["us"])
     st = result.get("step")
