@@ -484,14 +484,18 @@ __device__ __forceinline__ void static_for(Fn&& f) {
   static_for_impl<kN>(f, std::make_integer_sequence<int, kN>());
 }
 
-template <int kGpw, bool kQuant, int kDepth>
-__global__ __launch_bounds__(64 * kPWaves) void w8a8_staged_kernel(ActSrc act, ProjSet ps, int m,
-                                                                    int k, int total_strips,
-                                                                    int half_from) {
+// The activation a staged launch multiplies: E4M3 codes with their row scales, bf16 that the
+// launch quantizes itself (the fused form), or bf16 taken as is (the W8A16 tier).
+enum StagedAct { kActCodes = 0, kActQuantize = 1, kActBf16 = 2 };
+
+template <int kGpw, int kAct, int kDepth>
+__device__ __forceinline__ void staged_body(const ActSrc& act, const ProjSet& ps, int m, int k,
+                                            int total_strips, int half_from) {
   static_assert(kDepth >= 1 && kDepth <= 3, "copies at most three pieces ahead of four slots");
+  constexpr bool kQuant = kAct == kActQuantize;
   constexpr int kRound = 4;
   constexpr int kPartFloats = kRound * kPWaves * 4 * 64;
-  using Tile = ActTile<kQuant ? 16 : 8>;
+  using Tile = ActTile<kAct == kActCodes ? 8 : 16>;
   static_assert(kRound * 256 == kPWaves * 64 * 2, "reduce: two outputs per lane");
   // four slots as four arrays: every slot index below is a compile-time constant, so a
   // fragment read is seen not to touch the slot whose copies are still in flight
@@ -589,12 +593,17 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_staged_kernel(ActSrc act, P
   v8i a[kGpw];
   float4 as[kGpw];
   float scv[kGpw];  // kQuant: this lane's row scale of each group
+  uint4 af[kGpw][4];  // kActBf16: this lane's 32 bf16 of each group
   v4u raw[kGpw][Tile::kLoads];
-  float4 rs[kGpw];  // !kQuant: the row scales of lanes' four output rows
-#pragma unroll
-  for (int u = 0; u < kGpw; ++u) {
+  float4 rs[kGpw];  // kActCodes: the row scales of lanes' four output rows
+  // Every group's raw loads up front, except in the fused form with more than six groups per
+  // wave (K > 6144), where all the bf16 tiles and the codes would not fit in registers: there
+  // each group is loaded and quantized in turn after the copies (the fused form still spills
+  // from six groups per wave on, 96-328 bytes a lane).
+  constexpr bool kAllLoadsFirst = !(kQuant && kGpw > 6);
+  auto load_group = [&](int u) {
     const int goff = (8 * u + wv) * 128;  // first k of group 8u + wv
-    if constexpr (kQuant) {
+    if constexpr (kAct != kActCodes) {
       Tile::load(reinterpret_cast<const uint8_t*>(act.a_bf16) + 2 * goff, 2 * int64_t(k), m,
                  lane, raw[u]);
     } else {
@@ -605,6 +614,10 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_staged_kernel(ActSrc act, P
       rs[u].z = act.a_scale[int64_t(min(r0 + 2, m - 1)) * groups + g];
       rs[u].w = act.a_scale[int64_t(min(r0 + 3, m - 1)) * groups + g];
     }
+  };
+  if constexpr (kAllLoadsFirst) {
+#pragma unroll
+    for (int u = 0; u < kGpw; ++u) load_group(u);
   }
   // The first kDepth + 1 pieces (every slot with three ahead) are copied before the
   // activation fragments are made: the fused form's quantization alone is about 6 VALU
@@ -619,7 +632,10 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_staged_kernel(ActSrc act, P
   __builtin_amdgcn_sched_barrier(0);  // keep the copies ahead of the activation math
 
   auto make_fragments = [&](int u) {
-    if constexpr (!kQuant) {
+    if constexpr (kAct == kActBf16) {
+      // rows >= m repeat row m - 1 (Tile::load): finite, computed and never stored
+      Tile::exchange(tile, raw[u], lane, koff >> 3, af[u]);
+    } else if constexpr (kAct == kActCodes) {
       uint4 f[2];
       Tile::exchange(tile, raw[u], lane, koff >> 4, f);
       const v8i fr = {int(f[0].x), int(f[0].y), int(f[0].z), int(f[0].w),
@@ -655,7 +671,10 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_staged_kernel(ActSrc act, P
   };
 
 #pragma unroll
-  for (int u = 0; u < kGpw; ++u) make_fragments(u);
+  for (int u = 0; u < kGpw; ++u) {
+    if constexpr (!kAllLoadsFirst) load_group(u);
+    make_fragments(u);
+  }
 
   // Piece p of round item j (t = j kGpw + p), round items from i.  With one piece ahead the
   // next copies are issued before this piece's wait (one piece stays in flight while
@@ -688,12 +707,25 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_staged_kernel(ActSrc act, P
     const v4u y = *reinterpret_cast<const v4u*>(slot + 16 * ((c0 + 1) ^ row));
     const v8i b = {int(x[0]), int(x[1]), int(x[2]), int(x[3]),
                    int(y[0]), int(y[1]), int(y[2]), int(y[3])};
-    const v4f c = mfma_group(a[p], b);
     const float wsc = wsq[t & 3];
-    acc[0] = __builtin_fmaf(c[0], as[p].x * wsc, acc[0]);
-    acc[1] = __builtin_fmaf(c[1], as[p].y * wsc, acc[1]);
-    acc[2] = __builtin_fmaf(c[2], as[p].z * wsc, acc[2]);
-    acc[3] = __builtin_fmaf(c[3], as[p].w * wsc, acc[3]);
+    if constexpr (kAct == kActBf16) {
+      // the W8A16 tier: the 32 codes widened to bf16 (exact), four bf16 MFMAs over the group,
+      // its partial times the block scale (the activation carries no scale)
+      v4f c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf16, af[p][q]),
+                                                    widen8(uint32_t(b[2 * q]), uint32_t(b[2 * q + 1])),
+                                                    c, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(c[q], wsc, acc[q]);
+    } else {
+      const v4f c = mfma_group(a[p], b);
+      acc[0] = __builtin_fmaf(c[0], as[p].x * wsc, acc[0]);
+      acc[1] = __builtin_fmaf(c[1], as[p].y * wsc, acc[1]);
+      acc[2] = __builtin_fmaf(c[2], as[p].z * wsc, acc[2]);
+      acc[3] = __builtin_fmaf(c[3], as[p].w * wsc, acc[3]);
+    }
   };
   // One partial buffer: a round's reduce reads it in the next round's first piece, after that
   // piece's barrier, and the next partial tile goes in at the end of the round's first item,
@@ -740,6 +772,22 @@ __global__ __launch_bounds__(64 * kPWaves) void w8a8_staged_kernel(ActSrc act, P
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+template <int kGpw, bool kQuant, int kDepth>
+__global__ __launch_bounds__(64 * kPWaves) void w8a8_staged_kernel(ActSrc act, ProjSet ps, int m,
+                                                                    int k, int total_strips,
+                                                                    int half_from) {
+  staged_body<kGpw, kQuant ? kActQuantize : kActCodes, kDepth>(act, ps, m, k, total_strips,
+                                                                half_from);
+}
+
+// The W8A16 tier (1..4 bf16 activation rows) in the same staged form.
+template <int kGpw, int kDepth>
+__global__ __launch_bounds__(64 * kPWaves) void w8a16_staged_kernel(ActSrc act, ProjSet ps, int m,
+                                                                     int k, int total_strips,
+                                                                     int half_from) {
+  staged_body<kGpw, kActBf16, kDepth>(act, ps, m, k, total_strips, half_from);
+}
+
 template <int kWaves, int kChunk>
 int launch_gemm(const uint8_t* a_q, const float* a_scale, const uint8_t* w_q,
                 const float* w_scale, uint16_t* out, int m, int n, int k, int ldc,
@@ -769,6 +817,15 @@ int launch_staged(const ActSrc& act, const ProjSet& ps, int m, int k, int total,
                   hipStream_t stream) {
   launch((w8a8_staged_kernel<kGpw, kQuant, FP8Q_STAGE_DEPTH>), dim3(grid), dim3(64 * kPWaves), 0,
          stream, act, ps, m, k, total, halved_from(total, grid));
+  return launch_status();
+}
+
+template <int kGpw>
+int launch_w8a16_staged(const uint16_t* a, const ProjSet& ps, int m, int k, int total, int grid,
+                        hipStream_t stream) {
+  const ActSrc act = {nullptr, nullptr, a, nullptr, nullptr};
+  launch((w8a16_staged_kernel<kGpw, FP8Q_STAGE_DEPTH>), dim3(grid), dim3(64 * kPWaves), 0, stream,
+         act, ps, m, k, total, halved_from(total, grid));
   return launch_status();
 }
 
@@ -834,6 +891,23 @@ uint64_t split_workspace_bytes(int strips, int parts) {
 }
 
 }  // namespace
+
+int run_w8a16_staged(const uint16_t* a, const ProjSet& ps, int m, int k, hipStream_t stream) {
+  const int total = ps.strip_end[ps.count - 1];
+  const int grid = total < num_cus() ? total : num_cus();
+  switch (k / 1024) {
+    case 1: return launch_w8a16_staged<1>(a, ps, m, k, total, grid, stream);
+    case 2: return launch_w8a16_staged<2>(a, ps, m, k, total, grid, stream);
+    case 3: return launch_w8a16_staged<3>(a, ps, m, k, total, grid, stream);
+    case 4: return launch_w8a16_staged<4>(a, ps, m, k, total, grid, stream);
+    case 5: return launch_w8a16_staged<5>(a, ps, m, k, total, grid, stream);
+    case 6: return launch_w8a16_staged<6>(a, ps, m, k, total, grid, stream);
+    case 7: return launch_w8a16_staged<7>(a, ps, m, k, total, grid, stream);
+    case 8: return launch_w8a16_staged<8>(a, ps, m, k, total, grid, stream);
+    default: return FP8Q_EINVAL;
+  }
+}
+
 }  // namespace fp8q
 
 using namespace fp8q;

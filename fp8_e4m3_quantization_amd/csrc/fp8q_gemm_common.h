@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fp8q_device.h"
+
 namespace fp8q {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -155,5 +157,28 @@ struct ActTile {
     for (int i = 0; i < kFrag; ++i) frag[i] = tile[r * kChunks + slot(r, first_chunk + i)];
   }
 };
+
+// ---------------------------------------------------------------------------------
+// The W8A16 tier's weight operand: E4M3 codes widened to bf16 for v_mfma_f32_16x16x32_bf16.
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+
+// Two E4M3 codes (bytes 0,1 or 2,3 of w) -> two bf16 in one word: the binary32 decode is
+// exact and its top half is the bf16 value (no rounding: three mantissa bits).
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  const float2 f = e4m3x2_to_f32<kHigh>(w);
+  return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+}
+
+// Eight codes (two dwords) -> the eight bf16 of one MFMA operand, in k order.
+__device__ __forceinline__ v8bf16 widen8(uint32_t lo, uint32_t hi) {
+  const uint4 r = make_uint4(e4m3x2_to_bf16x2<false>(lo), e4m3x2_to_bf16x2<true>(lo),
+                             e4m3x2_to_bf16x2<false>(hi), e4m3x2_to_bf16x2<true>(hi));
+  return __builtin_bit_cast(v8bf16, r);
+}
+
+// The W8A16 tier over a projection set in the staged form (fp8q_gemm.hip): k a multiple of
+// 1024, k <= 8192, 1 <= m <= 4.
+int run_w8a16_staged(const uint16_t* a, const ProjSet& ps, int m, int k, hipStream_t stream);
 
 }  // namespace fp8q

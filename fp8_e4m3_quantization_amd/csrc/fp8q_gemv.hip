@@ -29,26 +29,9 @@
 namespace fp8q {
 namespace {
 
-typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
-
 constexpr int kGemvMaxRows = 4;
 constexpr int kGemvRound = 4;  // strips per LDS reduction
 constexpr int kGemvMaxK = kPWaves * 8 * 128;  // the persistent form holds <= 8 groups per wave
-
-// Two E4M3 codes (bytes 0,1 or 2,3 of w) -> two bf16 in one word: the binary32 decode is
-// exact and its top half is the bf16 value (no rounding: three mantissa bits).
-template <bool kHigh>
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
-  const float2 f = e4m3x2_to_f32<kHigh>(w);
-  return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
-}
-
-// Eight codes (two dwords) -> the eight bf16 of one MFMA operand, in k order.
-__device__ __forceinline__ v8bf16 widen8(uint32_t lo, uint32_t hi) {
-  const uint4 r = make_uint4(e4m3x2_to_bf16x2<false>(lo), e4m3x2_to_bf16x2<true>(lo),
-                             e4m3x2_to_bf16x2<false>(hi), e4m3x2_to_bf16x2<true>(hi));
-  return __builtin_bit_cast(v8bf16, r);
-}
 
 template <int kGpw>
 struct GemvSlice {
@@ -250,6 +233,9 @@ int launch_gemv(const uint16_t* a, const ProjSet& ps, int m, int k, int total,
 
 int run_gemv(const uint16_t* a, const ProjSet& ps, int m, int k, hipStream_t stream) {
   const int total = ps.strip_end[ps.count - 1];
+  // k a multiple of 1024: the weight stream staged through LDS in whole 1 KB rows (the W8A8
+  // decode GEMM's staged form with a bf16 activation)
+  if (k % 1024 == 0 && k <= kGemvMaxK) return run_w8a16_staged(a, ps, m, k, stream);
   if (k > kGemvMaxK) {
     launch(w8a16_long_kernel, dim3(unsigned(total)), dim3(64 * kPWaves), 0, stream, a, ps, m, k);
     return launch_status();
