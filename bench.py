@@ -1,10 +1,12 @@
 """Benchmark of the FP8 (E4M3) quantize-and-consume path on one MI355X.
 
 One step = one pass of the whole hot path over one decode batch:
-  per-token 1x128 group quant of the activation [16 x 5120] (bf16 -> E4M3 + scales) and
-  the four decode projections sharing it (W8A8 block-scaled GEMM, M=16, K=5120,
-  N = 16384, 12288, 5120, 1024) in one fused launch, the K/V absmax and the paged FP8 KV
-  write of the batch's 16 new tokens (4 KV heads x 128 dims) at the calibrated scale.
+  per-token 1x128 group quant of the activation [16 x 5120] (bf16 -> E4M3 + scales, a
+  launch of its own), the four decode projections sharing it (W8A8 block-scaled GEMM,
+  M=16, K=5120, N = 16384, 12288, 5120, 1024) in one grouped launch, the K/V absmax and the
+  paged FP8 KV write of the batch's 16 new tokens (4 KV heads x 128 dims) at the calibrated
+  scale in one launch.  The same step with the quantizer fused into the GEMM launch is
+  reported beside it.
 Steps are issued eagerly through the library's API (the same step replayed as one HIP
 graph per buffer set is reported beside it); inputs rotate over >= 1 GB of buffer sets so
 the 256 MB MALL cannot serve repeated reads.  value = algorithmic bytes per step /
@@ -23,7 +25,7 @@ operands rotate over >= 1 GB like every other leg.  Reference rows: an empty ker
 plain 2:1 read/write stream of the group quantizer's and the KV write's bytes, timed by the
 same hook.  The calibration window (256 tokens of seeded paged batches) reports the latency
 of an in-window observe and of the freezing observe.  The roofline object covers the step's
-dominant kernel (the fused quant + four-projection GEMM); cpu_baseline times the CPU oracle
+dominant kernel (the four-projection grouped GEMM); cpu_baseline times the CPU oracle
 on full steps, single-threaded and with quant and GEMM split by rows over the host threads.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -127,8 +129,16 @@ def fused_step_gemm_bytes(m, ns, k):
 
 
 def step_bytes():
-    """One decode step: the fused quant + GEMM launch, then the KV batch's rows read once for
+    """One decode step: the group quant launch (bf16 read, codes and scales written), the
+    grouped GEMM reading those codes and scales once, then the KV batch's rows read once for
     both its absmax and its write (+ the 8-byte running max)."""
+    return (quant_bytes(M_DECODE, K_DECODE) + grouped_gemm_bytes(M_DECODE, N_DECODE, K_DECODE)
+            + kv_write_bytes(M_DECODE) + 8)
+
+
+def fused_step_bytes():
+    """The same step with the quantizer fused into the GEMM launch (codes and scales still
+    written out, the activation read once as bf16)."""
     return fused_step_gemm_bytes(M_DECODE, N_DECODE, K_DECODE) + kv_write_bytes(M_DECODE) + 8
 
 
@@ -272,7 +282,7 @@ def main():
     cal.observe(s0["k"], s0["v"], KV_H, KV_D, kc, vc, s0["slots"], KV_BS)
     k_scale, v_scale = cal.scales()
 
-    def run_step(s):
+    def run_step_fused(s):
         # group quant fused into the grouped GEMM: one launch quantizes the activation (codes
         # and scales also written out) and computes the four projections
         fq.fp8_quant_w8a8_gemm_grouped(s["a"], [(s["w"][n][0], s["w"][n][1], s["out"][n])
@@ -282,9 +292,9 @@ def main():
         fq.fp8_kv_write_amax(s["k"], s["v"], kc, vc, s["slots"], KV_H, KV_D, KV_BS, k_scale,
                              v_scale, s["amax"])
 
-    def run_step_two(s):
-        # the same pass with the quantizer as a launch of its own (fp8_group_quant's codes and
-        # scales), then the four projections in one grouped launch, then the KV write
+    def run_step(s):
+        # the quantizer as a launch of its own (fp8_group_quant's codes and scales), then the
+        # four projections in one grouped launch, then the KV absmax and write in one launch
         fq.fp8_group_quant(s["a"], s["q"], s["s"])
         fq.w8a8_block_gemm_grouped(s["q"], s["s"], [(s["w"][n][0], s["w"][n][1], s["out"][n])
                                                     for n in N_DECODE])
@@ -306,12 +316,12 @@ def main():
 
     result = {}
     if "step" in only:
-        result["step_two_launch"] = dict(ms=time_steps(run_step_two))
-        log(f"step with the quantizer as its own launch: "
-            f"{result['step_two_launch']['ms'] * 1e3:.2f} us")
+        fms = time_steps(run_step_fused)
+        result["step_fused"] = dict(ms=fms, gbs=fused_step_bytes() / (fms * 1e-3) / 1e9)
+        log(f"step with the quantizer fused into the GEMM launch: {fms * 1e3:.2f} us")
         # Timed region: exactly K steps issued eagerly through the library's API (the host
-        # issues a step's two launches in ~25 us, ahead of the GPU's ~40 us, so the stream
-        # never runs dry), synchronized on both sides.
+        # issues a step's three launches well ahead of the GPU's ~38 us, so the stream never
+        # runs dry), synchronized on both sides.
         for i in range(args.warmup):
             run_step(sets[i % len(sets)])
         torch.cuda.synchronize()
@@ -658,15 +668,15 @@ def main():
         cpu = cpu_baseline(synth, log)
 
     # --------------------------------------------------------------- report
-    dom_name = "quant_w8a8_gemm_fused_m16_k5120_4proj"
+    dom_name = "w8a8_gemm_grouped_m16_k5120_4proj"
     dom = kernels.get(dom_name)
     roof = None
     if dom:
         roof = dict(bound="hbm", achieved=dom["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(dom["gbs"] / HBM_PEAK_GBS, 4),
                     traffic=profiled_traffic(dom_name),
-                    kernel="w8a8_staged_kernel<5, quant, 3> (group quant + 4 decode "
-                           "projections, one launch)",
+                    kernel="w8a8_staged_kernel<5, false, 3> (4 decode projections, one "
+                           "launch)",
                     bytes_per_launch=dom["bytes"], us_per_launch=dom["us"])
     st = result.get("step")
     line = {
@@ -694,8 +704,10 @@ def main():
         "step_launch": {"eager_us": round(st["ms"] * 1e3, 2) if st else None,
                         "graph_replay_us": round(result["step_graph"]["ms"] * 1e3, 2)
                         if "step_graph" in result else None,
-                        "quantizer_own_launch_us": round(result["step_two_launch"]["ms"] * 1e3, 2)
-                        if "step_two_launch" in result else None},
+                        "quantizer_fused_into_gemm_us": round(result["step_fused"]["ms"] * 1e3, 2)
+                        if "step_fused" in result else None,
+                        "quantizer_fused_into_gemm_gbs": round(result["step_fused"]["gbs"], 1)
+                        if "step_fused" in result else None},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,

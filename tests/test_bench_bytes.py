@@ -41,7 +41,11 @@ def test_grouped_and_fused_read_the_activation_once():
     # fused: bf16 read once, codes and scales written once, then weights and outputs
     fused = m * k * 2 + act_q + sum(bench.gemm_weight_bytes(n, k) + m * n * 2 for n in ns)
     assert bench.fused_step_gemm_bytes(m, ns, k) == fused
-    assert bench.step_bytes() == fused + bench.kv_write_bytes(16) + 8
+    assert bench.fused_step_bytes() == fused + bench.kv_write_bytes(16) + 8
+    # the headline step: the quantizer's own launch, then the grouped GEMM reading its
+    # codes and scales once
+    grouped = bench.grouped_gemm_bytes(m, ns, k)
+    assert bench.step_bytes() == (m * k * 2 + act_q) + grouped + bench.kv_write_bytes(16) + 8
 
 
 def test_more_than_one_gpu_is_refused_before_touching_a_device():
