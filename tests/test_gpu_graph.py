@@ -1,4 +1,5 @@
-"""The decode step captured in a HIP graph: every replay gives the eager bytes.
+"""The decode step (fused and with the quantizer as its own launch) captured in a HIP graph:
+every replay gives the eager bytes.
 
 The step (fused group quant + four projections, then the KV batch's absmax and write) is
 captured once; the graph is replayed several times with eager library calls and
@@ -42,9 +43,14 @@ def _state():
     return w, st
 
 
-def _step(w, st):
-    fq.fp8_quant_w8a8_gemm_grouped(st["a"], [(w[n][0], w[n][1], st["out"][n]) for n in NS],
-                                   q=st["q"], scales=st["s"])
+def _step(w, st, fused=True):
+    if fused:
+        fq.fp8_quant_w8a8_gemm_grouped(st["a"], [(w[n][0], w[n][1], st["out"][n]) for n in NS],
+                                       q=st["q"], scales=st["s"])
+    else:  # the quantizer as a launch of its own, then the grouped GEMM on its codes
+        fq.fp8_group_quant(st["a"], st["q"], st["s"])
+        fq.w8a8_block_gemm_grouped(st["q"], st["s"], [(w[n][0], w[n][1], st["out"][n])
+                                                      for n in NS])
     fq.fp8_kv_write_amax(st["k"], st["v"], st["kc"], st["vc"], st["slots"], H, D, BS, 0.05,
                          0.07, st["amax"])
 
@@ -61,19 +67,20 @@ def _clear(st):
         st["out"][n].zero_()
 
 
-def test_graph_replays_equal_eager():
+@pytest.mark.parametrize("fused", [True, False])
+def test_graph_replays_equal_eager(fused):
     w, st = _state()
-    _step(w, st)
+    _step(w, st, fused)
     want = _snapshot(st)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        _step(w, st)  # warm-up on the capture stream
+        _step(w, st, fused)  # warm-up on the capture stream
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        _step(w, st)
+        _step(w, st, fused)
     for rep in range(4):
         _clear(st)
         # eager library work between replays
